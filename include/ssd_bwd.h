@@ -1,0 +1,141 @@
+/*
+ * ssd_bwd.h -- C ABI of libssd_bwd.so: the deterministic backward of the
+ * Mamba-2 SSD (state space duality) chunked scan on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation.  The page "Deterministic bwd kernel for mamba2"
+ * (state-spaces/mamba PR 827, its per-kernel breakdown table) lists the
+ * kernels of this backward -- chunk_cumsum_bwd, chunk_state_bwd_dx/db/ddAcs,
+ * chunk_scan_bwd_dC/dx and combined_bwd_dx -- and makes them free of
+ * floating-point atomics; the page "Fix Incorrect Gradients and Illegal
+ * Memory Access Error in Mamba2" (PR 537) discusses the ddA_cumsum ("stable")
+ * kernel.  Neither page writes the equations; the layer is the SSD
+ * recurrence
+ *
+ *     a_t = dt_t * A_h
+ *     h_t = exp(a_t) * h_{t-1} + dt_t * x_t (outer) B_t        (P x N per head)
+ *     y_t = h_t C_t + D_h * x_t
+ *
+ * per batch row and head, restarted at every sequence start with
+ * h_{t0-1} = initial_states[s] (zeros when not given).  ssd_bwd returns the
+ * gradients of  l = sum_t dy_t . y_t  with respect to x, dt, A, B, C, D and
+ * the initial states.  It recomputes the forward chunk states internally;
+ * nothing from a forward pass is needed.
+ *
+ * Determinism.  Every output element and every workspace element is written
+ * by exactly one thread; cross-head and cross-chunk sums are formed in a
+ * fixed order that depends only on the problem shape (partials parked in
+ * per-(batch, chunk, head) slots, then summed in index order), the in-chunk
+ * cumulative sums use one fixed scan order that depends only on chunk_size,
+ * and no floating-point atomics are used.  For the same inputs, shape and
+ * library build the output bytes are identical on every call, in every
+ * process, on any stream.
+ *
+ * Layouts (row-major, contiguous, element counts):
+ *   x, dy, dx            (batch, seqlen, nheads, headdim)      io dtype
+ *   dt, ddt              (batch, seqlen, nheads)               float32
+ *   A, D, dA, dD         (nheads)                              float32
+ *   B, C, dB, dC         (batch, seqlen, ngroups, dstate)      io dtype
+ *   initial_states,
+ *   d_initial_states     (nseqs, nheads, headdim, dstate)      float32
+ *   seq_idx              (batch, seqlen)                       int32
+ * Head h uses group h / (nheads / ngroups).  dt is the already-activated
+ * (positive) step.  A sequence starts at (b, t) when t == 0 or
+ * seq_idx[b, t] != seq_idx[b, t-1]; starts are numbered 0..nseqs-1 in
+ * row-major (b, t) order.  With seq_idx == NULL every batch row is one
+ * sequence (nseqs == batch).
+ *
+ * Ownership and calling convention.  All tensor pointers are device
+ * pointers owned by the caller, 16-byte aligned.  Inputs are read-only;
+ * outputs are fully overwritten (never accumulated into).  The library never
+ * allocates or frees: it uses the caller's workspace, whose contents on entry
+ * do not affect the results.  ssd_bwd only enqueues work on `stream`
+ * (a hipStream_t; NULL = the default stream) and returns without host
+ * synchronisation; argument errors are reported before anything is enqueued.
+ * Concurrent calls must use distinct workspaces and outputs.
+ */
+#ifndef SSD_BWD_H
+#define SSD_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of x, B, C, dy and of the outputs dx, dB, dC */
+typedef enum { SSD_IO_BF16 = 0, SSD_IO_F32 = 1 } ssd_io_dtype;
+
+typedef struct {
+  int64_t batch;      /* >= 1 */
+  int64_t seqlen;     /* >= 1; need not be a multiple of chunk_size (tail masked) */
+  int64_t nheads;     /* >= 1, multiple of ngroups */
+  int64_t headdim;    /* P: 16/32/64 (f32 io) or 32/64 (bf16 io) */
+  int64_t ngroups;    /* >= 1 */
+  int64_t dstate;     /* N: multiple of 16 (f32) or 32 (bf16), <= 256 */
+  int64_t chunk_size; /* Q: 64, 128 or 256 */
+  int64_t nseqs;      /* number of sequence starts (see above); == batch without seq_idx */
+  int32_t io_dtype;   /* ssd_io_dtype */
+  int32_t reserved;   /* must be 0 */
+} ssd_shape;
+
+/* Status codes.  Negative = error; nothing was enqueued. */
+enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = -1,         /* NULL pointer where one is required, bad field */
+  SSD_ERR_UNSUPPORTED_SHAPE = -2,   /* shape outside the supported set above */
+  SSD_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < ssd_bwd_workspace_size() */
+  SSD_ERR_MISALIGNED = -4,          /* a pointer is not 16-byte aligned */
+  SSD_ERR_HIP = -5                  /* a HIP launch failed (see hipGetLastError) */
+};
+
+/* Bytes of device workspace ssd_bwd needs for this shape (written to *bytes).
+ * Pure host computation. */
+int ssd_bwd_workspace_size(const ssd_shape* shape, size_t* bytes);
+
+/*
+ * The backward.  Required: x, dt, A, B, C, dy, dx, ddt, dA, dB, dC, workspace.
+ * Optional (NULL allowed):
+ *   D                 -- treated as zeros; then dD must be NULL too
+ *   dD                -- dD_h = sum over (b, t) of dy . x; needs D
+ *   initial_states    -- zeros when NULL
+ *   seq_idx           -- one sequence per batch row when NULL
+ *   d_initial_states  -- not computed when NULL (computed even when
+ *                        initial_states is NULL)
+ * nseqs must equal the number of sequence starts seq_idx describes whenever
+ * initial_states or d_initial_states is given (it sizes those tensors); the
+ * device code clamps sequence indices into [0, nseqs) so a wrong nseqs cannot
+ * cause out-of-bounds accesses, but the results are then meaningless.
+ * Returns SSD_OK or a negative status.
+ */
+int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+            const void* B, const void* C, const float* D, const void* dy,
+            const float* initial_states, const int32_t* seq_idx,
+            void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+            float* d_initial_states, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* ssd_status_string(int status);
+
+/*
+ * Workspace regions, for inspecting intermediate results after a call
+ * (tests, profiling).  Offsets are in bytes from the workspace start.
+ *   SSD_WS_ACS    float32 (batch, nheads, nchunks, Q): in-chunk inclusive cumsum of
+ *                 dt*A, restarted at chunk and sequence starts
+ *   SSD_WS_HIN    float32 (batch, nheads, nchunks, P, N): state entering each chunk
+ *   SSD_WS_DSTATE float32 (batch, nheads, nchunks, P, N): gradient w.r.t. the state at
+ *                 the end of each chunk, through later positions only
+ * Returns SSD_OK and fills offset/bytes, or a negative status.
+ */
+enum { SSD_WS_ACS = 0, SSD_WS_HIN = 1, SSD_WS_DSTATE = 2 };
+int ssd_bwd_workspace_region(const ssd_shape* shape, int region, size_t* offset, size_t* bytes);
+
+/* Library version, (major << 16) | minor. */
+int ssd_bwd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_BWD_H */

@@ -117,19 +117,25 @@ class Oracle:
         return (y, fs) if return_final_states else y
 
     def backward(self, x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, head_lo=0,
-                 head_hi=None, chunk=0, nthreads=None, want_d_initial=True):
+                 head_hi=None, chunk=0, nthreads=None, want_d_initial=True, partial_groups=False):
         """All gradients of l = sum(dy * y) in fp64.
 
         Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states (None when
         not requested) and, when ``chunk`` > 0, ``chunk_states`` / ``chunk_dout``
         (B, nc, H, P, N).  Only heads [head_lo, head_hi) -- whole groups -- are
-        evaluated; entries of other heads/groups are left as NaN.
+        evaluated; entries of other heads/groups are left as NaN.  dB/dC need
+        every head of a group; with ``partial_groups`` a range may split
+        groups and dB/dC of those groups stay NaN.
         """
         x, dt, A, B, C, D, dy, h0 = map(_f64, (x, dt, A, B, C, D, dy, initial_states))
         si = _i32(seq_idx)
         s = self._shape(x, B, h0, si)
         if head_hi is None:
             head_hi = s.nheads
+        hpg = s.nheads // s.ngroups
+        if (head_lo % hpg or head_hi % hpg) and not partial_groups:
+            raise ValueError("head range must cover whole groups (or pass partial_groups=True; "
+                             "dB/dC are then left NaN for partly covered groups)")
         out = {
             "dx": np.full_like(x, np.nan), "ddt": np.full_like(dt, np.nan),
             "dA": np.full((s.nheads,), np.nan), "dB": np.full_like(B, np.nan),

@@ -367,7 +367,8 @@ int ssdo_forward(const ssdo_shape* s, const double* x, const double* dt, const d
 }
 
 /*
- * Backward over heads [head_lo, head_hi), which must cover whole groups.
+ * Backward over heads [head_lo, head_hi).  dB/dC are written only for the
+ * groups all of whose heads lie in the range.
  * Outputs (all fp64, caller-owned, written only for the covered heads/groups):
  *   dx (B,L,H,P), ddt (B,L,H), dA (H), dB (B,L,G,N), dC (B,L,G,N), dD (H),
  *   d_h0 (S,H,P,N, nullable).
@@ -386,8 +387,7 @@ int ssdo_backward(const ssdo_shape* s, const double* x, const double* dt, const 
       !dC || !dD)
     return SSDO_EINVAL;
   const int64_t hpg = s->nheads / s->ngroups;
-  if (head_lo < 0 || head_hi > s->nheads || head_lo >= head_hi || head_lo % hpg || head_hi % hpg)
-    return SSDO_EINVAL;
+  if (head_lo < 0 || head_hi > s->nheads || head_lo >= head_hi) return SSDO_EINVAL;
   const int64_t L = s->seqlen, N = s->dstate, P = s->headdim, BL = s->batch * L;
   const int64_t nh = head_hi - head_lo;
   ctx_t c;
@@ -419,8 +419,9 @@ int ssdo_backward(const ssdo_shape* s, const double* x, const double* dt, const 
     dA[h] = a;
     dD[h] = d;
   }
+  /* dB/dC only for the groups whose heads are all covered */
   for (int64_t b = 0; b < s->batch; ++b)
-    for (int64_t g = head_lo / hpg; g < head_hi / hpg; ++g)
+    for (int64_t g = (head_lo + hpg - 1) / hpg; g < head_hi / hpg; ++g)
       for (int64_t t = 0; t < L; ++t)
         for (int64_t n = 0; n < N; ++n) {
           double sb = 0.0, sc = 0.0;

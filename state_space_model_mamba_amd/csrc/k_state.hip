@@ -1,0 +1,305 @@
+// Chunk-state forward recompute + state passing, and the state-passing
+// backward (the inter-chunk half of the SSD backward whose intra-chunk
+// kernels the page "Deterministic bwd kernel for mamba2" lists).
+//
+// Both kernels own one (batch, head, dstate tile) and walk the chunks in
+// order, so every state element is produced by exactly one thread in a fixed
+// order; the next chunk's inputs are prefetched into registers while the
+// current chunk's MFMA contraction runs.
+//
+// Forward, chunk c (positions j of the chunk's last segment, Acs restarted at
+// that segment's start):
+//   S_c        = sum_j exp(Acs_end - Acs_j) dt_j x_j (outer) B_j      (P x N, MFMA over j)
+//   Hin_{c+1}  = exp(Acs_end) Hin_c + S_c                 if no sequence starts in chunk c
+//              = S_c + exp(Acs_end) h0[s_last]            otherwise (h0 term only if given)
+// Backward, chunk c from the last down (dOut = gradient w.r.t. the state at
+// the end of chunk c through later positions; zero for the last chunk):
+//   R_m        = sum_{i in segment m} exp(Acs_i) dy_i (outer) C_i  (MFMA over i)
+//   d_h0[s_m]  = R_m (+ exp(Acs_end) dOut if m is the chunk's last segment)   segments that start s_m
+//   dOut_{c-1} = R_0 + exp(Acs_end) dOut                if no sequence starts in chunk c
+//              = R_0 (segment 0 continues) or 0          otherwise
+#include "ssd_problem.h"
+#include "ssd_tiles.h"
+
+namespace ssd {
+
+template <typename T, int Q, int P, int NT>
+struct StateCfg {
+  static constexpr int VEC = Vec16<T>::N;
+  static constexpr int LDQ = Q + VEC;          // K-major rows of length Q (+16 B pad)
+  static constexpr int XV = Q * P / VEC;       // 16-byte vectors of one x/dy chunk
+  static constexpr int NXV = (XV + 255) / 256;
+  static constexpr int BV = Q * NT / VEC;      // vectors of one B/C chunk tile
+  static constexpr int NBV = (BV + 255) / 256;
+  static constexpr int PT = P / 16, NTT = NT / 16, NTILE = PT * NTT, TPW = (NTILE + 3) / 4;
+  static_assert(P % 16 == 0 && NT % 16 == 0 && Q % Mma<T>::KSTEP == 0, "tile shape");
+};
+
+template <typename T, int Q, int P, int NT>
+__device__ __forceinline__ void load_chunk_rows(const Problem& pb, const void* src_hp, const void* src_gn,
+                                                int b, int h, int g, int n0, int c,
+                                                uint4 (&xr)[StateCfg<T, Q, P, NT>::NXV],
+                                                uint4 (&br)[StateCfg<T, Q, P, NT>::NBV]) {
+  using Cf = StateCfg<T, Q, P, NT>;
+  const int tid = threadIdx.x;
+  const T* xs = static_cast<const T*>(src_hp);
+  const T* bs = static_cast<const T*>(src_gn);
+#pragma unroll
+  for (int k = 0; k < Cf::NXV; ++k) {
+    const int v = tid + 256 * k;
+    xr[k] = zero_u4();
+    if (v < Cf::XV) {
+      const int j = v / (P / Cf::VEC), pv = v % (P / Cf::VEC), t = c * Q + j;
+      if (t < pb.L)
+        xr[k] = ld_global16(xs + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * Cf::VEC);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < Cf::NBV; ++k) {
+    const int v = tid + 256 * k;
+    br[k] = zero_u4();
+    if (v < Cf::BV) {
+      const int j = v / (NT / Cf::VEC), nv = v % (NT / Cf::VEC), t = c * Q + j;
+      if (t < pb.L)
+        br[k] = ld_global16(bs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * Cf::VEC);
+    }
+  }
+}
+
+// x (or dy) chunk -> LDS, transposed to [p][j] and scaled by s_scale[j];
+// B (or C) tile -> LDS transposed to [n][j].
+template <typename T, int Q, int P, int NT>
+__device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q, P, NT>::NXV],
+                                                 const uint4 (&br)[StateCfg<T, Q, P, NT>::NBV],
+                                                 const float* s_scale, T* s_xt, T* s_bt) {
+  using Cf = StateCfg<T, Q, P, NT>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < Cf::NXV; ++k) {
+    const int v = tid + 256 * k;
+    if (v < Cf::XV) {
+      const int j = v / (P / Cf::VEC), pv = v % (P / Cf::VEC);
+      const float sc = s_scale[j];
+#pragma unroll
+      for (int e = 0; e < Cf::VEC; ++e)
+        s_xt[(pv * Cf::VEC + e) * Cf::LDQ + j] = Elem<T>::from_f(vget<T>(xr[k], e) * sc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < Cf::NBV; ++k) {
+    const int v = tid + 256 * k;
+    if (v < Cf::BV) {
+      const int j = v / (NT / Cf::VEC), nv = v % (NT / Cf::VEC);
+#pragma unroll
+      for (int e = 0; e < Cf::VEC; ++e) s_bt[(nv * Cf::VEC + e) * Cf::LDQ + j] = vraw<T>(br[k], e);
+    }
+  }
+}
+
+template <typename T, int Q, int P, int NT>
+__global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
+  using Cf = StateCfg<T, Q, P, NT>;
+  __shared__ __attribute__((aligned(16))) T s_xt[P * Cf::LDQ];
+  __shared__ __attribute__((aligned(16))) T s_bt[NT * Cf::LDQ];
+  __shared__ float s_w[Q];
+  __shared__ float s_acs_end;
+  __shared__ int s_nstart, s_seqbase, s_lolast;
+
+  const int ntiles = pb.N / NT;
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
+  const int64_t lb = xcd_logical_block(blockIdx.x, total);
+  const int ntile = static_cast<int>(lb % ntiles);
+  const int64_t bh = lb / ntiles;
+  const int h = static_cast<int>(bh % pb.H), b = static_cast<int>(bh / pb.H);
+  const int g = h / pb.hpg, n0 = ntile * NT;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+
+  uint4 xr[Cf::NXV], br[Cf::NBV];
+  f32x4_t st[Cf::TPW];
+#pragma unroll
+  for (int k = 0; k < Cf::TPW; ++k) st[k] = zero4();
+
+  load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, 0, xr, br);
+  for (int c = 0; c < pb.nc; ++c) {
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
+    if (tid == 0) {
+      s_nstart = pb.cinfo[bc * CINFO + 0];
+      s_seqbase = pb.cinfo[bc * CINFO + 3];
+      s_lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
+      s_acs_end = pb.acs[bhc * Q + Q - 1];
+    }
+    __syncthreads();
+    if (tid < Q)
+      s_w[tid] = (tid >= s_lolast) ? expf(s_acs_end - pb.acs[bhc * Q + tid]) * pb.dtc[bhc * Q + tid] : 0.f;
+    __syncthreads();
+    stage_chunk_rows<T, Q, P, NT>(xr, br, s_w, s_xt, s_bt);
+    __syncthreads();
+    if (c + 1 < pb.nc) load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, c + 1, xr, br);
+
+    const int kb = (s_lolast / Mma<T>::KSTEP) * Mma<T>::KSTEP;
+    const float decay = expf(s_acs_end);
+    const int nstart = s_nstart;
+    const int s_last = clamp_seq(s_seqbase + nstart - 1, pb.nseqs);
+#pragma unroll
+    for (int k = 0; k < Cf::TPW; ++k) {
+      const int tile = w + 4 * k;
+      if (tile < Cf::NTILE) {
+        const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
+        const f32x4_t S = tile_mma_kk<T>(zero4(), s_xt + pt * 16 * Cf::LDQ, Cf::LDQ,
+                                         s_bt + nt * 16 * Cf::LDQ, Cf::LDQ, kb, Q);
+        const int n = n0 + nt * 16 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = pt * 16 + 4 * kg + r;
+          pb.hin[(bhc * P + p) * pb.N + n] = st[k][r];
+          if (nstart == 0) {
+            st[k][r] = decay * st[k][r] + S[r];
+          } else {
+            float init = 0.f;
+            if (pb.h0) init = decay * pb.h0[((static_cast<int64_t>(s_last) * pb.H + h) * P + p) * pb.N + n];
+            st[k][r] = S[r] + init;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int Q, int P, int NT>
+__global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
+  using Cf = StateCfg<T, Q, P, NT>;
+  __shared__ __attribute__((aligned(16))) T s_dyt[P * Cf::LDQ];
+  __shared__ __attribute__((aligned(16))) T s_ct[NT * Cf::LDQ];
+  __shared__ float s_e[Q];
+  __shared__ int s_seg[Q];
+  __shared__ int s_segstart[Q + 1];
+  __shared__ float s_acs_end;
+  __shared__ int s_nstart, s_seqbase;
+
+  const int ntiles = pb.N / NT;
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
+  const int64_t lb = xcd_logical_block(blockIdx.x, total);
+  const int ntile = static_cast<int>(lb % ntiles);
+  const int64_t bh = lb / ntiles;
+  const int h = static_cast<int>(bh % pb.H), b = static_cast<int>(bh / pb.H);
+  const int g = h / pb.hpg, n0 = ntile * NT;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+
+  uint4 xr[Cf::NXV], br[Cf::NBV];
+  f32x4_t dout[Cf::TPW];
+#pragma unroll
+  for (int k = 0; k < Cf::TPW; ++k) dout[k] = zero4();
+
+  load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, pb.nc - 1, xr, br);
+  for (int c = pb.nc - 1; c >= 0; --c) {
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
+    if (tid == 0) {
+      s_nstart = pb.cinfo[bc * CINFO + 0];
+      s_seqbase = pb.cinfo[bc * CINFO + 3];
+      s_acs_end = pb.acs[bhc * Q + Q - 1];
+      s_segstart[0] = 0;
+    }
+    if (tid < Q) {
+      s_e[tid] = expf(pb.acs[bhc * Q + tid]);
+      s_seg[tid] = pb.segpos[bc * Q + tid];
+    }
+    __syncthreads();
+    const int nstart = s_nstart;
+    const int start0 = seg_rank(s_seg[0]);  // 1 when a sequence starts at position 0
+    const int nseg = nstart + 1 - start0;
+    if (tid < Q && tid > 0 && seg_lo(s_seg[tid]) == tid) s_segstart[seg_rank(s_seg[tid]) - start0] = tid;
+    if (tid == 0) s_segstart[nseg] = Q;
+    stage_chunk_rows<T, Q, P, NT>(xr, br, s_e, s_dyt, s_ct);
+    __syncthreads();
+    if (c > 0) load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, c - 1, xr, br);
+
+    const float decay = expf(s_acs_end);
+#pragma unroll
+    for (int k = 0; k < Cf::TPW; ++k) {
+      const int tile = w + 4 * k;
+      if (tile < Cf::NTILE) {
+        const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
+        const int n = n0 + nt * 16 + r16;
+        const T* ab = s_dyt + pt * 16 * Cf::LDQ;
+        const T* bb = s_ct + nt * 16 * Cf::LDQ;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pb.dstate[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = dout[k][r];
+        if (nstart == 0) {
+          const f32x4_t R = tile_mma_kk<T>(zero4(), ab, Cf::LDQ, bb, Cf::LDQ, 0, Q);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + decay * dout[k][r];
+        } else {
+          f32x4_t dhoff = zero4();
+          for (int m = 0; m < nseg; ++m) {
+            const int lo = s_segstart[m], hi = s_segstart[m + 1];
+            const f32x4_t R = tile_mma_kk_range<T>(zero4(), ab, Cf::LDQ, bb, Cf::LDQ, lo, hi);
+            const int rank = seg_rank(s_seg[lo]);
+            if (rank == 0) {
+              dhoff = R;
+            } else if (pb.dinit) {
+              const int s = clamp_seq(s_seqbase + rank - 1, pb.nseqs);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int p = pt * 16 + 4 * kg + r;
+                float v = R[r];
+                if (hi == Q) v += decay * dout[k][r];
+                pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n] = v;
+              }
+            }
+          }
+          dout[k] = dhoff;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// N-tile width of the state kernels.
+static int state_nt(int N, bool bf16) {
+  (void)bf16;
+  return (N % 32 == 0) ? 32 : 16;
+}
+
+template <typename T, int Q, int P, int NT>
+static hipError_t launch_state_t(const Problem& pb, bool fwd, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * (pb.N / NT);
+  if (fwd)
+    hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pb);
+  else
+    hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pb);
+  return hipGetLastError();
+}
+
+template <typename T, int Q, int P>
+static hipError_t launch_state_qp(const Problem& pb, bool fwd, hipStream_t s) {
+  if (state_nt(pb.N, sizeof(T) == 2) == 32) return launch_state_t<T, Q, P, 32>(pb, fwd, s);
+  return launch_state_t<T, Q, P, 16>(pb, fwd, s);
+}
+
+template <typename T>
+static hipError_t launch_state_any(const Problem& pb, bool fwd, hipStream_t s) {
+#define SSD_STATE_CASE(QQ, PP) \
+  if (pb.Q == QQ && pb.P == PP) return launch_state_qp<T, QQ, PP>(pb, fwd, s);
+  if constexpr (sizeof(T) == 2) {
+    SSD_BF16_SHAPES(SSD_STATE_CASE)
+  } else {
+    SSD_F32_SHAPES(SSD_STATE_CASE)
+  }
+#undef SSD_STATE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_state_fwd(const Problem& pb, bool io_bf16, hipStream_t s) {
+  return io_bf16 ? launch_state_any<bf16_t>(pb, true, s) : launch_state_any<float>(pb, true, s);
+}
+
+hipError_t launch_state_bwd(const Problem& pb, bool io_bf16, hipStream_t s) {
+  return io_bf16 ? launch_state_any<bf16_t>(pb, false, s) : launch_state_any<float>(pb, false, s);
+}
+
+}  // namespace ssd

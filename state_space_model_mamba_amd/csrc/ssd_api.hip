@@ -1,0 +1,171 @@
+// C ABI of libssd_bwd.so (declared in include/ssd_bwd.h): argument checks,
+// the workspace layout and the launch sequence of the SSD backward.
+#include <string.h>
+
+#include "ssd_bwd.h"
+#include "ssd_problem.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t segpos, cinfo, acs, dtc, hin, dstate, offd, endd, slot_dA, slot_dD, total;
+  int nc, ntg;
+};
+
+bool is_bf16(const ssd_shape* s) { return s->io_dtype == SSD_IO_BF16; }
+
+int check_shape(const ssd_shape* s) {
+  if (!s) return SSD_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->headdim < 1 || s->ngroups < 1 ||
+      s->dstate < 1 || s->chunk_size < 1 || s->nseqs < 0 || s->reserved != 0)
+    return SSD_ERR_INVALID_ARG;
+  if (s->io_dtype != SSD_IO_BF16 && s->io_dtype != SSD_IO_F32) return SSD_ERR_INVALID_ARG;
+  if (s->nheads % s->ngroups) return SSD_ERR_UNSUPPORTED_SHAPE;
+  const int64_t Q = s->chunk_size, P = s->headdim, N = s->dstate;
+  if (N % 16 || N > 256) return SSD_ERR_UNSUPPORTED_SHAPE;
+  if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) == ~size_t(0))
+    return SSD_ERR_UNSUPPORTED_SHAPE;
+  // index arithmetic inside the kernels uses int for positions and block counts
+  const int64_t nc = (s->seqlen + Q - 1) / Q;
+  if (s->seqlen > (int64_t(1) << 30) || s->batch * s->nheads * nc > (int64_t(1) << 30) ||
+      s->nheads > (1 << 20) || s->batch > (1 << 20) || s->nseqs > (int64_t(1) << 30))
+    return SSD_ERR_UNSUPPORTED_SHAPE;
+  const int ntg_w = ssd::group_ntile(static_cast<int>(N), is_bf16(s));
+  const size_t lim = 160 * 1024;
+  if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
+      ssd::group_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim)
+    return SSD_ERR_UNSUPPORTED_SHAPE;
+  return SSD_OK;
+}
+
+Layout make_layout(const ssd_shape* s) {
+  Layout L;
+  const size_t B = s->batch, H = s->nheads, Q = s->chunk_size, P = s->headdim, N = s->dstate;
+  const size_t nc = (s->seqlen + s->chunk_size - 1) / s->chunk_size;
+  const size_t ntg = N / ssd::group_ntile(static_cast<int>(N), is_bf16(s));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.segpos = take(B * nc * Q * 4);
+  L.cinfo = take(B * nc * ssd::CINFO * 4);
+  L.acs = take(B * H * nc * Q * 4);
+  L.dtc = take(B * H * nc * Q * 4);
+  L.hin = take(B * H * nc * P * N * 4);
+  L.dstate = take(B * H * nc * P * N * 4);
+  L.offd = take(B * H * nc * ntg * Q * 4);
+  L.endd = take(B * H * nc * ntg * 4);
+  L.slot_dA = take(B * nc * H * 4);
+  L.slot_dD = take(B * nc * H * 4);
+  L.total = off;
+  L.nc = static_cast<int>(nc);
+  L.ntg = static_cast<int>(ntg);
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int ssd_bwd_workspace_size(const ssd_shape* shape, size_t* bytes) {
+  const int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!bytes) return SSD_ERR_INVALID_ARG;
+  *bytes = make_layout(shape).total;
+  return SSD_OK;
+}
+
+extern "C" int ssd_bwd_workspace_region(const ssd_shape* shape, int region, size_t* offset, size_t* bytes) {
+  const int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!offset || !bytes) return SSD_ERR_INVALID_ARG;
+  const Layout L = make_layout(shape);
+  const size_t B = shape->batch, H = shape->nheads, Q = shape->chunk_size, P = shape->headdim,
+               N = shape->dstate, nc = L.nc;
+  switch (region) {
+    case SSD_WS_ACS: *offset = L.acs; *bytes = B * H * nc * Q * 4; return SSD_OK;
+    case SSD_WS_HIN: *offset = L.hin; *bytes = B * H * nc * P * N * 4; return SSD_OK;
+    case SSD_WS_DSTATE: *offset = L.dstate; *bytes = B * H * nc * P * N * 4; return SSD_OK;
+    default: return SSD_ERR_INVALID_ARG;
+  }
+}
+
+extern "C" const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SSD_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case SSD_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int ssd_bwd_version(void) { return (1 << 16) | 0; }
+
+extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, const void* dy,
+                       const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
+                       float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !workspace)
+    return SSD_ERR_INVALID_ARG;
+  if (dD && !D) return SSD_ERR_INVALID_ARG;
+  if (!seq_idx && (initial_states || d_initial_states) && shape->nseqs != shape->batch)
+    return SSD_ERR_INVALID_ARG;
+  if ((initial_states || d_initial_states) && shape->nseqs < 1) return SSD_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                        d_initial_states, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+  const Layout L = make_layout(shape);
+  if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+
+  ssd::Problem pb;
+  memset(&pb, 0, sizeof(pb));
+  pb.B = static_cast<int>(shape->batch);
+  pb.L = static_cast<int>(shape->seqlen);
+  pb.H = static_cast<int>(shape->nheads);
+  pb.P = static_cast<int>(shape->headdim);
+  pb.G = static_cast<int>(shape->ngroups);
+  pb.N = static_cast<int>(shape->dstate);
+  pb.Q = static_cast<int>(shape->chunk_size);
+  pb.nc = L.nc;
+  pb.hpg = pb.H / pb.G;
+  pb.nseqs = shape->nseqs > 0 ? static_cast<int>(shape->nseqs) : 1;
+  pb.ntg = L.ntg;
+  pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D; pb.dy = dy;
+  pb.h0 = initial_states; pb.seq_idx = seq_idx;
+  pb.dx = dx; pb.ddt = ddt; pb.dA = dA; pb.dB = dB; pb.dC = dC; pb.dD = dD;
+  pb.dinit = d_initial_states;
+  char* ws = static_cast<char*>(workspace);
+  pb.segpos = reinterpret_cast<int32_t*>(ws + L.segpos);
+  pb.cinfo = reinterpret_cast<int32_t*>(ws + L.cinfo);
+  pb.acs = reinterpret_cast<float*>(ws + L.acs);
+  pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
+  pb.hin = reinterpret_cast<float*>(ws + L.hin);
+  pb.dstate = reinterpret_cast<float*>(ws + L.dstate);
+  pb.offd = reinterpret_cast<float*>(ws + L.offd);
+  pb.endd = reinterpret_cast<float*>(ws + L.endd);
+  pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
+  pb.slot_dD = reinterpret_cast<float*>(ws + L.slot_dD);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = is_bf16(shape);
+  if (ssd::launch_prep(pb, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_group_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_reduce(pb, s) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}

@@ -1,0 +1,79 @@
+// Problem descriptor shared by the host code and the kernels of the SSD
+// backward, plus the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Per-(batch, chunk) integer record in the workspace.
+//   [0] number of sequence starts inside the chunk
+//   [1] unused
+//   [2] unused
+//   [3] global index of the first sequence that starts in the chunk
+constexpr int CINFO = 4;
+
+// segpos entry of chunk position i: low 16 bits = first position of i's
+// segment inside the chunk, high 16 bits = number of sequence starts at
+// positions <= i inside the chunk (0: the segment continues the previous
+// chunk's sequence).
+__host__ __device__ inline int seg_lo(int v) { return v & 0xffff; }
+__host__ __device__ inline int seg_rank(int v) { return v >> 16; }
+
+struct Problem {
+  int B, L, H, P, G, N, Q, nc, hpg, nseqs;
+  int ntg;  // number of dstate tiles in the group kernel
+  // inputs
+  const void* x;
+  const float* dt;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* D;
+  const void* dy;
+  const float* h0;
+  const int32_t* seq_idx;
+  // outputs
+  void* dx;
+  float* ddt;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;
+  float* dinit;
+  // workspace
+  int32_t* segpos;   // (B, nc, Q)
+  int32_t* cinfo;    // (B, nc, CINFO)
+  float* acs;        // (B, H, nc, Q)
+  float* dtc;        // (B, H, nc, Q)
+  float* hin;        // (B, H, nc, P, N)
+  float* dstate;     // (B, H, nc, P, N)
+  float* offd;       // (B, H, nc, ntg, Q)
+  float* endd;       // (B, H, nc, ntg)
+  float* slot_dA;    // (B, nc, H)
+  float* slot_dD;    // (B, nc, H)
+};
+
+// Launchers (defined next to their kernels).  Return hipSuccess or the
+// launch error.  io_bf16 selects the bf16 (true) or fp32 instantiation.
+hipError_t launch_prep(const Problem& pb, hipStream_t s);
+hipError_t launch_state_fwd(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_state_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_group_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_head_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_reduce(const Problem& pb, hipStream_t s);
+
+// The (chunk_size, headdim) pairs compiled for each io dtype.  bf16 needs
+// headdim % 32 == 0 (one MFMA k-step over P); fp32 stops at chunk 128 so that
+// its LDS tiles fit one workgroup.
+#define SSD_BF16_SHAPES(X) X(64, 32) X(64, 64) X(128, 32) X(128, 64) X(256, 32) X(256, 64)
+#define SSD_F32_SHAPES(X) X(64, 16) X(64, 32) X(64, 64) X(128, 16) X(128, 32) X(128, 64)
+
+// Shape support (host side): true when kernels exist for this combination
+// and fit the LDS of one workgroup.
+int group_ntile(int N, bool io_bf16);
+size_t group_lds_bytes(int Q, int P, int NTG, bool io_bf16);
+size_t head_lds_bytes(int Q, int P, bool io_bf16);
+
+}  // namespace ssd

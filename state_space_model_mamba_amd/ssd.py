@@ -1,0 +1,190 @@
+"""ctypes binding of libssd_bwd.so (see include/ssd_bwd.h).
+
+Argument marshalling only: shapes/dtypes are checked, outputs and the
+workspace are allocated with torch on the inputs' device, and the C entry
+point is called on the current HIP stream.  Every arithmetic step runs in the
+library's kernels.  Raises if the library is missing or returns an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libssd_bwd.so")
+
+SSD_IO_BF16 = 0
+SSD_IO_F32 = 1
+SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
+
+EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
+            "ssd_bwd_version")
+
+
+class SsdShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("chunk_size", ctypes.c_int64), ("nseqs", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIBRARY):
+    """Load libssd_bwd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m state_space_model_mamba_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    sp = ctypes.POINTER(SsdShape)
+    lib.ssd_bwd_workspace_size.restype = ctypes.c_int
+    lib.ssd_bwd_workspace_size.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_bwd_workspace_region.restype = ctypes.c_int
+    lib.ssd_bwd_workspace_region.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_bwd_version.restype = ctypes.c_int
+    lib.ssd_bwd_version.argtypes = []
+    lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_bwd.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(status).decode()
+
+
+def make_shape(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size, nseqs, io_dtype) -> SsdShape:
+    return SsdShape(batch, seqlen, nheads, headdim, ngroups, dstate, chunk_size, nseqs, io_dtype, 0)
+
+
+def workspace_size(shape: SsdShape) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load_library().ssd_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    if rc:
+        raise SsdError(rc, "ssd_bwd_workspace_size")
+    return n.value
+
+
+def workspace_region(shape: SsdShape, region: int) -> tuple[int, int]:
+    off = ctypes.c_size_t(0)
+    nb = ctypes.c_size_t(0)
+    rc = load_library().ssd_bwd_workspace_region(ctypes.byref(shape), region, ctypes.byref(off),
+                                                 ctypes.byref(nb))
+    if rc:
+        raise SsdError(rc, "ssd_bwd_workspace_region")
+    return off.value, nb.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = SSD_IO_BF16 if x.dtype == torch.bfloat16 else SSD_IO_F32
+    return make_shape(b, L, H, P, G, N, chunk_size, nseqs, io)
+
+
+def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size: int = 256,
+            nseqs: Optional[int] = None, want_d_initial_states: bool = True,
+            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+    """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
+
+    x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
+    dt: (b, L, H), A, D: (H,), initial_states: (S, H, P, N) fp32 or None,
+    seq_idx: (b, L) int32 or None.  ``nseqs`` (the number of sequence starts)
+    is needed only when seq_idx is given without initial_states.
+    Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states.
+    """
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_bwd runs on a HIP device; got tensors on " + str(dev))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = x.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported io dtype {io}")
+    if initial_states is not None:
+        S = initial_states.shape[0]
+    elif seq_idx is None:
+        S = b
+    else:
+        if nseqs is None and want_d_initial_states:
+            raise ValueError("pass nseqs (number of sequence starts) with seq_idx")
+        S = nseqs or 0
+    _check(x, "x", io, (b, L, H, P), dev)
+    _check(dy, "dy", io, (b, L, H, P), dev)
+    _check(B, "B", io, (b, L, G, N), dev)
+    _check(C, "C", io, (b, L, G, N), dev)
+    _check(dt, "dt", torch.float32, (b, L, H), dev)
+    _check(A, "A", torch.float32, (H,), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
+    _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
+    shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
+    nbytes = workspace_size(shape)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {
+            "dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+            "dA": torch.empty((H,), dtype=torch.float32, device=dev),
+            "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+            "dD": torch.empty((H,), dtype=torch.float32, device=dev) if D is not None else None,
+            "d_initial_states": (torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+                                 if want_d_initial_states and S > 0 else None),
+        }
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_bwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+                     _ptr(initial_states), _ptr(seq_idx), _ptr(out["dx"]), _ptr(out["ddt"]),
+                     _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                     _ptr(out["d_initial_states"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                     ctypes.c_void_p(stream))
+    if rc:
+        raise SsdError(rc, "ssd_bwd")
+    out["workspace"] = workspace
+    out["shape"] = shape
+    return out
+
+
+def workspace_view(result: dict, region: int) -> torch.Tensor:
+    """A float32 view of one workspace region of a finished call (Acs, Hin or dS)."""
+    shape = result["shape"]
+    off, nb = workspace_region(shape, region)
+    ws = result["workspace"]
+    nc = -(-shape.seqlen // shape.chunk_size)
+    flat = ws[off:off + nb].view(torch.float32)
+    if region == SSD_WS_ACS:
+        return flat.view(shape.batch, shape.nheads, nc, shape.chunk_size)
+    return flat.view(shape.batch, shape.nheads, nc, shape.headdim, shape.dstate)

@@ -1,0 +1,107 @@
+"""Shared helpers of the GPU tests: run the HIP library, run the oracle, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from state_space_model_mamba_amd import ssd
+from state_space_model_mamba_amd.workloads import to_f64_numpy
+
+GRADS = ("dx", "ddt", "dA", "dB", "dC", "dD", "d_initial_states")
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def to_device(inputs: dict, dev="cuda") -> dict:
+    out = {}
+    for k, v in inputs.items():
+        out[k] = v.to(dev) if isinstance(v, torch.Tensor) else v
+    return out
+
+
+def run_library(inputs: dict, chunk: int, nseqs=None, fill=None, sync=True, **kw) -> dict:
+    """Call the library on device copies of ``inputs``; outputs stay on the device.
+
+    ``fill``: value the outputs and workspace are pre-filled with (NaN or
+    garbage) to show that every element gets written and that the
+    workspace's prior contents do not matter.
+    """
+    d = to_device(inputs)
+    if nseqs is None:
+        nseqs = inputs["initial_states"].shape[0] if inputs.get("initial_states") is not None else None
+        if nseqs is None and inputs.get("seq_idx") is not None:
+            nseqs = oracle.count_sequences(inputs["x"].shape[0], inputs["x"].shape[1],
+                                           inputs["seq_idx"].numpy())
+    out = None
+    ws = None
+    if fill is not None:
+        x = d["x"]
+        b, L, H, P = x.shape
+        G, N = d["B"].shape[2], d["B"].shape[3]
+        S = nseqs if nseqs is not None else b
+        shape = ssd.make_shape(b, L, H, P, G, N, chunk, S,
+                               ssd.SSD_IO_BF16 if x.dtype == torch.bfloat16 else ssd.SSD_IO_F32)
+        ws = torch.empty(ssd.workspace_size(shape), dtype=torch.uint8, device=x.device)
+        if fill == "garbage":
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=x.device))
+        else:
+            ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+        out = {"dx": torch.full_like(x, float("nan")), "ddt": torch.full_like(d["dt"], float("nan")),
+               "dA": torch.full((H,), float("nan"), device=x.device),
+               "dB": torch.full_like(d["B"], float("nan")), "dC": torch.full_like(d["C"], float("nan")),
+               "dD": torch.full((H,), float("nan"), device=x.device) if d["D"] is not None else None,
+               "d_initial_states": torch.full((S, H, P, N), float("nan"), device=x.device)}
+    res = ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dy"],
+                      initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"),
+                      chunk_size=chunk, nseqs=nseqs, workspace=ws, out=out, **kw)
+    if sync:
+        torch.cuda.synchronize()
+    return res
+
+
+def to_numpy64(res: dict) -> dict:
+    return {k: (res[k].double().cpu().numpy() if res.get(k) is not None else None) for k in GRADS}
+
+
+def run_oracle(inputs: dict, **kw) -> dict:
+    f = to_f64_numpy(inputs)
+    return oracle.backward(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["dy"],
+                           f["initial_states"], f["seq_idx"], **kw)
+
+
+def normwise_err(got, ref) -> float:
+    """max |got - ref| / max |ref| over the entries ref defines (NaN entries of ref are skipped)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    m = ~np.isnan(ref)
+    if not m.any():
+        return 0.0
+    return float(np.max(np.abs(got[m] - ref[m])) / max(np.max(np.abs(ref[m])), 1e-30))
+
+
+def compare(got: dict, ref: dict, tol: float, keys=GRADS, label="") -> dict:
+    errs = {}
+    for k in keys:
+        if ref.get(k) is None or got.get(k) is None:
+            continue
+        assert not np.isnan(got[k]).any(), f"{label}{k}: NaN in library output"
+        errs[k] = normwise_err(got[k], ref[k])
+    print(f"{label} normwise errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{label} over tolerance {tol}: {bad}"
+    return errs
+
+
+def bytes_equal(a: dict, b: dict, keys=GRADS) -> list:
+    diff = []
+    for k in keys:
+        if a.get(k) is None:
+            continue
+        ta, tb = a[k].contiguous(), b[k].contiguous()
+        if ta.dtype == torch.bfloat16:
+            ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+        else:
+            ta, tb = ta.view(torch.int32), tb.view(torch.int32)
+        if not torch.equal(ta, tb):
+            diff.append(k)
+    return diff

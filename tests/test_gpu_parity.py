@@ -1,0 +1,270 @@
+"""GPU parity and determinism of libssd_bwd against the fp64 oracle.
+
+Tolerances (normwise max relative error per gradient): 1e-5 for fp32 inputs,
+2e-2 for bf16 inputs.  Determinism: identical output bytes across repeated
+calls, across workspaces pre-filled with garbage, and across processes.
+"""
+import hashlib
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from state_space_model_mamba_amd import ssd
+from state_space_model_mamba_amd.workloads import WORKLOADS, Workload, make_inputs, seq_idx_from_lengths
+from tests.gpu_helpers import (GRADS, TOL, bytes_equal, compare, run_library, run_oracle, to_numpy64)
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def small(name, **kw):
+    base = dict(batch=1, seqlen=256, nheads=4, headdim=16, ngroups=1, dstate=16, chunk=64, dtype="f32",
+                seed=7, scale_bc=False)
+    base.update(kw)
+    return Workload(name, **base)
+
+
+def packed(inputs, lengths_per_row, h0_std=0.1, seed=0):
+    """Add seq_idx rows (one list of lengths per batch row) and initial states."""
+    rows = [seq_idx_from_lengths(l)[0] for l in lengths_per_row]
+    inputs["seq_idx"] = torch.stack(rows).to(torch.int32).contiguous()
+    S = sum(len(l) for l in lengths_per_row)
+    g = torch.Generator().manual_seed(seed)
+    H, P, N = inputs["x"].shape[2], inputs["x"].shape[3], inputs["B"].shape[3]
+    inputs["initial_states"] = (torch.randn((S, H, P, N), generator=g) * h0_std).contiguous()
+    return inputs
+
+
+def check(inputs, chunk, tol, label, oracle_kw=None, lib_kw=None):
+    print(f"[case] {label}", flush=True)
+    res = run_library(inputs, chunk, **(lib_kw or {}))
+    got = to_numpy64(res)
+    ref = run_oracle(inputs, **(oracle_kw or {}))
+    compare(got, ref, tol, label=label)
+    return res, got, ref
+
+
+# --------------------------------------------------------------------------- parity
+def test_tiny_fp32_workload_and_chunk_states():
+    w = WORKLOADS["tiny_f32_L256"]
+    inputs = make_inputs(w)
+    res, got, ref = check(inputs, w.chunk, TOL["f32"], w.name, oracle_kw=dict(chunk=w.chunk))
+    hin = ssd.workspace_view(res, ssd.SSD_WS_HIN).double().cpu().numpy()     # (b, H, nc, P, N)
+    dst = ssd.workspace_view(res, ssd.SSD_WS_DSTATE).double().cpu().numpy()
+    from tests.gpu_helpers import normwise_err
+    e_h = normwise_err(hin.transpose(0, 2, 1, 3, 4), ref["chunk_states"])
+    e_d = normwise_err(dst.transpose(0, 2, 1, 3, 4), ref["chunk_dout"])
+    print(f"chunk states err {e_h:.2e}, state grads err {e_d:.2e}", flush=True)
+    assert e_h <= TOL["f32"] and e_d <= TOL["f32"]
+
+
+def test_fp32_packed_ragged_tail_chunk_aligned_start():
+    # row 0: starts at 0, 64 (chunk aligned), 104, 105 (length-1 sequence); row 1: one sequence
+    w = small("f32_packed", batch=2, seqlen=200, nheads=4, ngroups=2, headdim=16, dstate=32, chunk=64)
+    inputs = packed(make_inputs(w), [[64, 40, 1, 95], [200]])
+    check(inputs, 64, TOL["f32"], "f32 packed ragged")
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_fp32_headdim64_chunks(chunk):
+    w = small("f32_p64", batch=1, seqlen=300, nheads=4, ngroups=2, headdim=64, dstate=48, chunk=chunk, seed=3)
+    inputs = packed(make_inputs(w), [[100, 150, 50]])
+    check(inputs, chunk, TOL["f32"], f"f32 P64 Q{chunk}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_bf16_chunk_sizes_packed(chunk):
+    w = Workload("bf16_small", batch=2, seqlen=700, nheads=8, headdim=64, ngroups=2, dstate=128,
+                 chunk=chunk, dtype="bf16", seed=11)
+    inputs = packed(make_inputs(w), [[300, 256, 144], [700]])
+    check(inputs, chunk, TOL["bf16"], f"bf16 Q{chunk}")
+
+
+def test_bf16_headdim32_dstate64():
+    w = Workload("bf16_p32", batch=1, seqlen=520, nheads=6, headdim=32, ngroups=3, dstate=64,
+                 chunk=128, dtype="bf16", seed=12)
+    check(make_inputs(w), 128, TOL["bf16"], "bf16 P32 N64")
+
+
+def test_workload_L2048_full():
+    w = WORKLOADS["bf16_L2048_H128"]
+    check(make_inputs(w), w.chunk, TOL["bf16"], w.name)
+
+
+def test_workload_B2_L4096_sampled_group():
+    w = WORKLOADS["bf16_B2_L4096_H128"]
+    inputs = make_inputs(w)
+    check(inputs, w.chunk, TOL["bf16"], w.name + " group 3", oracle_kw=dict(head_lo=48, head_hi=64))
+
+
+def test_headline_L16384_sampled_group():
+    w = WORKLOADS["bf16_L16384_H128"]
+    inputs = make_inputs(w)
+    check(inputs, w.chunk, TOL["bf16"], w.name + " group 5", oracle_kw=dict(head_lo=80, head_hi=96))
+
+
+def test_varlen_N256_full_size_sampled_heads():
+    w = WORKLOADS["bf16_varlen7_L16384_N256"]
+    inputs = make_inputs(w)
+    # 8 of the 64 heads of the single group: per-head outputs; dB/dC need the whole group
+    check(inputs, w.chunk, TOL["bf16"], w.name + " heads 24..31",
+          oracle_kw=dict(head_lo=24, head_hi=32, partial_groups=True))
+
+
+def test_varlen_N256_shortened_all_outputs():
+    w = WORKLOADS["bf16_varlen7_L16384_N256"].scaled(seqlen=2048, min_len=128, name="varlen7_L2048_N256")
+    inputs = make_inputs(w)
+    check(inputs, w.chunk, TOL["bf16"], w.name)
+
+
+# --------------------------------------------------------------------------- edge cases
+def test_single_token_and_short_sequences():
+    w = small("L1", seqlen=1)
+    check(make_inputs(w), 64, TOL["f32"], "L=1")
+    w = small("L37", seqlen=37, nheads=2)
+    check(make_inputs(w), 64, TOL["f32"], "L=37 < Q")
+
+
+def test_every_position_starts_a_sequence():
+    w = small("allstarts", seqlen=70, nheads=2, chunk=64)
+    inputs = packed(make_inputs(w), [[1] * 70])
+    check(inputs, 64, TOL["f32"], "every position a start")
+
+
+def test_without_D_or_initial_state_gradients():
+    w = small("noD", seqlen=130, nheads=2)
+    inputs = make_inputs(w)
+    inputs["D"] = None
+    print("[case] no D", flush=True)
+    res = run_library(inputs, 64, want_d_initial_states=False)
+    assert res["dD"] is None and res["d_initial_states"] is None
+    ref = run_oracle(inputs)
+    compare(to_numpy64(res), ref, TOL["f32"], keys=("dx", "ddt", "dA", "dB", "dC"), label="no D")
+
+
+def test_wrong_nseqs_is_clamped_not_out_of_bounds():
+    w = small("nseqs", seqlen=200, nheads=2)
+    inputs = packed(make_inputs(w), [[50, 50, 100]])
+    inputs["initial_states"] = inputs["initial_states"][:2].contiguous()
+    print("[case] nseqs smaller than the number of starts", flush=True)
+    res = run_library(inputs, 64, nseqs=2)   # 3 starts, 2 states: indices are clamped
+    assert res["dx"].isfinite().all()
+
+
+# --------------------------------------------------------------------------- determinism
+def test_bitwise_repeatable_with_garbage_workspace():
+    w = WORKLOADS["bf16_L2048_H128"]
+    inputs = make_inputs(w)
+    print("[case] determinism L2048", flush=True)
+    a = run_library(inputs, w.chunk, fill="garbage")
+    b = run_library(inputs, w.chunk, fill="nan")
+    c = run_library(inputs, w.chunk)
+    assert bytes_equal(a, b) == [] and bytes_equal(a, c) == []
+
+
+def test_bitwise_repeatable_many_runs_packed():
+    w = Workload("bf16_det", batch=2, seqlen=1000, nheads=16, headdim=64, ngroups=4, dstate=128,
+                 chunk=256, dtype="bf16", seed=21)
+    inputs = packed(make_inputs(w), [[300, 300, 400], [512, 488]])
+    print("[case] determinism x30", flush=True)
+    first = run_library(inputs, 256)
+    for _ in range(30):
+        assert bytes_equal(first, run_library(inputs, 256)) == []
+
+
+def digest(res) -> str:
+    h = hashlib.sha256()
+    for k in GRADS:
+        if res.get(k) is not None:
+            h.update(res[k].contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def test_bitwise_identical_across_processes():
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from tests.test_gpu_parity import _digest_of_workload\n"
+            "print(_digest_of_workload())\n") % ROOT
+    print("[case] second process", flush=True)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == _digest_of_workload()
+
+
+def _digest_of_workload():
+    w = Workload("bf16_proc", batch=1, seqlen=1536, nheads=32, headdim=64, ngroups=2, dstate=128,
+                 chunk=256, dtype="bf16", seed=31)
+    return digest(run_library(make_inputs(w), 256))
+
+
+def test_linear_in_dy_bitwise():
+    w = Workload("bf16_lin", batch=1, seqlen=900, nheads=8, headdim=64, ngroups=2, dstate=128,
+                 chunk=256, dtype="bf16", seed=41)
+    inputs = make_inputs(w)
+    print("[case] 2*dy", flush=True)
+    a = run_library(inputs, 256)
+    inputs2 = dict(inputs)
+    inputs2["dy"] = inputs["dy"] * 2
+    b = run_library(inputs2, 256)
+    for k in GRADS:
+        if a.get(k) is None:
+            continue
+        assert torch.equal(b[k].float(), 2 * a[k].float()), k
+
+
+def test_batch_rows_independent_bitwise():
+    w = Workload("bf16_rows", batch=2, seqlen=600, nheads=8, headdim=64, ngroups=2, dstate=128,
+                 chunk=256, dtype="bf16", seed=51)
+    inputs = make_inputs(w)
+    print("[case] batch independence", flush=True)
+    both = run_library(inputs, 256)
+    for r in range(2):
+        one = {k: (v[r:r + 1].contiguous() if isinstance(v, torch.Tensor) and k in ("x", "dt", "B", "C", "dy")
+                   else v) for k, v in inputs.items()}
+        single = run_library(one, 256)
+        for k in ("dx", "ddt", "dB", "dC"):
+            assert torch.equal(single[k][0], both[k][r]), (r, k)
+        assert torch.equal(single["d_initial_states"][0], both["d_initial_states"][r])
+
+
+def test_dA_cumsum_matches_oracle_and_ignores_launch_shape():
+    w = small("acs", batch=2, seqlen=300, nheads=8, ngroups=2, chunk=64)
+    inputs = packed(make_inputs(w), [[100, 100, 100], [300]])
+    print("[case] dA_cumsum", flush=True)
+    res = run_library(inputs, 64)
+    acs = ssd.workspace_view(res, ssd.SSD_WS_ACS).cpu()
+    dt = inputs["dt"].double()
+    A = inputs["A"].double()
+    starts = torch.zeros(2, 320, dtype=torch.bool)
+    starts[:, ::64] = True
+    starts[0, [100, 200]] = True
+    ref = torch.zeros(2, 8, 320, dtype=torch.float64)
+    for b in range(2):
+        for h in range(8):
+            run = 0.0
+            for t in range(320):
+                a = float(dt[b, t, h] * A[h]) if t < 300 else 0.0
+                run = a if starts[b, t] else run + a
+                ref[b, h, t] = run
+    got = acs.double().reshape(2, 8, 320)
+    assert (got - ref).abs().max() <= 1e-5 * ref.abs().max()
+    # the same head computed inside a problem with a different head count
+    # (different grid and block-to-head assignment) gives the same bits
+    sub = {k: v for k, v in inputs.items()}
+    for k in ("x", "dt", "dy"):
+        sub[k] = inputs[k][:, :, 4:8].contiguous()
+    sub["A"] = inputs["A"][4:8].contiguous()
+    sub["D"] = inputs["D"][4:8].contiguous()
+    sub["B"] = inputs["B"][:, :, 1:2].contiguous()
+    sub["C"] = inputs["C"][:, :, 1:2].contiguous()
+    sub["initial_states"] = inputs["initial_states"][:, 4:8].contiguous()
+    r2 = run_library(sub, 64)
+    acs2 = ssd.workspace_view(r2, ssd.SSD_WS_ACS).cpu()
+    assert torch.equal(acs2.view(torch.int32), acs[:, 4:8].contiguous().view(torch.int32))
+    for k in ("dx", "ddt"):
+        assert torch.equal(r2[k], res[k][:, :, 4:8].contiguous()), k
+    assert torch.equal(r2["dB"], res["dB"][:, :, 1:2].contiguous())

@@ -336,8 +336,12 @@ def test_head_range_matches_full_run():
         assert np.isnan(part[k][:, :, :2]).all()
     np.testing.assert_array_equal(part["dB"][:, :, 1], full["dB"][:, :, 1])
     np.testing.assert_array_equal(part["dA"][2:4], full["dA"][2:4])
-    with pytest.raises(RuntimeError):
+    with pytest.raises(ValueError):
         run_oracle_bwd(p, head_lo=1, head_hi=4)   # not a whole group
+    q = run_oracle_bwd(p, head_lo=1, head_hi=4, partial_groups=True)
+    np.testing.assert_array_equal(q["dx"][:, :, 1:4], full["dx"][:, :, 1:4])
+    np.testing.assert_array_equal(q["dB"][:, :, 1], full["dB"][:, :, 1])
+    assert np.isnan(q["dB"][:, :, 0]).all() and np.isnan(q["dB"][:, :, 2]).all()
 
 
 def test_chunk_exports_match_definitions():
