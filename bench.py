@@ -1,0 +1,241 @@
+"""Benchmark of the deterministic SSD backward (libssd_bwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 300] [--warmup 50] [--workload bf16_L16384_H128]
+
+One step = one full ssd_bwd call (forward-state recompute + all backward
+kernels) over one synthetic batch already resident in HBM.  Prints one JSON
+line: tokens/s (value), ms per step (= ms per layer), the dominant kernel's
+roofline, the whole-step roofline, whether every step's outputs were bitwise
+identical, and the fp64 CPU oracle timed on a bounded sample of the same
+workload (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD bwd ms/layer + tokens/s at L=16K (1 GPU); bitwise repeat + % roofline"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_head.hip", "ssd_device.h",
+                  "ssd_tiles.h", "ssd_problem.h"]
+
+
+def sizes(w, ntg):
+    """Byte sizes of the tensors of one call (I/O dtype s bytes, fp32 elsewhere)."""
+    s = 2 if w.dtype == "bf16" else 4
+    nc = -(-w.seqlen // w.chunk)
+    S = w.nseqs_packed if w.nseqs_packed else w.batch
+    z = dict(
+        X=w.batch * w.seqlen * w.nheads * w.headdim * s,          # x, dy or dx
+        BC=w.batch * w.seqlen * w.ngroups * w.dstate * s,          # B, C, dB or dC
+        DT=w.batch * w.seqlen * w.nheads * 4,                      # dt or ddt
+        INIT=(S * w.nheads * w.headdim * w.dstate * 4) if w.h0_std > 0 else 0,
+        DINIT=S * w.nheads * w.headdim * w.dstate * 4,
+        SEQ=w.batch * w.seqlen * 4 if w.nseqs_packed else 0,
+        T=w.batch * w.nheads * nc * w.headdim * w.dstate * 4,      # Hin or dS (fp32)
+        CH=w.batch * w.nheads * nc * w.chunk * 4,                  # one per-chunk fp32 vector
+        OFFD=w.batch * w.nheads * nc * ntg * w.chunk * 4,
+        SEG=w.batch * nc * w.chunk * 4,
+    )
+    return z
+
+
+def step_alg_bytes(z):
+    """Compulsory I/O plus one write and one read of the fp32 chunk states and state gradients."""
+    return 3 * z["X"] + 4 * z["BC"] + 2 * z["DT"] + z["INIT"] + z["DINIT"] + z["SEQ"] + 4 * z["T"]
+
+
+def stage_alg_bytes(z):
+    """Each operand a stage must read or write, counted once."""
+    return {
+        "prep": z["DT"] + z["SEQ"] + 2 * z["CH"] + z["SEG"],
+        "state_fwd": z["X"] + z["BC"] + 2 * z["CH"] + z["INIT"] + z["T"],
+        "state_bwd": z["X"] + z["BC"] + z["CH"] + z["T"] + z["DINIT"],
+        "group_bwd": 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"],
+        "head_bwd": 3 * z["X"] + 2 * z["BC"] + z["T"] + 2 * z["CH"] + z["OFFD"] + 2 * z["DT"],
+        "reduce": 0,
+    }
+
+
+def step_alg_flops(w):
+    """MFMA flops of the chunked method, causal Q x Q products counted at half."""
+    nc = -(-w.seqlen // w.chunk)
+    Q, P, N = w.chunk, w.headdim, w.dstate
+    per_hc = 5 * 2 * P * N * Q + 2 * Q * Q * P
+    per_gc = 3 * Q * Q * N
+    return w.batch * nc * (w.nheads * per_hc + w.ngroups * per_gc)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "state_space_model_mamba_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from committed rocprofv3 counter runs, or None
+    when there are none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    ent = rec.get("workloads", {}).get(workload, {}).get(stage)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, groups=1):
+    """The fp64 oracle on the heads of `groups` groups of the workload (all tokens)."""
+    import numpy as np
+    import oracle
+    hpg = w.nheads // w.ngroups
+    h1 = groups * hpg
+    g1 = groups
+    f = {}
+    for k in ("x", "dy"):
+        f[k] = inputs[k][:, :, :h1].to(dtype=__import__("torch").float64).numpy()
+    f["dt"] = inputs["dt"][:, :, :h1].double().numpy()
+    f["A"] = inputs["A"][:h1].double().numpy()
+    f["D"] = inputs["D"][:h1].double().numpy()
+    f["B"] = inputs["B"][:, :, :g1].double().numpy()
+    f["C"] = inputs["C"][:, :, :g1].double().numpy()
+    h0 = inputs.get("initial_states")
+    f["h0"] = None if h0 is None else h0[:, :h1].double().numpy()
+    si = inputs.get("seq_idx")
+    f["seq_idx"] = None if si is None else si.numpy()
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.backward(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], f["dy"], f["h0"], f["seq_idx"],
+                    nthreads=threads)
+    dt = time.perf_counter() - t0
+    frac = h1 / w.nheads
+    return {"value": w.tokens * frac / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": (f"all {w.tokens} tokens, all {w.nheads} heads" if h1 == w.nheads else
+                       f"all {w.tokens} tokens of heads 0..{h1 - 1} ({groups} of {w.ngroups} groups); "
+                       f"tokens/s scaled by {h1}/{w.nheads} of the heads")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=0,
+                    help="groups of heads the CPU baseline covers (0 = all)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding of this path is a design note, not a measured run)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_model_mamba_amd import ssd
+    from state_space_model_mamba_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload or HEADLINE]
+    inputs = make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.items()}
+    S = d["initial_states"].shape[0] if d.get("initial_states") is not None else (
+        w.nseqs_packed or w.batch)
+    shape = ssd.shape_of(d["x"], d["B"], w.chunk, S)
+    ws = torch.empty(ssd.workspace_size(shape), dtype=torch.uint8, device=dev)
+    H, P, N = w.nheads, w.headdim, w.dstate
+    out = {"dx": torch.empty_like(d["x"]), "ddt": torch.empty_like(d["dt"]),
+           "dA": torch.empty(H, device=dev), "dB": torch.empty_like(d["B"]),
+           "dC": torch.empty_like(d["C"]), "dD": torch.empty(H, device=dev),
+           "d_initial_states": torch.empty((S, H, P, N), device=dev)}
+    names = ssd.stage_names()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dy"],
+                    initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
+                    nseqs=S, workspace=ws, out=out, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    ev_steps = [ssd.make_stage_events(stream) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(ev_steps[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {n: 0.0 for n in names}
+    for evs in ev_steps:
+        for i, n in enumerate(names):
+            stage_ms[n] += evs[i].elapsed_time(evs[i + 1]) / args.steps
+    bitwise = all(torch.equal(out[k].view(torch.uint8) if out[k].dtype != torch.bfloat16 else out[k].view(torch.int16),
+                              ref[k].view(torch.uint8) if ref[k].dtype != torch.bfloat16 else ref[k].view(torch.int16))
+                  for k in out)
+
+    ntg = N // (64 if N % 64 == 0 else (32 if N % 32 == 0 else 16))
+    z = sizes(w, ntg)
+    sb = stage_alg_bytes(z)
+    dom = max(stage_ms, key=stage_ms.get)
+    achieved = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(w.name, dom)
+    step_bytes = step_alg_bytes(z)
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    flops = step_alg_flops(w)
+    res = {
+        "metric": METRIC,
+        "value": w.tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": H, "headdim": P,
+                   "ngroups": w.ngroups, "dstate": N, "chunk": w.chunk,
+                   "nseqs": S, "initial_states": w.h0_std > 0, "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": sb[dom], "avg_ms": stage_ms[dom]},
+        "step_roofline": {"bound": "hbm", "alg_bytes": step_bytes, "achieved": step_gbs,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": step_gbs / PEAK_HBM_GBS,
+                          "roofline_ms": step_bytes / (PEAK_HBM_GBS * 1e9) * 1e3,
+                          "alg_mfma_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+                          "mfma_peak_tflops": PEAK_BF16_TFLOPS},
+        "stages_ms": stage_ms,
+        "bitwise_repeat": bitwise,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inputs, groups=args.cpu_groups or w.ngroups)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

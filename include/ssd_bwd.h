@@ -131,6 +131,27 @@ const char* ssd_status_string(int status);
 enum { SSD_WS_ACS = 0, SSD_WS_HIN = 1, SSD_WS_DSTATE = 2 };
 int ssd_bwd_workspace_region(const ssd_shape* shape, int region, size_t* offset, size_t* bytes);
 
+/*
+ * Profiling twin of ssd_bwd: the same computation, plus a hipEvent_t recorded
+ * on `stream` before the first stage and after every stage, so that a caller
+ * can time the stages (kernels) of the backward inside its own timed region
+ * without synchronising.  `events` points to ssd_bwd_stage_count() + 1
+ * hipEvent_t handles, created (with timing enabled) and owned by the caller;
+ * none may be NULL.  Stage i runs between events[i] and events[i + 1].
+ */
+int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                     const void* B, const void* C, const float* D, const void* dy,
+                     const float* initial_states, const int32_t* seq_idx,
+                     void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+                     float* d_initial_states, void* workspace, size_t workspace_bytes,
+                     void* stream, void* const* events);
+
+/* Number of stages of the backward and the name of stage i ("prep",
+ * "state_fwd", "state_bwd", "group_bwd", "head_bwd", "reduce"); NULL for an
+ * index out of range. */
+int ssd_bwd_stage_count(void);
+const char* ssd_bwd_stage_name(int stage);
+
 /* Library version, (major << 16) | minor. */
 int ssd_bwd_version(void);
 

@@ -110,11 +110,16 @@ extern "C" const char* ssd_status_string(int status) {
 
 extern "C" int ssd_bwd_version(void) { return (1 << 16) | 0; }
 
-extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A,
-                       const void* B, const void* C, const float* D, const void* dy,
-                       const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
-                       float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+const char* const kStageNames[] = {"prep", "state_fwd", "state_bwd", "group_bwd", "head_bwd", "reduce"};
+constexpr int kStages = 6;
+
+int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
+            const void* C, const float* D, const void* dy, const float* initial_states,
+            const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+            float* d_initial_states, void* workspace, size_t workspace_bytes, void* stream,
+            void* const* events) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !workspace)
@@ -127,6 +132,9 @@ extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, c
                         d_initial_states, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+  if (events)
+    for (int i = 0; i <= kStages; ++i)
+      if (!events[i]) return SSD_ERR_INVALID_ARG;
   const Layout L = make_layout(shape);
   if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
 
@@ -161,11 +169,43 @@ extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, c
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = is_bf16(shape);
-  if (ssd::launch_prep(pb, s) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_group_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_reduce(pb, s) != hipSuccess) return SSD_ERR_HIP;
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return SSD_ERR_HIP;
+  if (ssd::launch_prep(pb, s) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
+  if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
+  if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess || !mark(3)) return SSD_ERR_HIP;
+  if (ssd::launch_group_bwd(pb, bf16, s) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
+  if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess || !mark(5)) return SSD_ERR_HIP;
+  if (ssd::launch_reduce(pb, s) != hipSuccess || !mark(6)) return SSD_ERR_HIP;
   return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, const void* dy,
+                       const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
+                       float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(shape, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                                const void* B, const void* C, const float* D, const void* dy,
+                                const float* initial_states, const int32_t* seq_idx, void* dx,
+                                float* ddt, float* dA, void* dB, void* dC, float* dD,
+                                float* d_initial_states, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events) {
+  if (!events) return SSD_ERR_INVALID_ARG;
+  return run_bwd(shape, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, workspace, workspace_bytes, stream, events);
+}
+
+extern "C" int ssd_bwd_stage_count(void) { return kStages; }
+
+extern "C" const char* ssd_bwd_stage_name(int stage) {
+  return (stage >= 0 && stage < kStages) ? kStageNames[stage] : nullptr;
 }

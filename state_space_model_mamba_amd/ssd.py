@@ -21,7 +21,7 @@ SSD_IO_F32 = 1
 SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
-            "ssd_bwd_version")
+            "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name")
 
 
 class SsdShape(ctypes.Structure):
@@ -61,6 +61,12 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_version.argtypes = []
     lib.ssd_bwd.restype = ctypes.c_int
     lib.ssd_bwd.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp]
+    lib.ssd_bwd_profiled.restype = ctypes.c_int
+    lib.ssd_bwd_profiled.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp, ctypes.POINTER(vp)]
+    lib.ssd_bwd_stage_count.restype = ctypes.c_int
+    lib.ssd_bwd_stage_count.argtypes = []
+    lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
+    lib.ssd_bwd_stage_name.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -117,7 +123,7 @@ def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
 
 def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_d_initial_states: bool = True,
-            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None):
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
@@ -125,6 +131,8 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     seq_idx: (b, L) int32 or None.  ``nseqs`` (the number of sequence starts)
     is needed only when seq_idx is given without initial_states.
     Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states.
+    ``events``: optional list of stage_count() + 1 recorded torch.cuda.Event
+    (timing enabled) handed to the profiling entry point.
     """
     lib = load_library()
     dev = x.device
@@ -166,16 +174,22 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
                                  if want_d_initial_states and S > 0 else None),
         }
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssd_bwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
-                     _ptr(initial_states), _ptr(seq_idx), _ptr(out["dx"]), _ptr(out["ddt"]),
-                     _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-                     _ptr(out["d_initial_states"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                     ctypes.c_void_p(stream))
+    args = [ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+            _ptr(initial_states), _ptr(seq_idx), _ptr(out["dx"]), _ptr(out["ddt"]),
+            _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+            _ptr(out["d_initial_states"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            ctypes.c_void_p(stream)]
+    if events is None:
+        rc = lib.ssd_bwd(*args)
+    else:
+        handles = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        rc = lib.ssd_bwd_profiled(*args, handles)
     if rc:
         raise SsdError(rc, "ssd_bwd")
-    out["workspace"] = workspace
-    out["shape"] = shape
-    return out
+    res = dict(out)
+    res["workspace"] = workspace
+    res["shape"] = shape
+    return res
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:
@@ -188,3 +202,16 @@ def workspace_view(result: dict, region: int) -> torch.Tensor:
     if region == SSD_WS_ACS:
         return flat.view(shape.batch, shape.nheads, nc, shape.chunk_size)
     return flat.view(shape.batch, shape.nheads, nc, shape.headdim, shape.dstate)
+
+
+def stage_names() -> list[str]:
+    lib = load_library()
+    return [lib.ssd_bwd_stage_name(i).decode() for i in range(lib.ssd_bwd_stage_count())]
+
+
+def make_stage_events(stream=None) -> list:
+    """stage_count() + 1 timing events, each recorded once so that its HIP handle exists."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(load_library().ssd_bwd_stage_count() + 1)]
+    for e in evs:
+        e.record(stream)
+    return evs
