@@ -45,6 +45,7 @@ def sizes(w, ntg):
         CH=w.batch * w.nheads * nc * w.chunk * 4,                  # one per-chunk fp32 vector
         OFFD=w.batch * w.nheads * nc * ntg * w.chunk * 4,
         SEG=w.batch * nc * w.chunk * 4,
+        DCB=w.batch * w.ngroups * nc * w.chunk * w.chunk * s,      # dCB tile (or its transpose)
     )
     return z
 
@@ -60,7 +61,8 @@ def stage_alg_bytes(z):
         "prep": z["DT"] + z["SEQ"] + 2 * z["CH"] + z["SEG"],
         "state_fwd": z["X"] + z["BC"] + 2 * z["CH"] + z["INIT"] + z["T"],
         "state_bwd": z["X"] + z["BC"] + z["CH"] + z["T"] + z["DINIT"],
-        "group_bwd": 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"],
+        "dcb": 2 * z["X"] + 2 * z["CH"] + z["SEG"] + 2 * z["DCB"],
+        "dbdc": 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"] + 2 * z["DCB"],
         "head_bwd": 3 * z["X"] + 2 * z["BC"] + z["T"] + 2 * z["CH"] + z["OFFD"] + 2 * z["DT"],
         "reduce": 0,
     }
@@ -196,7 +198,7 @@ def main():
                               ref[k].view(torch.uint8) if ref[k].dtype != torch.bfloat16 else ref[k].view(torch.int16))
                   for k in out)
 
-    ntg = N // (64 if N % 64 == 0 else (32 if N % 32 == 0 else 16))
+    ntg = N // next(t for t in (128, 64, 32, 16) if N % t == 0)
     z = sizes(w, ntg)
     sb = stage_alg_bytes(z)
     dom = max(stage_ms, key=stage_ms.get)

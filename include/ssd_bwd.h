@@ -147,8 +147,8 @@ int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, con
                      void* stream, void* const* events);
 
 /* Number of stages of the backward and the name of stage i ("prep",
- * "state_fwd", "state_bwd", "group_bwd", "head_bwd", "reduce"); NULL for an
- * index out of range. */
+ * "state_fwd", "state_bwd", "dcb", "dbdc", "head_bwd", "reduce"); NULL for
+ * an index out of range. */
 int ssd_bwd_stage_count(void);
 const char* ssd_bwd_stage_name(int stage);
 

@@ -34,17 +34,19 @@ namespace ssd {
 template <typename T, int Q, int P>
 struct HeadCfg {
   static constexpr int T16 = Q / 16;
-  static constexpr int W = T16 / 2;
+  static constexpr int W = causal_waves<Q>();
+  using Split = CausalSplit<T16, W>;
+  static constexpr int NCOL = Split::NCOL;
   static constexpr int NTHR = W * WAVE;
   static constexpr int NCAUS = T16 * (T16 + 1) / 2;
   static constexpr int PT = P / 16;
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int NS = sizeof(T) == 2 ? 64 : 32;   // dstate slab
+  static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab (divides N)
   static constexpr int LDN = NS + VEC;
   static constexpr int LDP = P + VEC;
-  static constexpr int NOWN = T16 + 1;
-  static constexpr size_t RA_A = (size_t(2) * Q * LDN + size_t(P) * LDN) * sizeof(T);
-  static constexpr size_t RA_B = size_t(2) * Q * LDP * sizeof(T);
+  static constexpr int NOWN = Split::NOWN;
+  static constexpr size_t RA_A = size_t(2) * Q * LDN * sizeof(T);                 // C, B slabs
+  static constexpr size_t RA_B = (size_t(2) * Q * LDP + size_t(Q + P) * LDN) * sizeof(T);  // x, dy rows + B, dS slabs
   static constexpr size_t RA = RA_A > RA_B ? RA_A : RA_B;
   // tile sums: rs, cs [NCAUS*16], tot [NCAUS], vdiag [T16*256], t1 [T16], rs2 [Q], cs3 [Q]
   static constexpr size_t RS_FLOATS = size_t(NCAUS) * 33 + size_t(T16) * 257 + size_t(2) * Q;
@@ -54,17 +56,6 @@ struct HeadCfg {
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
 };
-
-template <int T16>
-__device__ __forceinline__ void head_owned_tile(int w, int k, int& I, int& J) {
-  if (k < T16 - w) {
-    J = w;
-    I = w + k;
-  } else {
-    J = T16 - 1 - w;
-    I = J + (k - (T16 - w));
-  }
-}
 
 __device__ __forceinline__ int causal_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
@@ -78,10 +69,11 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   // phase A
   T* s_ck = reinterpret_cast<T*>(smem);
   T* s_bk = s_ck + Q * LDN;
-  T* s_dsk = s_bk + Q * LDN;
   // phase B (aliases phase A)
   T* s_xk = reinterpret_cast<T*>(smem);
   T* s_dyk = s_xk + Q * LDP;
+  T* s_bz = s_dyk + Q * LDP;
+  T* s_dsz = s_bz + Q * LDN;
   float* s_rs = reinterpret_cast<float*>(smem + Cf::OFF_RS);
   float* s_cs = s_rs + NCAUS * 16;
   float* s_tot = s_cs + NCAUS * 16;
@@ -134,64 +126,67 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     s_ee[i] = e;
     s_w[i] = e * s_dt[i];
   }
-  const int own0 = w, own1 = T16 - 1 - w;
+  constexpr int NCOL = Cf::NCOL;
 
-  // ---- phase A: CB (owned causal tiles) and Z^T = dS B^T, slab by slab over N
+  // Row sources of the global tiles this block stages (nullptr = zero row).
+  auto bc_row = [&](const T* base, int n0) {
+    return [=](int i) -> const T* {
+      const int t = c * Q + i;
+      return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 : nullptr;
+    };
+  };
+  auto head_row = [&](const T* base) {
+    return [=](int i) -> const T* {
+      const int t = c * Q + i;
+      return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
+    };
+  };
+  auto ds_row = [&](int n0) {
+    return [=](int p) -> const float* { return pb.dstate + (bhc * P + p) * pb.N + n0; };
+  };
+
+  // ---- phase A: CB over the owned causal tiles, slab by slab over N; the
+  // next slab is loaded into registers while the current one is multiplied
   f32x4_t cb[Cf::NOWN];
-  f32x4_t zt[2][PT];
 #pragma unroll
   for (int k = 0; k < Cf::NOWN; ++k) cb[k] = zero4();
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) zt[a][pt] = zero4();
+  RowStage<T, Q, NS, NTHR> st_c, st_b;
+  RowStage<T, Q, P, NTHR> st_x, st_dy;
+  st_c.load(bc_row(Cg, 0));
+  st_b.load(bc_row(Bg, 0));
   for (int n0 = 0; n0 < pb.N; n0 += NS) {
     __syncthreads();
-    for (int v = tid; v < Q * NS / VEC; v += NTHR) {
-      const int i = v / (NS / VEC), nv = v % (NS / VEC), n = n0 + nv * VEC, t = c * Q + i;
-      uint4 uc = zero_u4(), ub = zero_u4();
-      if (t < pb.L && n < pb.N) {
-        const int64_t off = ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n;
-        uc = ld_global16(Cg + off);
-        ub = ld_global16(Bg + off);
-      }
-      *reinterpret_cast<uint4*>(s_ck + i * LDN + nv * VEC) = uc;
-      *reinterpret_cast<uint4*>(s_bk + i * LDN + nv * VEC) = ub;
-    }
-    for (int v = tid; v < P * NS; v += NTHR) {
-      const int p = v / NS, ns = v % NS, n = n0 + ns;
-      s_dsk[p * LDN + ns] = Elem<T>::from_f(n < pb.N ? pb.dstate[(bhc * P + p) * pb.N + n] : 0.f);
-    }
+    st_c.store(s_ck, LDN);
+    st_b.store(s_bk, LDN);
     __syncthreads();
-#pragma unroll
+    if (n0 + NS < pb.N) {
+      st_c.load(bc_row(Cg, n0 + NS));
+      st_b.load(bc_row(Bg, n0 + NS));
+    } else {
+      st_x.load(head_row(xg));
+      st_dy.load(head_row(dyg));
+    }
+    const int z = opaque_zero();
+    const int wz = w + z;
+#pragma clang loop unroll(full)
     for (int k = 0; k < Cf::NOWN; ++k) {
       int I, J;
-      head_owned_tile<T16>(w, k, I, J);
-      cb[k] = tile_mma_kk<T>(cb[k], s_ck + 16 * I * LDN, LDN, s_bk + 16 * J * LDN, LDN, 0, NS);
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int J = a == 0 ? own0 : own1;
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-        zt[a][pt] = tile_mma_kk<T>(zt[a][pt], s_dsk + 16 * pt * LDN, LDN, s_bk + 16 * J * LDN, LDN, 0, NS);
+      bool second;
+      Cf::Split::tile(wz, k, I, J, second);
+      cb[k] = tile_mma_kk<T>(cb[k], s_ck + z + 16 * I * LDN, LDN, s_bk + z + 16 * J * LDN, LDN, 0, NS);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
 
   // ---- phase B: x, dy rows; decays; M; ddt_intra; V tile sums; dx_intra
-  for (int v = tid; v < Q * P / VEC; v += NTHR) {
-    const int j = v / (P / VEC), pv = v % (P / VEC), t = c * Q + j;
-    uint4 ux = zero_u4(), ud = zero_u4();
-    if (t < pb.L) {
-      const int64_t off = ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * VEC;
-      ux = ld_global16(xg + off);
-      ud = ld_global16(dyg + off);
-    }
-    *reinterpret_cast<uint4*>(s_xk + j * LDP + pv * VEC) = ux;
-    *reinterpret_cast<uint4*>(s_dyk + j * LDP + pv * VEC) = ud;
-  }
+  st_x.store(s_xk, LDP);
+  st_dy.store(s_dyk, LDP);
   __syncthreads();
+  // first slab of phase B2 in flight during phase B
+  RowStage<float, P, NS, NTHR> st_ds;
+  st_b.load(bc_row(Bg, 0));
+  st_ds.load(ds_row(0));
   {
     float dd = 0.f;
     for (int v = tid; v < Q * P; v += NTHR) {
@@ -202,17 +197,19 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     if (l == 0) s_red[w] = dd;
   }
 
-  f32x4_t dxt[2][PT];
+  f32x4_t dxt[NCOL][PT];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NCOL; ++a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) dxt[a][pt] = zero4();
-  float ddti[2] = {0.f, 0.f};
+  float ddti[NCOL];
 #pragma unroll
+  for (int a = 0; a < NCOL; ++a) ddti[a] = 0.f;
+#pragma clang loop unroll(full)
   for (int k = 0; k < Cf::NOWN; ++k) {
     int I, J;
-    head_owned_tile<T16>(w, k, I, J);
-    const int a = (k < T16 - w) ? 0 : 1;
+    bool second;
+    Cf::Split::tile(w, k, I, J, second);
     const f32x4_t m = tile_mma_kk<T>(zero4(), s_dyk + 16 * I * LDP, LDP, s_xk + 16 * J * LDP, LDP, 0, P);
     const int j = 16 * J + r16;
     const int loj = seg_lo(s_seg[j]);
@@ -222,14 +219,16 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * I + 4 * kg + r;
       const bool ok = (j <= i) && (seg_lo(s_seg[i]) == loj);
-      const float gv = ok ? cb[k][r] * expf(s_acs[i] - aj) : 0.f;
+      // exp of a non-positive argument only; masked entries use a zero argument
+      const float e = expf(ok ? s_acs[i] - aj : 0.f);
+      const float gv = ok ? cb[k][r] * e : 0.f;
       cb[k][r] = gv;
       const float gm = gv * m[r];
       colgm += gm;
       vr[r] = gm * dtj;
       colv += vr[r];
     }
-    ddti[a] += sum_kgroups(colgm);
+    colgm = sum_kgroups(colgm);
     const int tix = causal_index(I, J);
     colv = sum_kgroups(colv);
     if (kg == 0) s_cs[tix * 16 + r16] = colv;
@@ -244,20 +243,59 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_vdiag[I * 256 + (4 * kg + r) * 16 + r16] = vr[r];
     }
+    float av[PT][4];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      float av[4];
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = Elem<T>::to_f(s_dyk[(16 * I + 4 * kg + r) * LDP + 16 * pt + r16]);
-      dxt[a][pt] = Mma<T>::mma_regdirect(av, cb[k], dxt[a][pt]);
+      for (int r = 0; r < 4; ++r) av[pt][r] = Elem<T>::to_f(s_dyk[(16 * I + 4 * kg + r) * LDP + 16 * pt + r16]);
+    // dx^T of the tile's column: slot 2q or 2q+1 of its pair (a wave-uniform
+    // choice); both slot indices are constants once the loop is unrolled
+    const int q = k / (T16 + 1);
+    if (!second) {
+      ddti[2 * q] += colgm;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) dxt[2 * q][pt] = Mma<T>::mma_regdirect(av[pt], cb[k], dxt[2 * q][pt]);
+    } else {
+      ddti[2 * q + 1] += colgm;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        dxt[2 * q + 1][pt] = Mma<T>::mma_regdirect(av[pt], cb[k], dxt[2 * q + 1][pt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- phase B2: Z^T = dS B^T for the owned column tiles, slab by slab over N
+  // (x and dy rows stay in LDS; B and dS slabs go to the region behind them)
+  f32x4_t zt[NCOL][PT];
+#pragma unroll
+  for (int a = 0; a < NCOL; ++a)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) zt[a][pt] = zero4();
+  for (int n0 = 0; n0 < pb.N; n0 += NS) {
+    __syncthreads();
+    st_b.store(s_bz, LDN);
+    st_ds.template store_convert<T>(s_dsz, LDN);
+    __syncthreads();
+    if (n0 + NS < pb.N) {
+      st_b.load(bc_row(Bg, n0 + NS));
+      st_ds.load(ds_row(n0 + NS));
+    }
+    const int z = opaque_zero();
+    const int wz = w + z;
+#pragma unroll
+    for (int a = 0; a < NCOL; ++a) {
+      const int J = Cf::Split::col(wz, a);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        zt[a][pt] = tile_mma_kk<T>(zt[a][pt], s_dsz + z + 16 * pt * LDN, LDN, s_bz + z + 16 * J * LDN, LDN, 0, NS);
     }
   }
 
   // ---- phase C: dx, and per column the ddt parts and s_j
   const float Dh = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int J = a == 0 ? own0 : own1;
+  for (int a = 0; a < NCOL; ++a) {
+    const int J = Cf::Split::col(w, a);
     const int j = 16 * J + r16, t = c * Q + j;
     const float dtj = s_dt[j], wj = s_w[j], eej = s_ee[j];
     float xz = 0.f;

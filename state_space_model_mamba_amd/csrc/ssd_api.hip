@@ -12,7 +12,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, hin, dstate, offd, endd, slot_dA, slot_dD, total;
+  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, offd, endd, slot_dA, slot_dD, total;
   int nc, ntg;
 };
 
@@ -59,6 +59,9 @@ Layout make_layout(const ssd_shape* s) {
   L.dtc = take(B * H * nc * Q * 4);
   L.hin = take(B * H * nc * P * N * 4);
   L.dstate = take(B * H * nc * P * N * 4);
+  const size_t es = is_bf16(s) ? 2 : 4;
+  L.dcb = take(B * s->ngroups * nc * Q * Q * es);
+  L.dcbt = take(B * s->ngroups * nc * Q * Q * es);
   L.offd = take(B * H * nc * ntg * Q * 4);
   L.endd = take(B * H * nc * ntg * 4);
   L.slot_dA = take(B * nc * H * 4);
@@ -112,8 +115,8 @@ extern "C" int ssd_bwd_version(void) { return (1 << 16) | 0; }
 
 namespace {
 
-const char* const kStageNames[] = {"prep", "state_fwd", "state_bwd", "group_bwd", "head_bwd", "reduce"};
-constexpr int kStages = 6;
+const char* const kStageNames[] = {"prep", "state_fwd", "state_bwd", "dcb", "dbdc", "head_bwd", "reduce"};
+constexpr int kStages = 7;
 
 int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
             const void* C, const float* D, const void* dy, const float* initial_states,
@@ -162,6 +165,8 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
   pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
   pb.hin = reinterpret_cast<float*>(ws + L.hin);
   pb.dstate = reinterpret_cast<float*>(ws + L.dstate);
+  pb.dcb = ws + L.dcb;
+  pb.dcbt = ws + L.dcbt;
   pb.offd = reinterpret_cast<float*>(ws + L.offd);
   pb.endd = reinterpret_cast<float*>(ws + L.endd);
   pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
@@ -176,9 +181,10 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
   if (ssd::launch_prep(pb, s) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
   if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
   if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess || !mark(3)) return SSD_ERR_HIP;
-  if (ssd::launch_group_bwd(pb, bf16, s) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
-  if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess || !mark(5)) return SSD_ERR_HIP;
-  if (ssd::launch_reduce(pb, s) != hipSuccess || !mark(6)) return SSD_ERR_HIP;
+  if (ssd::launch_dcb(pb, bf16, s) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
+  if (ssd::launch_dbdc(pb, bf16, s) != hipSuccess || !mark(5)) return SSD_ERR_HIP;
+  if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess || !mark(6)) return SSD_ERR_HIP;
+  if (ssd::launch_reduce(pb, s) != hipSuccess || !mark(7)) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

@@ -123,6 +123,16 @@ __device__ __forceinline__ f32x4_t tile_mma_kk(f32x4_t acc, const T* a_base, int
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// A zero the compiler cannot see through.  Adding it to an LDS base pointer
+// inside a loop keeps the per-tile addresses derived from that base from
+// being hoisted out of the loop and held live (which otherwise costs one
+// register per address per tile across the whole loop).
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("; opaque zero" : "=s"(z) : "0"(0));
+  return z;
+}
+
 // Sum over the 16 lanes that share lane / 16 (fixed butterfly order).
 __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1, WAVE);

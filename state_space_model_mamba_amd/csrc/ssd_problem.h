@@ -23,7 +23,7 @@ __host__ __device__ inline int seg_rank(int v) { return v >> 16; }
 
 struct Problem {
   int B, L, H, P, G, N, Q, nc, hpg, nseqs;
-  int ntg;  // number of dstate tiles in the group kernel
+  int ntg;  // number of dstate tiles of the dB/dC kernel
   // inputs
   const void* x;
   const float* dt;
@@ -49,6 +49,8 @@ struct Problem {
   float* dtc;        // (B, H, nc, Q)
   float* hin;        // (B, H, nc, P, N)
   float* dstate;     // (B, H, nc, P, N)
+  void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB
+  void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose
   float* offd;       // (B, H, nc, ntg, Q)
   float* endd;       // (B, H, nc, ntg)
   float* slot_dA;    // (B, nc, H)
@@ -60,7 +62,8 @@ struct Problem {
 hipError_t launch_prep(const Problem& pb, hipStream_t s);
 hipError_t launch_state_fwd(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_state_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
-hipError_t launch_group_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_dcb(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_dbdc(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_head_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_reduce(const Problem& pb, hipStream_t s);
 

@@ -29,6 +29,69 @@ template <typename T> __device__ __forceinline__ float vget(const uint4& v, int 
   return Elem<T>::to_f(vraw<T>(v, e));
 }
 
+// ---------------------------------------------------------------------------
+// Block-wide staging of a ROWS x COLS tile from global memory (rows given by
+// a functor returning the row's first element, or nullptr for a zero row)
+// into LDS.  All of a thread's 16-byte loads are issued before any LDS store,
+// so a stage costs one memory latency instead of one per loop trip.
+// ---------------------------------------------------------------------------
+template <typename TIN, int ROWS, int COLS, int NTHR>
+struct RowStage {
+  static constexpr int VEC = Vec16<TIN>::N;
+  static constexpr int CV = COLS / VEC;                 // vectors per row
+  static constexpr int NV = ROWS * CV;
+  static constexpr int IT = (NV + NTHR - 1) / NTHR;     // vectors per thread
+  static_assert(COLS % VEC == 0, "row length must be a multiple of 16 bytes");
+  uint4 buf[IT];
+
+  template <typename RowPtr>
+  __device__ __forceinline__ void load(RowPtr rowptr) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      buf[k] = zero_u4();
+      if (NV % NTHR == 0 || v < NV) {
+        const TIN* p = rowptr(v / CV);
+        if (p) buf[k] = ld_global16(p + (v % CV) * VEC);
+      }
+    }
+  }
+  // row-major into LDS (same element type): lds[r * ld + c]
+  __device__ __forceinline__ void store(TIN* lds, int ld) const {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      if (NV % NTHR == 0 || v < NV) *reinterpret_cast<uint4*>(lds + (v / CV) * ld + (v % CV) * VEC) = buf[k];
+    }
+  }
+  // row-major with conversion: lds[r * ld + c] = TOUT(x)
+  template <typename TOUT>
+  __device__ __forceinline__ void store_convert(TOUT* lds, int ld) const {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      if (NV % NTHR == 0 || v < NV) {
+        const int r = v / CV, c0 = (v % CV) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lds[r * ld + c0 + e] = Elem<TOUT>::from_f(vget<TIN>(buf[k], e));
+      }
+    }
+  }
+  // transposed with conversion: lds[c * ld + r] = TOUT(x)
+  template <typename TOUT>
+  __device__ __forceinline__ void store_transposed(TOUT* lds, int ld) const {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      if (NV % NTHR == 0 || v < NV) {
+        const int r = v / CV, c0 = (v % CV) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) lds[(c0 + e) * ld + r] = Elem<TOUT>::from_f(vget<TIN>(buf[k], e));
+      }
+    }
+  }
+};
+
 // Masked KW-fragment of a K-major operand: elements whose k index falls
 // outside [lo, hi) read as zero.
 template <typename T>
@@ -60,6 +123,43 @@ __device__ __forceinline__ f32x4_t tile_mma_kk_range(f32x4_t acc, const T* a_bas
   for (int k = kb; k < hi; k += KS)
     acc = Mma<T>::mma(load_k_masked<T>(ap + k, k + kg * KW, lo, hi), Mma<T>::load_k(bp + k), acc);
   return acc;
+}
+
+// The causal 16x16 tiles (I >= J) of a Q x Q matrix, T = Q/16 tiles per side,
+// split over W waves.  Column tiles are paired as {p, T-1-p} (T+1 causal tiles
+// per pair, so every pair costs the same); wave w owns the pairs
+// p = w, w + W, ... < T/2 and all causal tiles of their columns.
+template <int T16, int W>
+struct CausalSplit {
+  static_assert(T16 % 2 == 0 && (T16 / 2) % W == 0, "pairs must split evenly over the waves");
+  static constexpr int PPW = T16 / 2 / W;        // pairs per wave
+  static constexpr int NOWN = PPW * (T16 + 1);   // causal tiles per wave
+  static constexpr int NCOL = 2 * PPW;           // owned column tiles per wave
+  // column tile of owned slot a (slots 2q, 2q+1 are the two columns of pair q)
+  static __device__ __forceinline__ int col(int w, int a) {
+    const int p = w + W * (a >> 1);
+    return (a & 1) ? T16 - 1 - p : p;
+  }
+  // tile k of wave w: rows I >= J of column J; `second` tells which column of
+  // its pair (slot 2q + second) the tile belongs to (wave-uniform)
+  static __device__ __forceinline__ void tile(int w, int k, int& I, int& J, bool& second) {
+    const int q = k / (T16 + 1), kk = k % (T16 + 1);
+    const int p = w + W * q;
+    second = kk >= T16 - p;
+    if (!second) {
+      J = p;
+      I = p + kk;
+    } else {
+      J = T16 - 1 - p;
+      I = J + (kk - (T16 - p));
+    }
+  }
+};
+
+// waves of the blocks that own causal tiles: one per SIMD, at most T/2
+template <int Q>
+constexpr int causal_waves() {
+  return (Q / 32) < 4 ? (Q / 32) : 4;
 }
 
 __device__ __forceinline__ int clamp_seq(int s, int nseqs) {
