@@ -109,7 +109,7 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
         const int i = 16 * I + 4 * kg + r;
         const bool ok = (j <= i) && (lov[i] == loj);
         // exp of a non-positive argument only; masked entries use a zero argument
-        const float e = expf(ok ? acs[i] - aj : 0.f);
+        const float e = Elem<T>::exp(ok ? acs[i] - aj : 0.f);
         dcb[k][r] += (ok ? e * dtj : 0.f) * m[r];
       }
       // keep the scheduler from hoisting every tile's fragment loads at once
@@ -290,7 +290,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dbdc(Problem 
     const int h = g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
     __syncthreads();
-    for (int i = tid; i < Q; i += NTHR) s_v[i] = expf(pb.acs[bhc * Q + i]);
+    for (int i = tid; i < Q; i += NTHR) s_v[i] = Elem<T>::exp(pb.acs[bhc * Q + i]);
     {
       RowStage<T, Q, P, NTHR> st_dy;
       st_dy.load(head_row(dyg, h));
@@ -388,7 +388,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dbdc(Problem 
     __syncthreads();
     const float acs_end = pb.acs[bhc * Q + Q - 1];
     for (int i = tid; i < Q; i += NTHR)
-      s_v[i] = (i >= lolast) ? expf(acs_end - pb.acs[bhc * Q + i]) * pb.dtc[bhc * Q + i] : 0.f;
+      s_v[i] = (i >= lolast) ? Elem<T>::exp(acs_end - pb.acs[bhc * Q + i]) * pb.dtc[bhc * Q + i] : 0.f;
     {
       RowStage<T, Q, P, NTHR> st_x;
       RowStage<float, P, NTG, NTHR> st_s;

@@ -122,7 +122,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const int lolast = seg_lo(s_seg[Q - 1]);
   const float acs_end = s_acs[Q - 1];
   for (int i = tid; i < Q; i += NTHR) {
-    const float e = (i >= lolast) ? expf(acs_end - s_acs[i]) : 0.f;
+    const float e = (i >= lolast) ? Elem<T>::exp(acs_end - s_acs[i]) : 0.f;
     s_ee[i] = e;
     s_w[i] = e * s_dt[i];
   }
@@ -220,7 +220,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
       const int i = 16 * I + 4 * kg + r;
       const bool ok = (j <= i) && (seg_lo(s_seg[i]) == loj);
       // exp of a non-positive argument only; masked entries use a zero argument
-      const float e = expf(ok ? s_acs[i] - aj : 0.f);
+      const float e = Elem<T>::exp(ok ? s_acs[i] - aj : 0.f);
       const float gv = ok ? cb[k][r] * e : 0.f;
       cb[k][r] = gv;
       const float gm = gv * m[r];
@@ -243,23 +243,23 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_vdiag[I * 256 + (4 * kg + r) * 16 + r16] = vr[r];
     }
-    float av[PT][4];
+    // register-direct operands: dy^T values (raw) and the G tile (converted once)
+    typename Mma<T>::rfrag av[PT];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) av[pt][r] = Elem<T>::to_f(s_dyk[(16 * I + 4 * kg + r) * LDP + 16 * pt + r16]);
+    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load(s_dyk + (16 * I + 4 * kg) * LDP + 16 * pt + r16, LDP);
+    const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
     // dx^T of the tile's column: slot 2q or 2q+1 of its pair (a wave-uniform
     // choice); both slot indices are constants once the loop is unrolled
     const int q = k / (T16 + 1);
     if (!second) {
       ddti[2 * q] += colgm;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) dxt[2 * q][pt] = Mma<T>::mma_regdirect(av[pt], cb[k], dxt[2 * q][pt]);
+      for (int pt = 0; pt < PT; ++pt) dxt[2 * q][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q][pt]);
     } else {
       ddti[2 * q + 1] += colgm;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
-        dxt[2 * q + 1][pt] = Mma<T>::mma_regdirect(av[pt], cb[k], dxt[2 * q + 1][pt]);
+        dxt[2 * q + 1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q + 1][pt]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -363,7 +363,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
       for (int jj = 0; jj < kap; ++jj) t4 += s_vdiag[K * 256 + ii * 16 + jj];
     s_daint[k] = ((s_t1[K] + t2) + t3) + t4;
   }
-  if (tid == 0) s_dd[Q - 1] += sum_s + expf(acs_end) * endd;
+  if (tid == 0) s_dd[Q - 1] += sum_s + Elem<T>::exp(acs_end) * endd;
   __syncthreads();
   if (w == 0) {
     // reverse in-chunk, in-segment cumulative sum of ddAcs (fixed order)

@@ -131,14 +131,14 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
     }
     __syncthreads();
     if (tid < Q)
-      s_w[tid] = (tid >= s_lolast) ? expf(s_acs_end - pb.acs[bhc * Q + tid]) * pb.dtc[bhc * Q + tid] : 0.f;
+      s_w[tid] = (tid >= s_lolast) ? Elem<T>::exp(s_acs_end - pb.acs[bhc * Q + tid]) * pb.dtc[bhc * Q + tid] : 0.f;
     __syncthreads();
     stage_chunk_rows<T, Q, P, NT>(xr, br, s_w, s_xt, s_bt);
     __syncthreads();
     if (c + 1 < pb.nc) load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, c + 1, xr, br);
 
     const int kb = (s_lolast / Mma<T>::KSTEP) * Mma<T>::KSTEP;
-    const float decay = expf(s_acs_end);
+    const float decay = Elem<T>::exp(s_acs_end);
     const int nstart = s_nstart;
     const int s_last = clamp_seq(s_seqbase + nstart - 1, pb.nseqs);
 #pragma unroll
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
       s_segstart[0] = 0;
     }
     if (tid < Q) {
-      s_e[tid] = expf(pb.acs[bhc * Q + tid]);
+      s_e[tid] = Elem<T>::exp(pb.acs[bhc * Q + tid]);
       s_seg[tid] = pb.segpos[bc * Q + tid];
     }
     __syncthreads();
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
     __syncthreads();
     if (c > 0) load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, c - 1, xr, br);
 
-    const float decay = expf(s_acs_end);
+    const float decay = Elem<T>::exp(s_acs_end);
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
       const int tile = w + 4 * k;

@@ -11,7 +11,8 @@
 // * "register-direct" products: an accumulator tile X (rows = k) used as the
 //   B operand of a K = 16 contraction, Out[m][n] = sum_k A[m][k] X[k][n],
 //   without a round trip through LDS.
-// * wave-level scans and reductions in a fixed shuffle order.
+// * wave-level reductions in registers (DPP row operations and the gfx950
+//   row swaps), each in one fixed order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,21 +33,23 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
+// round to nearest even (the hardware v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_f32(v); }
   static __device__ __forceinline__ bf16_t from_f(float f) { return f32_to_bf16(f); }
+  // exp of the decay factors: the hardware exp2 path (about 1 ulp), ample next
+  // to bf16 operands
+  static __device__ __forceinline__ float exp(float x) { return __expf(x); }
 };
 template <> struct Elem<float> {
   static __device__ __forceinline__ float to_f(float v) { return v; }
   static __device__ __forceinline__ float from_f(float f) { return f; }
+  static __device__ __forceinline__ float exp(float x) { return expf(x); }
 };
 
 template <typename T> struct Mma;
@@ -71,17 +74,24 @@ template <> struct Mma<bf16_t> {
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // Out += A * X where X is an accumulator tile (k = its row index) and
-  // a[r] = A[m = lane % 16][k = 4 * (lane / 16) + r].
-  static __device__ __forceinline__ f32x4_t mma_regdirect(const float a[4], f32x4_t x, f32x4_t c) {
-    u16x4_t av, bv;
+  // Register-direct products: Out += A * X where X is an accumulator tile
+  // (k = its row index), with rd-fragments holding 4 k-values per lane:
+  //   A: a[r] = A[m = lane % 16][k = 4 * (lane / 16) + r]
+  //   X: the tile's own 4 values per lane.
+  typedef s16x4_t rfrag;
+  static __device__ __forceinline__ rfrag rfrag_from_acc(f32x4_t x) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(rfrag, __builtin_convertvector(x, bf16x4_t));
+  }
+  // 4 values at p, p + stride, p + 2 stride, p + 3 stride
+  static __device__ __forceinline__ rfrag rfrag_load(const bf16_t* p, int stride) {
+    u16x4_t v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      av[r] = f32_to_bf16(a[r]);
-      bv[r] = f32_to_bf16(x[r]);
-    }
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, av),
-                                                     __builtin_bit_cast(s16x4_t, bv), c, 0, 0, 0);
+    for (int r = 0; r < 4; ++r) v[r] = p[r * stride];
+    return __builtin_bit_cast(rfrag, v);
+  }
+  static __device__ __forceinline__ f32x4_t mma_rd(rfrag a, rfrag x, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, x, c, 0, 0, 0);
   }
 };
 
@@ -95,7 +105,12 @@ template <> struct Mma<float> {
   static __device__ __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f32x4_t mma_regdirect(const float a[4], f32x4_t x, f32x4_t c) {
+  typedef f32x4_t rfrag;
+  static __device__ __forceinline__ rfrag rfrag_from_acc(f32x4_t x) { return x; }
+  static __device__ __forceinline__ rfrag rfrag_load(const float* p, int stride) {
+    return f32x4_t{p[0], p[stride], p[2 * stride], p[3 * stride]};
+  }
+  static __device__ __forceinline__ f32x4_t mma_rd(rfrag a, rfrag x, f32x4_t c) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], x[r], c, 0, 0, 0);
     return c;
@@ -133,28 +148,50 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
-// Sum over the 16 lanes that share lane / 16 (fixed butterfly order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row (the lanes sharing lane / 16), in registers
+// (DPP quad permutes, then row rotations by 4 and 8).  Every lane receives a
+// sum of the same 16 values; the association differs between the quads of a
+// row, so callers read the result from one fixed lane (lane % 16 == 0).
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, WAVE);
-  v += __shfl_xor(v, 2, WAVE);
-  v += __shfl_xor(v, 4, WAVE);
-  v += __shfl_xor(v, 8, WAVE);
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x124>(v);  // row_ror:4
+  v += dpp_move<0x128>(v);  // row_ror:8
   return v;
 }
 
-// Sum over the 4 lanes that share lane % 16 (fixed butterfly order).
+// Sum over the 4 lanes that share lane % 16 (one per row), with the gfx950
+// row swaps; all four lanes receive identical bits.
+// v_permlane16_swap / v_permlane32_swap exchange lanes between their two
+// register operands (odd rows of the first with even rows of the second, and
+// the upper half of the first with the lower half of the second); both
+// operands are outputs, so they are issued here with both bound read-write.
+// The s_nop padding covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void permlane16_swap(unsigned& a, unsigned& b) {
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(unsigned& a, unsigned& b) {
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+
+// Sum over the 4 lanes that share lane % 16 (one per row); all four lanes
+// receive identical bits.
 __device__ __forceinline__ float sum_kgroups(float v) {
-  v += __shfl_xor(v, 16, WAVE);
-  v += __shfl_xor(v, 32, WAVE);
-  return v;
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  permlane16_swap(a, b);   // a = (r0, r0, r2, r2), b = (r1, r1, r3, r3)
+  const float y = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  unsigned c = __builtin_bit_cast(unsigned, y), d = c;
+  permlane32_swap(c, d);   // c = (lo, lo), d = (hi, hi)
+  return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
 }
 
-// Sum over the whole wave (fixed butterfly order); every lane gets the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
-}
+// Sum over the whole wave; lane 0's result is the one to use.
+__device__ __forceinline__ float wave_sum(float v) { return sum_kgroups(sum16(v)); }
 
 // Remap a linear block id so that consecutive logical ids run on the same XCD
 // (MI355X dispatches block i to XCD i % 8), which lets blocks that read the
