@@ -66,6 +66,30 @@ __device__ __forceinline__ void load_chunk_rows(const Problem& pb, const void* s
   }
 }
 
+// Metadata of one (batch, head, chunk): this thread's position (tid < Q) and
+// the chunk-wide values every thread needs.
+struct ChunkMeta {
+  float acs, dt, acs_end;
+  int seg, lolast, nstart, seqbase;
+  __device__ __forceinline__ void load(const Problem& pb, int b, int h, int c) {
+    const int tid = threadIdx.x;
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
+    acs = 0.f;
+    dt = 0.f;
+    seg = 0;
+    if (tid < pb.Q) {
+      acs = pb.acs[bhc * pb.Q + tid];
+      dt = pb.dtc[bhc * pb.Q + tid];
+      seg = pb.segpos[bc * pb.Q + tid];
+    }
+    acs_end = pb.acs[bhc * pb.Q + pb.Q - 1];
+    lolast = seg_lo(pb.segpos[bc * pb.Q + pb.Q - 1]);
+    nstart = pb.cinfo[bc * CINFO + 0];
+    seqbase = pb.cinfo[bc * CINFO + 3];
+  }
+};
+
 // x (or dy) chunk -> LDS, transposed to [p][j] and scaled by s_scale[j];
 // B (or C) tile -> LDS transposed to [n][j].
 template <typename T, int Q, int P, int NT>
@@ -102,8 +126,6 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
   __shared__ __attribute__((aligned(16))) T s_xt[P * Cf::LDQ];
   __shared__ __attribute__((aligned(16))) T s_bt[NT * Cf::LDQ];
   __shared__ float s_w[Q];
-  __shared__ float s_acs_end;
-  __shared__ int s_nstart, s_seqbase, s_lolast;
 
   const int ntiles = pb.N / NT;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
@@ -119,28 +141,26 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
 #pragma unroll
   for (int k = 0; k < Cf::TPW; ++k) st[k] = zero4();
 
+  // per-chunk metadata, prefetched into registers one chunk ahead together
+  // with the chunk's x / B rows
+  ChunkMeta cur, nxt;
+  cur.load(pb, b, h, 0);
   load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, 0, xr, br);
   for (int c = 0; c < pb.nc; ++c) {
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-    if (tid == 0) {
-      s_nstart = pb.cinfo[bc * CINFO + 0];
-      s_seqbase = pb.cinfo[bc * CINFO + 3];
-      s_lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
-      s_acs_end = pb.acs[bhc * Q + Q - 1];
-    }
-    __syncthreads();
-    if (tid < Q)
-      s_w[tid] = (tid >= s_lolast) ? Elem<T>::exp(s_acs_end - pb.acs[bhc * Q + tid]) * pb.dtc[bhc * Q + tid] : 0.f;
+    if (tid < Q) s_w[tid] = (tid >= cur.lolast) ? Elem<T>::exp(cur.acs_end - cur.acs) * cur.dt : 0.f;
     __syncthreads();
     stage_chunk_rows<T, Q, P, NT>(xr, br, s_w, s_xt, s_bt);
     __syncthreads();
-    if (c + 1 < pb.nc) load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, c + 1, xr, br);
+    if (c + 1 < pb.nc) {
+      nxt.load(pb, b, h, c + 1);
+      load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, c + 1, xr, br);
+    }
 
-    const int kb = (s_lolast / Mma<T>::KSTEP) * Mma<T>::KSTEP;
-    const float decay = Elem<T>::exp(s_acs_end);
-    const int nstart = s_nstart;
-    const int s_last = clamp_seq(s_seqbase + nstart - 1, pb.nseqs);
+    const int kb = (cur.lolast / Mma<T>::KSTEP) * Mma<T>::KSTEP;
+    const float decay = Elem<T>::exp(cur.acs_end);
+    const int nstart = cur.nstart;
+    const int s_last = clamp_seq(cur.seqbase + nstart - 1, pb.nseqs);
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
       const int tile = w + 4 * k;
@@ -164,6 +184,7 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
       }
     }
     __syncthreads();
+    cur = nxt;
   }
 }
 
@@ -175,8 +196,6 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
   __shared__ float s_e[Q];
   __shared__ int s_seg[Q];
   __shared__ int s_segstart[Q + 1];
-  __shared__ float s_acs_end;
-  __shared__ int s_nstart, s_seqbase;
 
   const int ntiles = pb.N / NT;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
@@ -192,31 +211,30 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
 #pragma unroll
   for (int k = 0; k < Cf::TPW; ++k) dout[k] = zero4();
 
+  ChunkMeta cur, nxt;
+  cur.load(pb, b, h, pb.nc - 1);
   load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, pb.nc - 1, xr, br);
   for (int c = pb.nc - 1; c >= 0; --c) {
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-    if (tid == 0) {
-      s_nstart = pb.cinfo[bc * CINFO + 0];
-      s_seqbase = pb.cinfo[bc * CINFO + 3];
-      s_acs_end = pb.acs[bhc * Q + Q - 1];
-      s_segstart[0] = 0;
-    }
     if (tid < Q) {
-      s_e[tid] = Elem<T>::exp(pb.acs[bhc * Q + tid]);
-      s_seg[tid] = pb.segpos[bc * Q + tid];
+      s_e[tid] = Elem<T>::exp(cur.acs);
+      s_seg[tid] = cur.seg;
     }
+    if (tid == 0) s_segstart[0] = 0;
     __syncthreads();
-    const int nstart = s_nstart;
+    const int nstart = cur.nstart;
     const int start0 = seg_rank(s_seg[0]);  // 1 when a sequence starts at position 0
     const int nseg = nstart + 1 - start0;
-    if (tid < Q && tid > 0 && seg_lo(s_seg[tid]) == tid) s_segstart[seg_rank(s_seg[tid]) - start0] = tid;
+    if (tid < Q && tid > 0 && seg_lo(cur.seg) == tid) s_segstart[seg_rank(cur.seg) - start0] = tid;
     if (tid == 0) s_segstart[nseg] = Q;
     stage_chunk_rows<T, Q, P, NT>(xr, br, s_e, s_dyt, s_ct);
     __syncthreads();
-    if (c > 0) load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, c - 1, xr, br);
+    if (c > 0) {
+      nxt.load(pb, b, h, c - 1);
+      load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, c - 1, xr, br);
+    }
 
-    const float decay = Elem<T>::exp(s_acs_end);
+    const float decay = Elem<T>::exp(cur.acs_end);
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
       const int tile = w + 4 * k;
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
             if (rank == 0) {
               dhoff = R;
             } else if (pb.dinit) {
-              const int s = clamp_seq(s_seqbase + rank - 1, pb.nseqs);
+              const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int p = pt * 16 + 4 * kg + r;
@@ -256,6 +274,7 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
       }
     }
     __syncthreads();
+    cur = nxt;
   }
 }
 
