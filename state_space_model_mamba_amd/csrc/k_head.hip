@@ -20,12 +20,17 @@
 // The intra-chunk da is formed the "stable" way that the page "Fix Incorrect
 // Gradients and Illegal Memory Access Error in Mamba2" discusses for its
 // ddA_cumsum kernel: straight from V, never as the difference of a row sum
-// and a column sum, so nothing cancels.  With k = 16K + kappa it splits over
-// 16x16 tiles into (full tiles strictly below-left) + (row tile K, rows >= k)
-// + (column tile K, columns < k) + (the diagonal tile); each piece is a sum of
-// per-tile row sums / column sums / totals taken in a fixed order.  Every
-// element of ddt, dx and of the slots is written once, by its owner, at an
-// absolute index.
+// and a column sum, so nothing cancels.  The wave that owns column tile J
+// walks its tiles from the bottom (I = T-1) up to the diagonal and keeps, in
+// an accumulator tile, the column sums of V over the tiles already passed.
+// For row tile K it forms with two fp32 MFMA products (0/1 weights, exact
+// products)
+//   S[kappa][jj] = sum_{ii >= kappa} V_KJ[ii][jj] + sum_{I > K} colsum_IJ[jj]
+// = sum over rows i >= 16K + kappa of V[i][16J + jj]; the row sums of S (over
+// jj, and only jj < kappa on the diagonal tile) are column tile J's share of
+// da at positions 16K + kappa, and da_intra = sum over J <= K of those shares
+// in ascending J.  Every element of ddt, dx and of the slots is written once,
+// by its owner, at an absolute index.
 #include "ssd_problem.h"
 #include "ssd_tiles.h"
 
@@ -34,22 +39,23 @@ namespace ssd {
 template <typename T, int Q, int P>
 struct HeadCfg {
   static constexpr int T16 = Q / 16;
-  static constexpr int W = causal_waves<Q>();
+  static constexpr int W = (Q / 32) < 8 ? (Q / 32) : 8;   // two waves per SIMD at Q = 256
   using Split = CausalSplit<T16, W>;
   static constexpr int NCOL = Split::NCOL;
   static constexpr int NTHR = W * WAVE;
-  static constexpr int NCAUS = T16 * (T16 + 1) / 2;
+  static_assert(NTHR >= Q, "one thread per chunk position");
   static constexpr int PT = P / 16;
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab (divides N)
+  static constexpr int NSL = 4;                         // CB slabs in flight
   static constexpr int LDN = NS + VEC;
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
   static constexpr size_t RA_A = size_t(2) * Q * LDN * sizeof(T);                 // C, B slabs
   static constexpr size_t RA_B = (size_t(2) * Q * LDP + size_t(Q + P) * LDN) * sizeof(T);  // x, dy rows + B, dS slabs
   static constexpr size_t RA = RA_A > RA_B ? RA_A : RA_B;
-  // tile sums: rs, cs [NCAUS*16], tot [NCAUS], vdiag [T16*256], t1 [T16], rs2 [Q], cs3 [Q]
-  static constexpr size_t RS_FLOATS = size_t(NCAUS) * 33 + size_t(T16) * 257 + size_t(2) * Q;
+  // da shares: [column tile J][position]
+  static constexpr size_t RS_FLOATS = size_t(T16) * Q;
   // vectors: acs dt w ee ddacs ddtp sj dd daint (9 Q floats) + seg (Q ints) + red (W + 8)
   static constexpr size_t RV_FLOATS = size_t(10) * Q + W + 8;
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
@@ -57,13 +63,11 @@ struct HeadCfg {
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
 };
 
-__device__ __forceinline__ int causal_index(int I, int J) { return I * (I + 1) / 2 + J; }
-
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
-  constexpr int NS = Cf::NS, LDN = Cf::LDN, LDP = Cf::LDP, NCAUS = Cf::NCAUS;
+  constexpr int NS = Cf::NS, NSL = Cf::NSL, LDN = Cf::LDN, LDP = Cf::LDP;
   constexpr int R = Q / WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // phase A
@@ -74,13 +78,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   T* s_dyk = s_xk + Q * LDP;
   T* s_bz = s_dyk + Q * LDP;
   T* s_dsz = s_bz + Q * LDN;
-  float* s_rs = reinterpret_cast<float*>(smem + Cf::OFF_RS);
-  float* s_cs = s_rs + NCAUS * 16;
-  float* s_tot = s_cs + NCAUS * 16;
-  float* s_vdiag = s_tot + NCAUS;
-  float* s_t1 = s_vdiag + T16 * 256;
-  float* s_rs2 = s_t1 + T16;
-  float* s_cs3 = s_rs2 + Q;
+  float* s_share = reinterpret_cast<float*>(smem + Cf::OFF_RS);
   float* s_acs = reinterpret_cast<float*>(smem + Cf::OFF_RV);
   float* s_dt = s_acs + Q;
   float* s_w = s_dt + Q;
@@ -110,23 +108,18 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const T* Bg = static_cast<const T*>(pb.Bm);
   const T* Cg = static_cast<const T*>(pb.Cm);
 
-  for (int i = tid; i < Q; i += NTHR) {
-    s_acs[i] = pb.acs[bhc * Q + i];
-    s_dt[i] = pb.dtc[bhc * Q + i];
-    s_seg[i] = pb.segpos[bc * Q + i];
-    float o = 0.f;
-    for (int nt = 0; nt < pb.ntg; ++nt) o += pb.offd[(bhc * pb.ntg + nt) * Q + i];
-    s_ddacs[i] = o;
+  // per-position metadata (thread tid owns position tid), loaded first so
+  // that the bulk loads below do not delay it
+  float acs_i = 0.f, dt_i = 0.f, offd_i = 0.f;
+  int seg_i = 0;
+  if (tid < Q) {
+    acs_i = pb.acs[bhc * Q + tid];
+    dt_i = pb.dtc[bhc * Q + tid];
+    seg_i = pb.segpos[bc * Q + tid];
+    for (int nt = 0; nt < pb.ntg; ++nt) offd_i += pb.offd[(bhc * pb.ntg + nt) * Q + tid];
   }
-  __syncthreads();
-  const int lolast = seg_lo(s_seg[Q - 1]);
-  const float acs_end = s_acs[Q - 1];
-  for (int i = tid; i < Q; i += NTHR) {
-    const float e = (i >= lolast) ? Elem<T>::exp(acs_end - s_acs[i]) : 0.f;
-    s_ee[i] = e;
-    s_w[i] = e * s_dt[i];
-  }
-  constexpr int NCOL = Cf::NCOL;
+  const float acs_end = pb.acs[bhc * Q + Q - 1];
+  const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
 
   // Row sources of the global tiles this block stages (nullptr = zero row).
   auto bc_row = [&](const T* base, int n0) {
@@ -145,66 +138,99 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     return [=](int p) -> const float* { return pb.dstate + (bhc * P + p) * pb.N + n0; };
   };
 
-  // ---- phase A: CB over the owned causal tiles, slab by slab over N; the
-  // next slab is loaded into registers while the current one is multiplied
+  // ---- phase A: CB over the owned causal tiles, slab by slab over N.  The
+  // first NSL slabs of C and B and the x, dy rows are all requested up front;
+  // each slab's registers are refilled with the slab NSL further on.
+  RowStage<T, Q, NS, NTHR> st_c[NSL], st_b[NSL];
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    if (sl * NS < pb.N) {
+      st_c[sl].load(bc_row(Cg, sl * NS));
+      st_b[sl].load(bc_row(Bg, sl * NS));
+    }
+  }
+  RowStage<T, Q, P, NTHR> st_x, st_dy;
+  st_x.load(head_row(xg));
+  st_dy.load(head_row(dyg));
+
+  if (tid < Q) {
+    s_acs[tid] = acs_i;
+    s_dt[tid] = dt_i;
+    s_seg[tid] = seg_i;
+    s_ddacs[tid] = offd_i;
+    const float e = (tid >= lolast) ? Elem<T>::exp(acs_end - acs_i) : 0.f;
+    s_ee[tid] = e;
+    s_w[tid] = e * dt_i;
+  }
+
   f32x4_t cb[Cf::NOWN];
 #pragma unroll
   for (int k = 0; k < Cf::NOWN; ++k) cb[k] = zero4();
-  RowStage<T, Q, NS, NTHR> st_c, st_b;
-  RowStage<T, Q, P, NTHR> st_x, st_dy;
-  st_c.load(bc_row(Cg, 0));
-  st_b.load(bc_row(Bg, 0));
-  for (int n0 = 0; n0 < pb.N; n0 += NS) {
-    __syncthreads();
-    st_c.store(s_ck, LDN);
-    st_b.store(s_bk, LDN);
-    __syncthreads();
-    if (n0 + NS < pb.N) {
-      st_c.load(bc_row(Cg, n0 + NS));
-      st_b.load(bc_row(Bg, n0 + NS));
-    } else {
-      st_x.load(head_row(xg));
-      st_dy.load(head_row(dyg));
-    }
-    const int z = opaque_zero();
-    const int wz = w + z;
+  for (int nb = 0; nb < pb.N; nb += NSL * NS) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int n0 = nb + sl * NS;
+      if (n0 < pb.N) {
+        __syncthreads();
+        st_c[sl].store(s_ck, LDN);
+        st_b[sl].store(s_bk, LDN);
+        __syncthreads();
+        if (n0 + NSL * NS < pb.N) {
+          st_c[sl].load(bc_row(Cg, n0 + NSL * NS));
+          st_b[sl].load(bc_row(Bg, n0 + NSL * NS));
+        }
+        const int z = opaque_zero();
+        const int wz = w + z;
 #pragma clang loop unroll(full)
-    for (int k = 0; k < Cf::NOWN; ++k) {
-      int I, J;
-      bool second;
-      Cf::Split::tile(wz, k, I, J, second);
-      cb[k] = tile_mma_kk<T>(cb[k], s_ck + z + 16 * I * LDN, LDN, s_bk + z + 16 * J * LDN, LDN, 0, NS);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < Cf::NOWN; ++k) {
+          int I, J;
+          bool second;
+          Cf::Split::tile(wz, k, I, J, second);
+          cb[k] = tile_mma_kk<T>(cb[k], s_ck + z + 16 * I * LDN, LDN, s_bk + z + 16 * J * LDN, LDN, 0, NS);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- phase B: x, dy rows; decays; M; ddt_intra; V tile sums; dx_intra
+  // ---- phase B: x, dy rows; decays; M; ddt_intra; da shares; dx_intra
   st_x.store(s_xk, LDP);
   st_dy.store(s_dyk, LDP);
   __syncthreads();
   // first slab of phase B2 in flight during phase B
   RowStage<float, P, NS, NTHR> st_ds;
-  st_b.load(bc_row(Bg, 0));
+  st_b[0].load(bc_row(Bg, 0));
   st_ds.load(ds_row(0));
   {
     float dd = 0.f;
-    for (int v = tid; v < Q * P; v += NTHR) {
-      const int i = v / P, p = v % P;
-      dd += Elem<T>::to_f(s_dyk[i * LDP + p]) * Elem<T>::to_f(s_xk[i * LDP + p]);
+    for (int v = tid; v < Q * P / VEC; v += NTHR) {
+      const int i = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+      const uint4 dv = *reinterpret_cast<const uint4*>(s_dyk + i * LDP + p0);
+      const uint4 xv = *reinterpret_cast<const uint4*>(s_xk + i * LDP + p0);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dd += vget<T>(dv, e) * vget<T>(xv, e);
     }
     dd = wave_sum(dd);
     if (l == 0) s_red[w] = dd;
   }
 
-  f32x4_t dxt[NCOL][PT];
+  // 0/1 operands of the share products: U[kappa][ii] = (ii >= kappa), all-ones
+  f32x4_t uincl, ones;
 #pragma unroll
-  for (int a = 0; a < NCOL; ++a)
+  for (int r = 0; r < 4; ++r) {
+    uincl[r] = (4 * kg + r >= r16) ? 1.f : 0.f;
+    ones[r] = 1.f;
+  }
+  f32x4_t dxt[Cf::NCOL][PT];
+#pragma unroll
+  for (int a = 0; a < Cf::NCOL; ++a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) dxt[a][pt] = zero4();
-  float ddti[NCOL];
+  float ddti[Cf::NCOL];   // per-lane partial sums of G o M over a column's tiles
 #pragma unroll
-  for (int a = 0; a < NCOL; ++a) ddti[a] = 0.f;
+  for (int a = 0; a < Cf::NCOL; ++a) ddti[a] = 0.f;
+  f32x4_t below = zero4();   // column sums of V over the tiles below (all rows kappa alike)
 #pragma clang loop unroll(full)
   for (int k = 0; k < Cf::NOWN; ++k) {
     int I, J;
@@ -214,49 +240,50 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     const int j = 16 * J + r16;
     const int loj = seg_lo(s_seg[j]);
     const float aj = s_acs[j], dtj = s_dt[j];
-    float colgm = 0.f, colv = 0.f, vr[4];
+    const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
+    const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+    float gms = 0.f;
+    f32x4_t v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * I + 4 * kg + r;
-      const bool ok = (j <= i) && (seg_lo(s_seg[i]) == loj);
+      const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
+      const bool ok = (j <= i) && (seg_lo(sgi) == loj);
       // exp of a non-positive argument only; masked entries use a zero argument
-      const float e = Elem<T>::exp(ok ? s_acs[i] - aj : 0.f);
+      const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
       const float gv = ok ? cb[k][r] * e : 0.f;
       cb[k][r] = gv;
       const float gm = gv * m[r];
-      colgm += gm;
-      vr[r] = gm * dtj;
-      colv += vr[r];
+      gms += gm;
+      v[r] = gm * dtj;
     }
-    colgm = sum_kgroups(colgm);
-    const int tix = causal_index(I, J);
-    colv = sum_kgroups(colv);
-    if (kg == 0) s_cs[tix * 16 + r16] = colv;
-    const float tot = sum16(colv);
-    if (l == 0) s_tot[tix] = tot;
+    // column tile J's share of da at the rows of tile I
+    if (I == T16 - 1) below = zero4();
+    f32x4_t sh = Mma<float>::mma_rd(uincl, v, below);
+    if (I != J) {
+      below = Mma<float>::mma_rd(ones, v, below);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float rsum = sum16(vr[r]);
-      if (r16 == 0) s_rs[tix * 16 + 4 * kg + r] = rsum;
+      for (int r = 0; r < 4; ++r) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;
     }
-    if (I == J) {
+    f32x4_t rs;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_vdiag[I * 256 + (4 * kg + r) * 16 + r16] = vr[r];
-    }
+    for (int r = 0; r < 4; ++r) rs[r] = sum16(sh[r]);
+    if (r16 == 0) *reinterpret_cast<f32x4_t*>(s_share + J * Q + 16 * I + 4 * kg) = rs;
     // register-direct operands: dy^T values (raw) and the G tile (converted once)
     typename Mma<T>::rfrag av[PT];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load(s_dyk + (16 * I + 4 * kg) * LDP + 16 * pt + r16, LDP);
+    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
     const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
     // dx^T of the tile's column: slot 2q or 2q+1 of its pair (a wave-uniform
     // choice); both slot indices are constants once the loop is unrolled
     const int q = k / (T16 + 1);
     if (!second) {
-      ddti[2 * q] += colgm;
+      ddti[2 * q] += gms;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) dxt[2 * q][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q][pt]);
     } else {
-      ddti[2 * q + 1] += colgm;
+      ddti[2 * q + 1] += gms;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
         dxt[2 * q + 1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q + 1][pt]);
@@ -266,24 +293,24 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 
   // ---- phase B2: Z^T = dS B^T for the owned column tiles, slab by slab over N
   // (x and dy rows stay in LDS; B and dS slabs go to the region behind them)
-  f32x4_t zt[NCOL][PT];
+  f32x4_t zt[Cf::NCOL][PT];
 #pragma unroll
-  for (int a = 0; a < NCOL; ++a)
+  for (int a = 0; a < Cf::NCOL; ++a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) zt[a][pt] = zero4();
   for (int n0 = 0; n0 < pb.N; n0 += NS) {
     __syncthreads();
-    st_b.store(s_bz, LDN);
+    st_b[0].store(s_bz, LDN);
     st_ds.template store_convert<T>(s_dsz, LDN);
     __syncthreads();
     if (n0 + NS < pb.N) {
-      st_b.load(bc_row(Bg, n0 + NS));
+      st_b[0].load(bc_row(Bg, n0 + NS));
       st_ds.load(ds_row(n0 + NS));
     }
     const int z = opaque_zero();
     const int wz = w + z;
 #pragma unroll
-    for (int a = 0; a < NCOL; ++a) {
+    for (int a = 0; a < Cf::NCOL; ++a) {
       const int J = Cf::Split::col(wz, a);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
@@ -294,7 +321,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   // ---- phase C: dx, and per column the ddt parts and s_j
   const float Dh = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
-  for (int a = 0; a < NCOL; ++a) {
+  for (int a = 0; a < Cf::NCOL; ++a) {
     const int J = Cf::Split::col(w, a);
     const int j = 16 * J + r16, t = c * Q + j;
     const float dtj = s_dt[j], wj = s_w[j], eej = s_ee[j];
@@ -317,55 +344,39 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
       }
     }
     xz = sum_kgroups(xz);
+    const float gsum = sum_kgroups(ddti[a]);
     if (kg == 0) {
-      s_ddtp[j] = ddti[a] + eej * xz;
+      s_ddtp[j] = gsum + eej * xz;
       s_sj[j] = wj * xz;
     }
   }
   __syncthreads();
 
   // ---- phase D: da and its consumers
-  if (tid < T16) {
-    const int K = tid;
-    float t1 = 0.f;
-    for (int I = K + 1; I < T16; ++I)
-      for (int J = 0; J < K; ++J) t1 += s_tot[causal_index(I, J)];
-    s_t1[K] = t1;
-  }
   if (tid < Q) {
-    const int i = tid, K = i / 16, ii = i % 16;
-    float rs2 = 0.f;
-    for (int J = 0; J < K; ++J) rs2 += s_rs[causal_index(K, J) * 16 + ii];
-    s_rs2[i] = rs2;
-    float cs3 = 0.f;
-    for (int I = K + 1; I < T16; ++I) cs3 += s_cs[causal_index(I, K) * 16 + ii];
-    s_cs3[i] = cs3;
-    s_dd[i] = s_ddacs[i] - s_sj[i];
+    const int k = tid, K = k / 16;
+    float da = 0.f;
+#pragma unroll
+    for (int J = 0; J < T16; ++J) {
+      const float v = s_share[J * Q + k];
+      da += (J <= K) ? v : 0.f;
+    }
+    s_daint[k] = da;
+    s_dd[k] = s_ddacs[k] - s_sj[k];
   }
-  float sum_s = 0.f;
+  float tail = 0.f;   // chunk-end terms of ddAcs at position Q-1 (wave 0, lane 0)
   if (w == 0) {
     float v = 0.f;
 #pragma unroll
     for (int e = 0; e < R; ++e) v += s_sj[l * R + e];
-    sum_s = wave_sum(v);
+    const float sum_s = wave_sum(v);
+    float endd = 0.f;
+    for (int nt = 0; nt < pb.ntg; ++nt) endd += pb.endd[bhc * pb.ntg + nt];
+    tail = sum_s + Elem<T>::exp(acs_end) * endd;
   }
-  float endd = 0.f;
-  for (int nt = 0; nt < pb.ntg; ++nt) endd += pb.endd[bhc * pb.ntg + nt];
-  __syncthreads();
-  if (tid < Q) {
-    const int k = tid, K = k / 16, kap = k % 16;
-    float t2 = 0.f;
-    for (int ii = 15; ii >= kap; --ii) t2 += s_rs2[16 * K + ii];
-    float t3 = 0.f;
-    for (int jj = 0; jj < kap; ++jj) t3 += s_cs3[16 * K + jj];
-    float t4 = 0.f;
-    for (int ii = kap; ii < 16; ++ii)
-      for (int jj = 0; jj < kap; ++jj) t4 += s_vdiag[K * 256 + ii * 16 + jj];
-    s_daint[k] = ((s_t1[K] + t2) + t3) + t4;
-  }
-  if (tid == 0) s_dd[Q - 1] += sum_s + Elem<T>::exp(acs_end) * endd;
   __syncthreads();
   if (w == 0) {
+    tail = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tail)));
     // reverse in-chunk, in-segment cumulative sum of ddAcs (fixed order)
     float v[R], loc[R];
     int f[R];
@@ -373,6 +384,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     for (int e = 0; e < R; ++e) {
       const int i = l * R + e;
       v[e] = s_dd[i];
+      if (i == Q - 1) v[e] += tail;
       f[e] = (i == Q - 1) || (seg_lo(s_seg[i + 1]) == i + 1);
     }
     float run = 0.f;

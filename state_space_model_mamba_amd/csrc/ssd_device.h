@@ -52,6 +52,18 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ float exp(float x) { return expf(x); }
 };
 
+// gfx950 LDS transpose read (ds_read_b64_tr_b16) of 16-bit elements.  Each
+// lane passes the address of 4 consecutive elements (8-byte aligned); within
+// every group of 16 lanes, lane i of the group receives element i % 4 of the
+// chunks addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12 of its
+// group.  So when lane j of the wave addresses row j / 4, columns
+// 4 (j % 4) .. 4 (j % 4) + 3 of a row-major 16 x 16 block, lane i receives
+// column i % 16 of rows 4 (i / 16) .. 4 (i / 16) + 3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<void*>(p)));
+}
+
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16_t> {
@@ -93,6 +105,12 @@ template <> struct Mma<bf16_t> {
   static __device__ __forceinline__ f32x4_t mma_rd(rfrag a, rfrag x, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, x, c, 0, 0, 0);
   }
+  // rd-fragment of a row-major 16 x 16 block M (LDS, rows = k):
+  // lane gets M[4 * (lane / 16) + r][lane % 16], r = 0..3
+  static __device__ __forceinline__ rfrag rfrag_load_kn(const bf16_t* blk, int ld) {
+    const int l = static_cast<int>(threadIdx.x) & 63;
+    return lds_read_tr16(blk + (l >> 2) * ld + 4 * (l & 3));
+  }
 };
 
 template <> struct Mma<float> {
@@ -109,6 +127,10 @@ template <> struct Mma<float> {
   static __device__ __forceinline__ rfrag rfrag_from_acc(f32x4_t x) { return x; }
   static __device__ __forceinline__ rfrag rfrag_load(const float* p, int stride) {
     return f32x4_t{p[0], p[stride], p[2 * stride], p[3 * stride]};
+  }
+  static __device__ __forceinline__ rfrag rfrag_load_kn(const float* blk, int ld) {
+    const int l = static_cast<int>(threadIdx.x) & 63;
+    return rfrag_load(blk + 4 * (l >> 4) * ld + (l & 15), ld);
   }
   static __device__ __forceinline__ f32x4_t mma_rd(rfrag a, rfrag x, f32x4_t c) {
 #pragma unroll

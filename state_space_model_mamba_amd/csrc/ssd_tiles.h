@@ -140,18 +140,19 @@ struct CausalSplit {
     const int p = w + W * (a >> 1);
     return (a & 1) ? T16 - 1 - p : p;
   }
-  // tile k of wave w: rows I >= J of column J; `second` tells which column of
-  // its pair (slot 2q + second) the tile belongs to (wave-uniform)
+  // tile k of wave w: column J, row tile I, each column walked from the
+  // bottom (I = T-1) up to its diagonal tile (I = J); `second` tells which
+  // column of its pair (slot 2q + second) the tile belongs to (wave-uniform)
   static __device__ __forceinline__ void tile(int w, int k, int& I, int& J, bool& second) {
     const int q = k / (T16 + 1), kk = k % (T16 + 1);
     const int p = w + W * q;
     second = kk >= T16 - p;
     if (!second) {
       J = p;
-      I = p + kk;
+      I = T16 - 1 - kk;
     } else {
       J = T16 - 1 - p;
-      I = J + (kk - (T16 - p));
+      I = T16 - 1 - (kk - (T16 - p));
     }
   }
 };
