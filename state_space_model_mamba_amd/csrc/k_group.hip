@@ -6,6 +6,7 @@
 // slots and no atomics.
 //
 // k_dcb, per (batch, group, chunk):
+//   CB  = C B^T over the causal tiles (head independent; fp32, for the head kernel)
 //   dCB = sum_h W_h o (dy_h x_h^T),  W_h[i,j] = exp(Acs_i - Acs_j) dt_j  (j <= i, same segment)
 //   written as a Q x Q tile and as its transpose (zeros above the diagonal).
 // k_dbdc, per (batch, group, chunk, dstate tile):
@@ -28,12 +29,16 @@ namespace ssd {
 template <typename T, int Q, int P>
 struct DcbCfg {
   static constexpr int T16 = Q / 16;
-  static constexpr int W = T16 / 2;   // 8 waves at Q = 256 (VALU-updated accumulators stay in VGPRs)
+  static constexpr int W = causal_waves<Q>();   // the head kernel's split (8 waves at Q = 256)
   using Split = CausalSplit<T16, W>;
   static constexpr int NTHR = W * WAVE;
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
+  static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab of the CB product
+  static constexpr int NSL = 4;                         // slabs in flight
+  static constexpr int LDN = NS + VEC;
+  static_assert(LDN <= LDP, "C/B slabs reuse the x/dy rows' LDS");
   static constexpr int NV = Q * P / VEC;                 // vectors of x (or dy) per head
   static constexpr int NVT = (NV + NTHR - 1) / NTHR;     // per thread
   static constexpr size_t LDS = size_t(2) * Q * LDP * sizeof(T) + size_t(3) * Q * 4;
@@ -60,7 +65,65 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   const T* xg = static_cast<const T*>(pb.x);
   const T* dyg = static_cast<const T*>(pb.dy);
 
+  const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
   for (int i = tid; i < Q; i += NTHR) s_lo[i] = seg_lo(pb.segpos[bc * Q + i]);
+
+  // ---- CB = C B^T over the owned causal tiles.  It is the same for every
+  // head of the group, so it is formed once here and stored for the head
+  // kernel in fp32, in that kernel's (wave, tile) order and lane layout.
+  {
+    constexpr int NS = Cf::NS, NSL = Cf::NSL, LDN = Cf::LDN;
+    T* s_ck = s_xk;   // the x / dy rows are not staged yet
+    T* s_bk = s_ck + Q * LDN;
+    const T* Bg = static_cast<const T*>(pb.Bm);
+    const T* Cg = static_cast<const T*>(pb.Cm);
+    auto bc_row = [&](const T* base, int n0) {
+      return [=](int i) -> const T* {
+        const int t = c * Q + i;
+        return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 : nullptr;
+      };
+    };
+    RowStage<T, Q, NS, NTHR> st_c[NSL], st_b[NSL];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl * NS < pb.N) {
+        st_c[sl].load(bc_row(Cg, sl * NS));
+        st_b[sl].load(bc_row(Bg, sl * NS));
+      }
+    }
+    f32x4_t cbt[Cf::NOWN];
+#pragma unroll
+    for (int k = 0; k < Cf::NOWN; ++k) cbt[k] = zero4();
+    for (int nb = 0; nb < pb.N; nb += NSL * NS) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const int n0 = nb + sl * NS;
+        if (n0 < pb.N) {
+          __syncthreads();
+          st_c[sl].store(s_ck, LDN);
+          st_b[sl].store(s_bk, LDN);
+          __syncthreads();
+          if (n0 + NSL * NS < pb.N) {
+            st_c[sl].load(bc_row(Cg, n0 + NSL * NS));
+            st_b[sl].load(bc_row(Bg, n0 + NSL * NS));
+          }
+          const int z = opaque_zero();
+          const int wz = w + z;
+#pragma clang loop unroll(full)
+          for (int k = 0; k < Cf::NOWN; ++k) {
+            int I, J;
+            bool second;
+            Cf::Split::tile(wz, k, I, J, second);
+            cbt[k] = tile_mma_kk<T>(cbt[k], s_ck + z + 16 * I * LDN, LDN, s_bk + z + 16 * J * LDN, LDN, 0, NS);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+    float* dst = pb.cbt + (bgc * Cf::W + w) * Cf::NOWN * 256 + l * 4;
+#pragma unroll
+    for (int k = 0; k < Cf::NOWN; ++k) *reinterpret_cast<f32x4_t*>(dst + k * 256) = cbt[k];
+  }
 
   f32x4_t dcb[Cf::NOWN];
 #pragma unroll
@@ -118,7 +181,6 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   }
 
   // write dCB (row-major) and dCB^T, the owned columns in full (zeros above the diagonal)
-  const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
   T* dcb_out = static_cast<T*>(pb.dcb) + bgc * Q * Q;
   T* dcbt_out = static_cast<T*>(pb.dcbt) + bgc * Q * Q;
 #pragma clang loop unroll(full)

@@ -3,7 +3,7 @@
 // (ddA_cumsum) and chunk_cumsum_bwd (ddt and the dA partial) in the kernel
 // list of the page "Deterministic bwd kernel for mamba2".
 //
-//   CB        = C B^T                         (Q x Q causal, MFMA over N)
+//   CB        = C B^T                         (Q x Q causal, from the dCB kernel)
 //   G[i,j]    = CB[i,j] exp(Acs_i - Acs_j)    (j <= i, same segment; else 0)
 //   M         = dy x^T                        (MFMA over P)
 //   Z^T       = dS B^T                        (P x Q, MFMA over N)
@@ -21,16 +21,17 @@
 // Gradients and Illegal Memory Access Error in Mamba2" discusses for its
 // ddA_cumsum kernel: straight from V, never as the difference of a row sum
 // and a column sum, so nothing cancels.  The wave that owns column tile J
-// walks its tiles from the bottom (I = T-1) up to the diagonal and keeps, in
-// an accumulator tile, the column sums of V over the tiles already passed.
-// For row tile K it forms with two fp32 MFMA products (0/1 weights, exact
-// products)
-//   S[kappa][jj] = sum_{ii >= kappa} V_KJ[ii][jj] + sum_{I > K} colsum_IJ[jj]
-// = sum over rows i >= 16K + kappa of V[i][16J + jj]; the row sums of S (over
-// jj, and only jj < kappa on the diagonal tile) are column tile J's share of
-// da at positions 16K + kappa, and da_intra = sum over J <= K of those shares
-// in ascending J.  Every element of ddt, dx and of the slots is written once,
-// by its owner, at an absolute index.
+// walks its tiles from the bottom (I = T-1) up to the diagonal, carrying each
+// lane's column sum of V over the tiles already passed.  For row tile K and
+// kappa in [0, 16) it forms, per column j of the tile,
+//   S[kappa][j] = sum over rows i >= 16K + kappa of V[i][j]
+// (in-lane suffix sums, the other row groups' sums gathered with the row
+// swaps, plus the carried column sum), and the row sum of S over j (only
+// j < 16K + kappa on the diagonal tile) is column tile J's share of da at
+// position 16K + kappa.  da_intra is the sum of the shares over J <= K in
+// ascending J.  CB itself comes from the dCB kernel (same causal split).
+// Every element of ddt, dx and of the slots is written once, by its owner, at
+// an absolute index.
 #include "ssd_problem.h"
 #include "ssd_tiles.h"
 
@@ -39,7 +40,7 @@ namespace ssd {
 template <typename T, int Q, int P>
 struct HeadCfg {
   static constexpr int T16 = Q / 16;
-  static constexpr int W = (Q / 32) < 8 ? (Q / 32) : 8;   // two waves per SIMD at Q = 256
+  static constexpr int W = causal_waves<Q>();   // the dCB kernel's split (8 waves at Q = 256)
   using Split = CausalSplit<T16, W>;
   static constexpr int NCOL = Split::NCOL;
   static constexpr int NTHR = W * WAVE;
@@ -47,17 +48,15 @@ struct HeadCfg {
   static constexpr int PT = P / 16;
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab (divides N)
-  static constexpr int NSL = 4;                         // CB slabs in flight
   static constexpr int LDN = NS + VEC;
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
-  static constexpr size_t RA_A = size_t(2) * Q * LDN * sizeof(T);                 // C, B slabs
-  static constexpr size_t RA_B = (size_t(2) * Q * LDP + size_t(Q + P) * LDN) * sizeof(T);  // x, dy rows + B, dS slabs
-  static constexpr size_t RA = RA_A > RA_B ? RA_A : RA_B;
+  static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(Q + P) * LDN) * sizeof(T);  // x, dy rows + B, dS slabs
   // da shares: [column tile J][position]
   static constexpr size_t RS_FLOATS = size_t(T16) * Q;
-  // vectors: acs dt w ee ddacs ddtp sj dd daint (9 Q floats) + seg (Q ints) + red (W + 8)
-  static constexpr size_t RV_FLOATS = size_t(10) * Q + W + 8;
+  // vectors: acs dt w ee ddacs ddtp sj dd daint er (10 Q floats) + seg (Q ints) + red (W + 8)
+  static constexpr size_t RV_FLOATS = size_t(11) * Q + W + 8;
+  static constexpr int NSB = 4;   // B / dS slabs of phase B2 in flight
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
@@ -67,13 +66,9 @@ template <typename T, int Q, int P>
 __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
-  constexpr int NS = Cf::NS, NSL = Cf::NSL, LDN = Cf::LDN, LDP = Cf::LDP;
+  constexpr int NS = Cf::NS, LDN = Cf::LDN, LDP = Cf::LDP;
   constexpr int R = Q / WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // phase A
-  T* s_ck = reinterpret_cast<T*>(smem);
-  T* s_bk = s_ck + Q * LDN;
-  // phase B (aliases phase A)
   T* s_xk = reinterpret_cast<T*>(smem);
   T* s_dyk = s_xk + Q * LDP;
   T* s_bz = s_dyk + Q * LDP;
@@ -88,7 +83,8 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   float* s_sj = s_ddtp + Q;
   float* s_dd = s_sj + Q;
   float* s_daint = s_dd + Q;
-  int* s_seg = reinterpret_cast<int*>(s_daint + Q);
+  float* s_er = s_daint + Q;
+  int* s_seg = reinterpret_cast<int*>(s_er + Q);
   float* s_red = reinterpret_cast<float*>(s_seg + Q);
 
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
@@ -106,7 +102,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const T* xg = static_cast<const T*>(pb.x);
   const T* dyg = static_cast<const T*>(pb.dy);
   const T* Bg = static_cast<const T*>(pb.Bm);
-  const T* Cg = static_cast<const T*>(pb.Cm);
+  const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
 
   // per-position metadata (thread tid owns position tid), loaded first so
   // that the bulk loads below do not delay it
@@ -138,21 +134,24 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     return [=](int p) -> const float* { return pb.dstate + (bhc * P + p) * pb.N + n0; };
   };
 
-  // ---- phase A: CB over the owned causal tiles, slab by slab over N.  The
-  // first NSL slabs of C and B and the x, dy rows are all requested up front;
-  // each slab's registers are refilled with the slab NSL further on.
-  RowStage<T, Q, NS, NTHR> st_c[NSL], st_b[NSL];
+  // ---- phase A: the CB tiles of this wave (formed once per group by the
+  // dCB kernel, same split) and the x, dy rows, all requested up front
+  f32x4_t cb[Cf::NOWN];
+  {
+    const float* src = pb.cbt + (bgc * W + w) * Cf::NOWN * 256 + l * 4;
 #pragma unroll
-  for (int sl = 0; sl < NSL; ++sl) {
-    if (sl * NS < pb.N) {
-      st_c[sl].load(bc_row(Cg, sl * NS));
-      st_b[sl].load(bc_row(Bg, sl * NS));
-    }
+    for (int k = 0; k < Cf::NOWN; ++k) cb[k] = *reinterpret_cast<const f32x4_t*>(src + k * 256);
   }
   RowStage<T, Q, P, NTHR> st_x, st_dy;
   st_x.load(head_row(xg));
   st_dy.load(head_row(dyg));
 
+  // A chunk without sequence starts after position 0 has one segment, and its
+  // Acs never increases; there exp(Acs_i - Acs_j) of an off-diagonal tile is
+  // formed as er_i * exp(Acs_{16I} - Acs_j), both factors <= 1, with
+  // er_i = exp(Acs_i - Acs_{16I}) tabled once per block.
+  const bool uniform = __builtin_amdgcn_readfirstlane(lolast) == 0;
+  const float acs_tile0 = __shfl(acs_i, l & ~15, WAVE);
   if (tid < Q) {
     s_acs[tid] = acs_i;
     s_dt[tid] = dt_i;
@@ -161,47 +160,24 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     const float e = (tid >= lolast) ? Elem<T>::exp(acs_end - acs_i) : 0.f;
     s_ee[tid] = e;
     s_w[tid] = e * dt_i;
+    s_er[tid] = uniform ? Elem<T>::exp(acs_i - acs_tile0) : 0.f;
   }
-
-  f32x4_t cb[Cf::NOWN];
-#pragma unroll
-  for (int k = 0; k < Cf::NOWN; ++k) cb[k] = zero4();
-  for (int nb = 0; nb < pb.N; nb += NSL * NS) {
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      const int n0 = nb + sl * NS;
-      if (n0 < pb.N) {
-        __syncthreads();
-        st_c[sl].store(s_ck, LDN);
-        st_b[sl].store(s_bk, LDN);
-        __syncthreads();
-        if (n0 + NSL * NS < pb.N) {
-          st_c[sl].load(bc_row(Cg, n0 + NSL * NS));
-          st_b[sl].load(bc_row(Bg, n0 + NSL * NS));
-        }
-        const int z = opaque_zero();
-        const int wz = w + z;
-#pragma clang loop unroll(full)
-        for (int k = 0; k < Cf::NOWN; ++k) {
-          int I, J;
-          bool second;
-          Cf::Split::tile(wz, k, I, J, second);
-          cb[k] = tile_mma_kk<T>(cb[k], s_ck + z + 16 * I * LDN, LDN, s_bk + z + 16 * J * LDN, LDN, 0, NS);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  }
-  __syncthreads();
 
   // ---- phase B: x, dy rows; decays; M; ddt_intra; da shares; dx_intra
   st_x.store(s_xk, LDP);
   st_dy.store(s_dyk, LDP);
   __syncthreads();
-  // first slab of phase B2 in flight during phase B
-  RowStage<float, P, NS, NTHR> st_ds;
-  st_b[0].load(bc_row(Bg, 0));
-  st_ds.load(ds_row(0));
+  // the first NSB slabs of phase B2 in flight during phase B
+  constexpr int NSB = Cf::NSB;
+  RowStage<T, Q, NS, NTHR> st_bz[NSB];
+  RowStage<float, P, NS, NTHR> st_ds[NSB];
+#pragma unroll
+  for (int sl = 0; sl < NSB; ++sl) {
+    if (sl * NS < pb.N) {
+      st_bz[sl].load(bc_row(Bg, sl * NS));
+      st_ds[sl].load(ds_row(sl * NS));
+    }
+  }
   {
     float dd = 0.f;
     for (int v = tid; v < Q * P / VEC; v += NTHR) {
@@ -215,13 +191,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     if (l == 0) s_red[w] = dd;
   }
 
-  // 0/1 operands of the share products: U[kappa][ii] = (ii >= kappa), all-ones
-  f32x4_t uincl, ones;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    uincl[r] = (4 * kg + r >= r16) ? 1.f : 0.f;
-    ones[r] = 1.f;
-  }
   f32x4_t dxt[Cf::NCOL][PT];
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a)
@@ -230,7 +199,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   float ddti[Cf::NCOL];   // per-lane partial sums of G o M over a column's tiles
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a) ddti[a] = 0.f;
-  f32x4_t below = zero4();   // column sums of V over the tiles below (all rows kappa alike)
+  float below = 0.f;   // this lane's column sum of V over the column's tiles already passed
 #pragma clang loop unroll(full)
   for (int k = 0; k < Cf::NOWN; ++k) {
     int I, J;
@@ -238,38 +207,71 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     Cf::Split::tile(w, k, I, J, second);
     const f32x4_t m = tile_mma_kk<T>(zero4(), s_dyk + 16 * I * LDP, LDP, s_xk + 16 * J * LDP, LDP, 0, P);
     const int j = 16 * J + r16;
-    const int loj = seg_lo(s_seg[j]);
     const float aj = s_acs[j], dtj = s_dt[j];
-    const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
-    const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+    if (uniform && I != J) {
+      const float ec = Elem<T>::exp(s_acs[16 * I] - aj);
+      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
+    } else {
+      const int loj = seg_lo(s_seg[j]);
+      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
+      const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * kg + r;
+        const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
+        const bool ok = (j <= i) && (seg_lo(sgi) == loj);
+        // exp of a non-positive argument only; masked entries use a zero argument
+        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
+        e4[r] = ok ? e : 0.f;
+      }
+    }
     float gms = 0.f;
     f32x4_t v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * kg + r;
-      const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
-      const bool ok = (j <= i) && (seg_lo(sgi) == loj);
-      // exp of a non-positive argument only; masked entries use a zero argument
-      const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
-      const float gv = ok ? cb[k][r] * e : 0.f;
+      const float gv = cb[k][r] * e4[r];
       cb[k][r] = gv;
       const float gm = gv * m[r];
       gms += gm;
       v[r] = gm * dtj;
     }
-    // column tile J's share of da at the rows of tile I
-    if (I == T16 - 1) below = zero4();
-    f32x4_t sh = Mma<float>::mma_rd(uincl, v, below);
-    if (I != J) {
-      below = Mma<float>::mma_rd(ones, v, below);
-    } else {
+    // column tile J's share of da at the rows of tile I (see the top of the file):
+    // sh[r] = sum over rows i >= 16I + 4kg + r of V[i][j], then summed over j
+    if (I == T16 - 1) below = 0.f;
+    float sfx[4];
+    sfx[3] = v[3];
+    sfx[2] = v[2] + sfx[3];
+    sfx[1] = v[1] + sfx[2];
+    sfx[0] = v[0] + sfx[1];
+    float grp[4];
+    gather_kgroups(sfx[0], grp);   // the 4 row groups' sums of column j
+    const float s2 = grp[3], s1 = s2 + grp[2], s0 = s1 + grp[1];
+    const float lower = kg == 0 ? s0 : (kg == 1 ? s1 : (kg == 2 ? s2 : 0.f));
+    const float base = below + lower;
+    float sh[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      sh[r] = base + sfx[r];
+      if (I == J) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;   // diagonal tile: columns j < k only
     }
-    f32x4_t rs;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rs[r] = sum16(sh[r]);
-    if (r16 == 0) *reinterpret_cast<f32x4_t*>(s_share + J * Q + 16 * I + 4 * kg) = rs;
+    below += s0 + grp[0];
+    // row sums over the 16 lanes (columns): a butterfly that halves the values
+    // per lane at each step; lane r16 < 4 ends with row 2 (r16 & 1) + (r16 >> 1)
+    {
+      const bool odd = (r16 & 1) != 0, hi = (r16 & 2) != 0;
+      const float k0 = odd ? sh[2] : sh[0], k1 = odd ? sh[3] : sh[1];
+      const float t0 = odd ? sh[0] : sh[2], t1 = odd ? sh[1] : sh[3];
+      const float a0 = k0 + dpp_move<0xB1>(t0);   // quad_perm [1,0,3,2]
+      const float a1 = k1 + dpp_move<0xB1>(t1);
+      const float kk = hi ? a1 : a0, tt = hi ? a0 : a1;
+      float rsum = kk + dpp_move<0x4E>(tt);      // quad_perm [2,3,0,1]
+      rsum += dpp_move<0x124>(rsum);             // row_ror:4
+      rsum += dpp_move<0x128>(rsum);             // row_ror:8
+      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum;
+    }
     // register-direct operands: dy^T values (raw) and the G tile (converted once)
     typename Mma<T>::rfrag av[PT];
 #pragma unroll
@@ -298,23 +300,29 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   for (int a = 0; a < Cf::NCOL; ++a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) zt[a][pt] = zero4();
-  for (int n0 = 0; n0 < pb.N; n0 += NS) {
-    __syncthreads();
-    st_b[0].store(s_bz, LDN);
-    st_ds.template store_convert<T>(s_dsz, LDN);
-    __syncthreads();
-    if (n0 + NS < pb.N) {
-      st_b[0].load(bc_row(Bg, n0 + NS));
-      st_ds.load(ds_row(n0 + NS));
-    }
-    const int z = opaque_zero();
-    const int wz = w + z;
+  for (int nb = 0; nb < pb.N; nb += NSB * NS) {
 #pragma unroll
-    for (int a = 0; a < Cf::NCOL; ++a) {
-      const int J = Cf::Split::col(wz, a);
+    for (int sl = 0; sl < NSB; ++sl) {
+      const int n0 = nb + sl * NS;
+      if (n0 < pb.N) {
+        __syncthreads();
+        st_bz[sl].store(s_bz, LDN);
+        st_ds[sl].template store_convert<T>(s_dsz, LDN);
+        __syncthreads();
+        if (n0 + NSB * NS < pb.N) {
+          st_bz[sl].load(bc_row(Bg, n0 + NSB * NS));
+          st_ds[sl].load(ds_row(n0 + NSB * NS));
+        }
+        const int z = opaque_zero();
+        const int wz = w + z;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-        zt[a][pt] = tile_mma_kk<T>(zt[a][pt], s_dsz + z + 16 * pt * LDN, LDN, s_bz + z + 16 * J * LDN, LDN, 0, NS);
+        for (int a = 0; a < Cf::NCOL; ++a) {
+          const int J = Cf::Split::col(wz, a);
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt)
+            zt[a][pt] = tile_mma_kk<T>(zt[a][pt], s_dsz + z + 16 * pt * LDN, LDN, s_bz + z + 16 * J * LDN, LDN, 0, NS);
+        }
+      }
     }
   }
 
@@ -328,20 +336,17 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     float xz = 0.f;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-      T outv[4];
+      const f32x4_t dyv = load4f<T>(s_dyk + j * LDP + 16 * pt + 4 * kg);
+      const f32x4_t xv = load4f<T>(s_xk + j * LDP + 16 * pt + 4 * kg);
+      f32x4_t outv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = 16 * pt + 4 * kg + r;
-        const float dyv = Elem<T>::to_f(s_dyk[j * LDP + p]);
-        const float xv = Elem<T>::to_f(s_xk[j * LDP + p]);
-        outv[r] = Elem<T>::from_f(dtj * dxt[a][pt][r] + wj * zt[a][pt][r] + Dh * dyv);
-        xz += xv * zt[a][pt][r];
+        outv[r] = dtj * dxt[a][pt][r] + wj * zt[a][pt][r] + Dh * dyv[r];
+        xz += xv[r] * zt[a][pt][r];
       }
-      if (t < pb.L) {
-        T* dst = static_cast<T*>(pb.dx) + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + 16 * pt + 4 * kg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[r] = outv[r];
-      }
+      if (t < pb.L)
+        store4f<T>(static_cast<T*>(pb.dx) + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + 16 * pt + 4 * kg,
+                   outv);
     }
     xz = sum_kgroups(xz);
     const float gsum = sum_kgroups(ddti[a]);

@@ -26,7 +26,8 @@ namespace ssd {
 template <typename T, int Q, int P, int NT>
 struct StateCfg {
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int LDQ = Q + VEC;          // K-major rows of length Q (+16 B pad)
+  static constexpr int LDX = kn_pitch<T>(P);   // x / dy chunk rows [j][p]
+  static constexpr int LDB = kn_pitch<T>(NT);  // B / C tile rows [j][n]
   static constexpr int XV = Q * P / VEC;       // 16-byte vectors of one x/dy chunk
   static constexpr int NXV = (XV + 255) / 256;
   static constexpr int BV = Q * NT / VEC;      // vectors of one B/C chunk tile
@@ -90,32 +91,34 @@ struct ChunkMeta {
   }
 };
 
-// x (or dy) chunk -> LDS, transposed to [p][j] and scaled by s_scale[j];
-// B (or C) tile -> LDS transposed to [n][j].
+// x (or dy) chunk rows -> LDS [j][p], each row scaled by s_scale[j]; B (or C)
+// tile rows -> LDS [j][n] as they are.  16-byte stores only; the MFMA reads
+// them with LDS transpose reads.
 template <typename T, int Q, int P, int NT>
 __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q, P, NT>::NXV],
                                                  const uint4 (&br)[StateCfg<T, Q, P, NT>::NBV],
-                                                 const float* s_scale, T* s_xt, T* s_bt) {
+                                                 const float* s_scale, T* s_x, T* s_b) {
   using Cf = StateCfg<T, Q, P, NT>;
+  constexpr int VEC = Cf::VEC;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < Cf::NXV; ++k) {
     const int v = tid + 256 * k;
     if (v < Cf::XV) {
-      const int j = v / (P / Cf::VEC), pv = v % (P / Cf::VEC);
+      const int j = v / (P / VEC), pv = v % (P / VEC);
       const float sc = s_scale[j];
+      T o[VEC];
 #pragma unroll
-      for (int e = 0; e < Cf::VEC; ++e)
-        s_xt[(pv * Cf::VEC + e) * Cf::LDQ + j] = Elem<T>::from_f(vget<T>(xr[k], e) * sc);
+      for (int e = 0; e < VEC; ++e) o[e] = Elem<T>::from_f(vget<T>(xr[k], e) * sc);
+      *reinterpret_cast<uint4*>(s_x + j * Cf::LDX + pv * VEC) = *reinterpret_cast<const uint4*>(o);
     }
   }
 #pragma unroll
   for (int k = 0; k < Cf::NBV; ++k) {
     const int v = tid + 256 * k;
     if (v < Cf::BV) {
-      const int j = v / (NT / Cf::VEC), nv = v % (NT / Cf::VEC);
-#pragma unroll
-      for (int e = 0; e < Cf::VEC; ++e) s_bt[(nv * Cf::VEC + e) * Cf::LDQ + j] = vraw<T>(br[k], e);
+      const int j = v / (NT / VEC), nv = v % (NT / VEC);
+      *reinterpret_cast<uint4*>(s_b + j * Cf::LDB + nv * VEC) = br[k];
     }
   }
 }
@@ -123,8 +126,8 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_xt[P * Cf::LDQ];
-  __shared__ __attribute__((aligned(16))) T s_bt[NT * Cf::LDQ];
+  __shared__ __attribute__((aligned(16))) T s_xt[Q * Cf::LDX];
+  __shared__ __attribute__((aligned(16))) T s_bt[Q * Cf::LDB];
   __shared__ float s_w[Q];
 
   const int ntiles = pb.N / NT;
@@ -166,8 +169,7 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
       const int tile = w + 4 * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
-        const f32x4_t S = tile_mma_kk<T>(zero4(), s_xt + pt * 16 * Cf::LDQ, Cf::LDQ,
-                                         s_bt + nt * 16 * Cf::LDQ, Cf::LDQ, kb, Q);
+        const f32x4_t S = tile_mma_kn<T>(zero4(), s_xt + pt * 16, Cf::LDX, s_bt + nt * 16, Cf::LDB, kb, Q);
         const int n = n0 + nt * 16 + r16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -191,8 +193,8 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_dyt[P * Cf::LDQ];
-  __shared__ __attribute__((aligned(16))) T s_ct[NT * Cf::LDQ];
+  __shared__ __attribute__((aligned(16))) T s_dyt[Q * Cf::LDX];
+  __shared__ __attribute__((aligned(16))) T s_ct[Q * Cf::LDB];
   __shared__ float s_e[Q];
   __shared__ int s_seg[Q];
   __shared__ int s_segstart[Q + 1];
@@ -241,20 +243,20 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const int n = n0 + nt * 16 + r16;
-        const T* ab = s_dyt + pt * 16 * Cf::LDQ;
-        const T* bb = s_ct + nt * 16 * Cf::LDQ;
+        const T* ab = s_dyt + pt * 16;
+        const T* bb = s_ct + nt * 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           pb.dstate[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = dout[k][r];
         if (nstart == 0) {
-          const f32x4_t R = tile_mma_kk<T>(zero4(), ab, Cf::LDQ, bb, Cf::LDQ, 0, Q);
+          const f32x4_t R = tile_mma_kn<T>(zero4(), ab, Cf::LDX, bb, Cf::LDB, 0, Q);
 #pragma unroll
           for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + decay * dout[k][r];
         } else {
           f32x4_t dhoff = zero4();
           for (int m = 0; m < nseg; ++m) {
             const int lo = s_segstart[m], hi = s_segstart[m + 1];
-            const f32x4_t R = tile_mma_kk_range<T>(zero4(), ab, Cf::LDQ, bb, Cf::LDQ, lo, hi);
+            const f32x4_t R = tile_mma_kn_range<T>(zero4(), ab, Cf::LDX, bb, Cf::LDB, lo, hi);
             const int rank = seg_rank(s_seg[lo]);
             if (rank == 0) {
               dhoff = R;

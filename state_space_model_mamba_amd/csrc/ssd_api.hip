@@ -12,7 +12,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, offd, endd, slot_dA, slot_dD, total;
+  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, total;
   int nc, ntg;
 };
 
@@ -62,6 +62,7 @@ Layout make_layout(const ssd_shape* s) {
   const size_t es = is_bf16(s) ? 2 : 4;
   L.dcb = take(B * s->ngroups * nc * Q * Q * es);
   L.dcbt = take(B * s->ngroups * nc * Q * Q * es);
+  L.cbt = take(B * s->ngroups * nc * (Q * (Q + 16) / 2) * 4);
   L.offd = take(B * H * nc * ntg * Q * 4);
   L.endd = take(B * H * nc * ntg * 4);
   L.slot_dA = take(B * nc * H * 4);
@@ -167,6 +168,7 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
   pb.dstate = reinterpret_cast<float*>(ws + L.dstate);
   pb.dcb = ws + L.dcb;
   pb.dcbt = ws + L.dcbt;
+  pb.cbt = reinterpret_cast<float*>(ws + L.cbt);
   pb.offd = reinterpret_cast<float*>(ws + L.offd);
   pb.endd = reinterpret_cast<float*>(ws + L.endd);
   pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);

@@ -212,6 +212,20 @@ __device__ __forceinline__ float sum_kgroups(float v) {
   return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
 }
 
+// The values of the 4 lanes that share lane % 16 (one per row, row = lane /
+// 16), gathered into each of those lanes: out[q] = v of row q.
+__device__ __forceinline__ void gather_kgroups(float v, float (&out)[4]) {
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  permlane16_swap(a, b);   // a = (r0, r0, r2, r2), b = (r1, r1, r3, r3)
+  unsigned a0 = a, a2 = a, b1 = b, b3 = b;
+  permlane32_swap(a0, a2);  // a0 = r0, a2 = r2 in every row
+  permlane32_swap(b1, b3);  // b1 = r1, b3 = r3 in every row
+  out[0] = __builtin_bit_cast(float, a0);
+  out[1] = __builtin_bit_cast(float, b1);
+  out[2] = __builtin_bit_cast(float, a2);
+  out[3] = __builtin_bit_cast(float, b3);
+}
+
 // Sum over the whole wave; lane 0's result is the one to use.
 __device__ __forceinline__ float wave_sum(float v) { return sum_kgroups(sum16(v)); }
 

@@ -51,6 +51,8 @@ struct Problem {
   float* dstate;     // (B, H, nc, P, N)
   void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB
   void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose
+  float* cbt;        // (B, G, nc, Q(Q+16)/512 tiles, 256): C B^T causal tiles, fp32, in the
+                     // causal split's (wave, tile) order and accumulator lane layout
   float* offd;       // (B, H, nc, ntg, Q)
   float* endd;       // (B, H, nc, ntg)
   float* slot_dA;    // (B, nc, H)

@@ -92,6 +92,90 @@ struct RowStage {
   }
 };
 
+// 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as floats,
+// and the reverse with round-to-nearest-even
+template <typename T> __device__ __forceinline__ f32x4_t load4f(const T* p);
+template <> __device__ __forceinline__ f32x4_t load4f<bf16_t>(const bf16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+template <> __device__ __forceinline__ f32x4_t load4f<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <typename T> __device__ __forceinline__ void store4f(T* p, f32x4_t v);
+template <> __device__ __forceinline__ void store4f<bf16_t>(bf16_t* p, f32x4_t v) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4_t));
+}
+template <> __device__ __forceinline__ void store4f<float>(float* p, f32x4_t v) {
+  *reinterpret_cast<f32x4_t*>(p) = v;
+}
+
+// MFMA fragments of an operand stored with k as the row index ("kn" layout:
+// X[k][m], m contiguous; X points at column m0), k in [k0, k0 + KSTEP):
+//   bf16: lane (kg, r16) gets X[k0 + 8 kg + e][r16], e = 0..7, with two LDS
+//         transpose reads (lane j of each 16-lane group addresses row
+//         k0 + 8 kg + j / 4 (+ 4), columns 4 (j % 4) .. + 3)
+//   fp32: lane (kg, r16) gets X[k0 + kg][r16]
+// ld must keep rows 8-byte aligned (a multiple of 4 elements).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_kn(const T* X, int ld, int k0);
+template <>
+__device__ __forceinline__ Mma<bf16_t>::frag load_kn<bf16_t>(const bf16_t* X, int ld, int k0) {
+  const int l = lane_id();
+  const bf16_t* p = X + (k0 + 8 * (l >> 4) + ((l & 15) >> 2)) * ld + 4 * (l & 3);
+  const s16x4_t lo = lds_read_tr16(p);
+  const s16x4_t hi = lds_read_tr16(p + 4 * ld);
+  return __builtin_bit_cast(Mma<bf16_t>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <>
+__device__ __forceinline__ float load_kn<float>(const float* X, int ld, int k0) {
+  const int l = lane_id();
+  return X[(k0 + (l >> 4)) * ld + (l & 15)];
+}
+
+// 16x16 tile product with both operands in the kn layout:
+//   acc[m][n] += sum_k A[k][m] B[k][n],  k in [k_begin, k_end) (multiples of KSTEP)
+template <typename T>
+__device__ __forceinline__ f32x4_t tile_mma_kn(f32x4_t acc, const T* a, int lda, const T* b, int ldb,
+                                               int k_begin, int k_end) {
+  for (int k = k_begin; k < k_end; k += Mma<T>::KSTEP)
+    acc = Mma<T>::mma(load_kn<T>(a, lda, k), load_kn<T>(b, ldb, k), acc);
+  return acc;
+}
+
+// Like tile_mma_kn, but only k in [lo, hi) contributes (A elements outside
+// read as zero).
+template <typename T>
+__device__ __forceinline__ f32x4_t tile_mma_kn_range(f32x4_t acc, const T* a, int lda, const T* b, int ldb,
+                                                     int lo, int hi) {
+  constexpr int KS = Mma<T>::KSTEP, KW = Mma<T>::KW;
+  const int kg = lane_id() >> 4;
+  for (int k = (lo / KS) * KS; k < hi; k += KS) {
+    typename Mma<T>::frag fa = load_kn<T>(a, lda, k);
+    if constexpr (KW == 1) {
+      if (k + kg < lo || k + kg >= hi) fa = 0.f;
+    } else {
+      u16x8_t v = __builtin_bit_cast(u16x8_t, fa);
+#pragma unroll
+      for (int e = 0; e < KW; ++e)
+        if (k + KW * kg + e < lo || k + KW * kg + e >= hi) v[e] = 0;
+      fa = __builtin_bit_cast(typename Mma<T>::frag, v);
+    }
+    acc = Mma<T>::mma(fa, load_kn<T>(b, ldb, k), acc);
+  }
+  return acc;
+}
+
+// Row pitch (elements) of a row-major LDS tile of `cols` 16-bit columns read
+// with load_kn: rows land 32 or 96 bytes apart modulo 128, so the four rows
+// of a transpose read hit distinct banks.  Four-byte elements get 16 bytes.
+template <typename T>
+constexpr int kn_pitch(int cols) {
+  return sizeof(T) == 2 ? ((cols * 2) % 128 == 32 || (cols * 2) % 128 == 96 ? cols : cols + 16) : cols + 4;
+}
+
 // Masked KW-fragment of a K-major operand: elements whose k index falls
 // outside [lo, hi) read as zero.
 template <typename T>
@@ -157,10 +241,13 @@ struct CausalSplit {
   }
 };
 
-// waves of the blocks that own causal tiles: one per SIMD, at most T/2
+// Waves of the blocks that own the causal tiles of a Q x Q chunk product:
+// one column pair {p, T-1-p} per wave (8 waves, two per SIMD, at Q = 256).
+// The dCB/CB kernel and the head kernel use the same split, so a wave of one
+// owns exactly the tiles of the same wave of the other.
 template <int Q>
 constexpr int causal_waves() {
-  return (Q / 32) < 4 ? (Q / 32) : 4;
+  return Q / 32;
 }
 
 __device__ __forceinline__ int clamp_seq(int s, int nseqs) {
