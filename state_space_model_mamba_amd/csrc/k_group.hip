@@ -41,8 +41,54 @@ struct DcbCfg {
   static_assert(LDN <= LDP, "C/B slabs reuse the x/dy rows' LDS");
   static constexpr int NV = Q * P / VEC;                 // vectors of x (or dy) per head
   static constexpr int NVT = (NV + NTHR - 1) / NTHR;     // per thread
-  static constexpr size_t LDS = size_t(2) * Q * LDP * sizeof(T) + size_t(3) * Q * 4;
+  static constexpr size_t LDS = size_t(2) * Q * LDP * sizeof(T) + size_t(4) * Q * 4;
 };
+
+// One head's contribution to the owned dCB tiles: dcb[k] += W o (dy x^T) on
+// tile k.  UNI: the chunk has a single segment (the off-diagonal decays are
+// factored through the per-row table er); the two versions keep the unrolled
+// tile sequence free of branches.
+template <typename T, int Q, int P, bool UNI, int NOWN>
+__device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, const T* dyk,
+                                          const float* acs, const float* dtv, const float* erv, const int* lov,
+                                          int wz) {
+  using Cf = DcbCfg<T, Q, P>;
+  constexpr int LDP = Cf::LDP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+#pragma clang loop unroll(full)
+  for (int k = 0; k < Cf::NOWN; ++k) {
+    int I, J;
+    bool second;
+    Cf::Split::tile(wz, k, I, J, second);
+    const f32x4_t m = tile_mma_kk<T>(zero4(), dyk + 16 * I * LDP, LDP, xk + 16 * J * LDP, LDP, 0, P);
+    const int j = 16 * J + r16;
+    const float aj = acs[j], dtj = dtv[j];
+    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+    if (UNI && k < Cf::Split::NOFF) {
+      const float ec = Elem<T>::exp(acs[16 * I] - aj);
+      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(erv + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
+    } else {
+      const int loj = lov[j];
+      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(acs + 16 * I + 4 * kg);
+      const int4 lo4 = *reinterpret_cast<const int4*>(lov + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * kg + r;
+        const int loi = r == 0 ? lo4.x : (r == 1 ? lo4.y : (r == 2 ? lo4.z : lo4.w));
+        const bool ok = (j <= i) & (loi == loj);
+        // exp of a non-positive argument only; masked entries use a zero argument
+        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
+        e4[r] = ok ? e : 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dcb[k][r] += (e4[r] * dtj) * m[r];
+    // keep the scheduler from hoisting every tile's fragment loads at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
@@ -53,14 +99,15 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   T* s_dyk = s_xk + Q * LDP;
   float* s_acs = reinterpret_cast<float*>(s_dyk + Q * LDP);
   float* s_dt = s_acs + Q;
-  int* s_lo = reinterpret_cast<int*>(s_dt + Q);
+  float* s_er = s_dt + Q;
+  int* s_lo = reinterpret_cast<int*>(s_er + Q);
 
   const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
   const int64_t lb = xcd_logical_block(blockIdx.x, total);
   const int c = static_cast<int>(lb % pb.nc);
   const int64_t bg = lb / pb.nc;
   const int g = static_cast<int>(bg % pb.G), b = static_cast<int>(bg / pb.G);
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
   const T* xg = static_cast<const T*>(pb.x);
   const T* dyg = static_cast<const T*>(pb.dy);
@@ -135,21 +182,43 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
       return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
     };
   };
+  // each head's x / dy rows and Acs / dt are loaded into registers while the
+  // previous head's tiles are multiplied
+  static_assert(NTHR >= Q, "one thread per chunk position");
   RowStage<T, Q, P, NTHR> st_x, st_dy;
-
-  for (int hh = 0; hh < pb.hpg; ++hh) {
+  float acs_n = 0.f, dt_n = 0.f;
+  auto load_head = [&](int hh) {
     const int h = g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    __syncthreads();
     st_x.load(head_row(xg, h));
     st_dy.load(head_row(dyg, h));
+    if (tid < Q) {
+      acs_n = pb.acs[bhc * Q + tid];
+      dt_n = pb.dtc[bhc * Q + tid];
+    }
+  };
+  // A chunk without sequence starts after position 0 has one segment and a
+  // non-increasing Acs: there the decay of an off-diagonal tile is
+  // er_i * exp(Acs_{16I} - Acs_j) with er_i = exp(Acs_i - Acs_{16 floor(i/16)}),
+  // both factors <= 1.
+  const bool uniform = __builtin_amdgcn_readfirstlane(seg_lo(pb.segpos[bc * Q + Q - 1])) == 0;
+  __syncthreads();   // (keeps the first head's loads out of the CB phase's registers)
+  load_head(0);
+
+  for (int hh = 0; hh < pb.hpg; ++hh) {
+    __syncthreads();
     st_x.store(s_xk, LDP);
     st_dy.store(s_dyk, LDP);
-    for (int i = tid; i < Q; i += NTHR) {
-      s_acs[i] = pb.acs[bhc * Q + i];
-      s_dt[i] = pb.dtc[bhc * Q + i];
+    {
+      const float acs_tile0 = __shfl(acs_n, l & ~15, WAVE);
+      if (tid < Q) {
+        s_acs[tid] = acs_n;
+        s_dt[tid] = dt_n;
+        s_er[tid] = uniform ? Elem<T>::exp(acs_n - acs_tile0) : 0.f;
+      }
     }
     __syncthreads();
+    if (hh + 1 < pb.hpg) load_head(hh + 1);
 
     const int z = opaque_zero();
     const int wz = w + z;
@@ -157,27 +226,12 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
     const T* dyk = s_dyk + z;
     const float* acs = s_acs + z;
     const float* dtv = s_dt + z;
+    const float* erv = s_er + z;
     const int* lov = s_lo + z;
-#pragma clang loop unroll(full)
-    for (int k = 0; k < Cf::NOWN; ++k) {
-      int I, J;
-      bool second;
-      Cf::Split::tile(wz, k, I, J, second);
-      const f32x4_t m = tile_mma_kk<T>(zero4(), dyk + 16 * I * LDP, LDP, xk + 16 * J * LDP, LDP, 0, P);
-      const int j = 16 * J + r16;
-      const int loj = lov[j];
-      const float aj = acs[j], dtj = dtv[j];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * kg + r;
-        const bool ok = (j <= i) && (lov[i] == loj);
-        // exp of a non-positive argument only; masked entries use a zero argument
-        const float e = Elem<T>::exp(ok ? acs[i] - aj : 0.f);
-        dcb[k][r] += (ok ? e * dtj : 0.f) * m[r];
-      }
-      // keep the scheduler from hoisting every tile's fragment loads at once
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    if (uniform)
+      dcb_tiles<T, Q, P, true, Cf::NOWN>(dcb, xk, dyk, acs, dtv, erv, lov, wz);
+    else
+      dcb_tiles<T, Q, P, false, Cf::NOWN>(dcb, xk, dyk, acs, dtv, erv, lov, wz);
   }
 
   // write dCB (row-major) and dCB^T, the owned columns in full (zeros above the diagonal)

@@ -62,6 +62,116 @@ struct HeadCfg {
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
 };
 
+// Phase B over the wave's causal tiles (see the top of the file): G, M,
+// ddt_intra partials, da shares and dx_intra.  UNI: the chunk has a single
+// segment (off-diagonal decays factored through the per-row table er); the
+// two versions keep the unrolled tile sequence free of branches on it.
+template <typename T, int Q, int P, bool UNI>
+__device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&dxt)[2][P / 16], float (&ddti)[2],
+                                           const T* s_xk, const T* s_dyk, const float* s_acs, const float* s_dt,
+                                           const float* s_er, const int* s_seg, float* s_share, int w) {
+  using Cf = HeadCfg<T, Q, P>;
+  using Split = typename Cf::Split;
+  constexpr int PT = Cf::PT, LDP = Cf::LDP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  float below0 = 0.f, below1 = 0.f;   // this lane's column sums of V over the tiles passed (per column slot)
+#pragma clang loop unroll(full)
+  for (int k = 0; k < Split::NOWN; ++k) {
+    int I, J;
+    bool second;
+    Split::tile(w, k, I, J, second);
+    const bool diag = k >= Split::NOFF;   // a constant once unrolled
+    const f32x4_t m = tile_mma_kk<T>(zero4(), s_dyk + 16 * I * LDP, LDP, s_xk + 16 * J * LDP, LDP, 0, P);
+    const int j = 16 * J + r16;
+    const float aj = s_acs[j], dtj = s_dt[j];
+    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+    if (UNI && !diag) {
+      const float ec = Elem<T>::exp(s_acs[16 * I] - aj);
+      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
+    } else {
+      const int loj = seg_lo(s_seg[j]);
+      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
+      const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * kg + r;
+        const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
+        const bool ok = (j <= i) & (seg_lo(sgi) == loj);
+        // exp of a non-positive argument only; masked entries use a zero argument
+        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
+        e4[r] = ok ? e : 0.f;
+      }
+    }
+    float gms = 0.f;
+    f32x4_t v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gv = cb[k][r] * e4[r];
+      cb[k][r] = gv;
+      const float gm = gv * m[r];
+      gms += gm;
+      v[r] = gm * dtj;
+    }
+    // column tile J's share of da at the rows of tile I (see the top of the file):
+    // sh[r] = sum over rows i >= 16I + 4kg + r of V[i][j], then summed over j
+    const float below = second ? below1 : below0;
+    float sfx[4];
+    sfx[3] = v[3];
+    sfx[2] = v[2] + sfx[3];
+    sfx[1] = v[1] + sfx[2];
+    sfx[0] = v[0] + sfx[1];
+    float grp[4];
+    gather_kgroups(sfx[0], grp);   // the 4 row groups' sums of column j
+    const float s2 = grp[3], s1 = s2 + grp[2], s0 = s1 + grp[1];
+    const float lower = kg == 0 ? s0 : (kg == 1 ? s1 : (kg == 2 ? s2 : 0.f));
+    const float base = below + lower;
+    float sh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sh[r] = base + sfx[r];
+      if (diag) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;   // diagonal tile: columns j < k only
+    }
+    if (!diag) {   // (a column's diagonal tile is its last)
+      const float nb = below + (s0 + grp[0]);
+      below0 = second ? below0 : nb;
+      below1 = second ? nb : below1;
+    }
+    // row sums over the 16 lanes (columns): a butterfly that halves the values
+    // per lane at each step; lane r16 < 4 ends with row 2 (r16 & 1) + (r16 >> 1)
+    {
+      const bool odd = (r16 & 1) != 0, hi = (r16 & 2) != 0;
+      const float k0 = odd ? sh[2] : sh[0], k1 = odd ? sh[3] : sh[1];
+      const float t0 = odd ? sh[0] : sh[2], t1 = odd ? sh[1] : sh[3];
+      const float a0 = k0 + dpp_move<0xB1>(t0);   // quad_perm [1,0,3,2]
+      const float a1 = k1 + dpp_move<0xB1>(t1);
+      const float kk = hi ? a1 : a0, tt = hi ? a0 : a1;
+      float rsum = kk + dpp_move<0x4E>(tt);      // quad_perm [2,3,0,1]
+      rsum += dpp_move<0x124>(rsum);             // row_ror:4
+      rsum += dpp_move<0x128>(rsum);             // row_ror:8
+      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum;
+    }
+    // register-direct operands: dy^T values (raw) and the G tile (converted once)
+    typename Mma<T>::rfrag av[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
+    const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
+    // dx^T of the tile's column: slot 0 or 1 (a wave-uniform choice)
+    if (!second) {
+      ddti[0] += gms;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) dxt[0][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[0][pt]);
+    } else {
+      ddti[1] += gms;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) dxt[1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[1][pt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+}
+
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
   using Cf = HeadCfg<T, Q, P>;
@@ -199,99 +309,10 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   float ddti[Cf::NCOL];   // per-lane partial sums of G o M over a column's tiles
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a) ddti[a] = 0.f;
-  float below = 0.f;   // this lane's column sum of V over the column's tiles already passed
-#pragma clang loop unroll(full)
-  for (int k = 0; k < Cf::NOWN; ++k) {
-    int I, J;
-    bool second;
-    Cf::Split::tile(w, k, I, J, second);
-    const f32x4_t m = tile_mma_kk<T>(zero4(), s_dyk + 16 * I * LDP, LDP, s_xk + 16 * J * LDP, LDP, 0, P);
-    const int j = 16 * J + r16;
-    const float aj = s_acs[j], dtj = s_dt[j];
-    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
-    if (uniform && I != J) {
-      const float ec = Elem<T>::exp(s_acs[16 * I] - aj);
-      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
-    } else {
-      const int loj = seg_lo(s_seg[j]);
-      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
-      const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * kg + r;
-        const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
-        const bool ok = (j <= i) && (seg_lo(sgi) == loj);
-        // exp of a non-positive argument only; masked entries use a zero argument
-        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
-        e4[r] = ok ? e : 0.f;
-      }
-    }
-    float gms = 0.f;
-    f32x4_t v;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gv = cb[k][r] * e4[r];
-      cb[k][r] = gv;
-      const float gm = gv * m[r];
-      gms += gm;
-      v[r] = gm * dtj;
-    }
-    // column tile J's share of da at the rows of tile I (see the top of the file):
-    // sh[r] = sum over rows i >= 16I + 4kg + r of V[i][j], then summed over j
-    if (I == T16 - 1) below = 0.f;
-    float sfx[4];
-    sfx[3] = v[3];
-    sfx[2] = v[2] + sfx[3];
-    sfx[1] = v[1] + sfx[2];
-    sfx[0] = v[0] + sfx[1];
-    float grp[4];
-    gather_kgroups(sfx[0], grp);   // the 4 row groups' sums of column j
-    const float s2 = grp[3], s1 = s2 + grp[2], s0 = s1 + grp[1];
-    const float lower = kg == 0 ? s0 : (kg == 1 ? s1 : (kg == 2 ? s2 : 0.f));
-    const float base = below + lower;
-    float sh[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sh[r] = base + sfx[r];
-      if (I == J) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;   // diagonal tile: columns j < k only
-    }
-    below += s0 + grp[0];
-    // row sums over the 16 lanes (columns): a butterfly that halves the values
-    // per lane at each step; lane r16 < 4 ends with row 2 (r16 & 1) + (r16 >> 1)
-    {
-      const bool odd = (r16 & 1) != 0, hi = (r16 & 2) != 0;
-      const float k0 = odd ? sh[2] : sh[0], k1 = odd ? sh[3] : sh[1];
-      const float t0 = odd ? sh[0] : sh[2], t1 = odd ? sh[1] : sh[3];
-      const float a0 = k0 + dpp_move<0xB1>(t0);   // quad_perm [1,0,3,2]
-      const float a1 = k1 + dpp_move<0xB1>(t1);
-      const float kk = hi ? a1 : a0, tt = hi ? a0 : a1;
-      float rsum = kk + dpp_move<0x4E>(tt);      // quad_perm [2,3,0,1]
-      rsum += dpp_move<0x124>(rsum);             // row_ror:4
-      rsum += dpp_move<0x128>(rsum);             // row_ror:8
-      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum;
-    }
-    // register-direct operands: dy^T values (raw) and the G tile (converted once)
-    typename Mma<T>::rfrag av[PT];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
-    const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
-    // dx^T of the tile's column: slot 2q or 2q+1 of its pair (a wave-uniform
-    // choice); both slot indices are constants once the loop is unrolled
-    const int q = k / (T16 + 1);
-    if (!second) {
-      ddti[2 * q] += gms;
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) dxt[2 * q][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q][pt]);
-    } else {
-      ddti[2 * q + 1] += gms;
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt)
-        dxt[2 * q + 1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[2 * q + 1][pt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  if (uniform)
+    head_tiles<T, Q, P, true>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w);
+  else
+    head_tiles<T, Q, P, false>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w);
 
   // ---- phase B2: Z^T = dS B^T for the owned column tiles, slab by slab over N
   // (x and dy rows stay in LDS; B and dS slabs go to the region behind them)

@@ -141,6 +141,11 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) / WAVE; }
+// the same as a scalar (wave-uniform) value: tile indices derived from it
+// stay in scalar registers
+__device__ __forceinline__ int wave_id_s() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / WAVE);
+}
 
 // 16x16 tile product over k in [k_begin, k_end) (multiples of KSTEP):
 //   acc += A[m0.., k] * B[k, n0..]

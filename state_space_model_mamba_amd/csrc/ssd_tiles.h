@@ -210,33 +210,39 @@ __device__ __forceinline__ f32x4_t tile_mma_kk_range(f32x4_t acc, const T* a_bas
 }
 
 // The causal 16x16 tiles (I >= J) of a Q x Q matrix, T = Q/16 tiles per side,
-// split over W waves.  Column tiles are paired as {p, T-1-p} (T+1 causal tiles
-// per pair, so every pair costs the same); wave w owns the pairs
-// p = w, w + W, ... < T/2 and all causal tiles of their columns.
+// split over W = T/2 waves: wave p owns the column pair {p, T-1-p} (T+1 causal
+// tiles, so every wave costs the same).  Its tiles k = 0 .. T are ordered
+//   k <  T-1-p : column p,      row tiles T-1 down to p+1
+//   k <  T-1   : column T-1-p,  row tiles T-1 down to T-p
+//   k == T-1   : diagonal tile (p, p)
+//   k == T     : diagonal tile (T-1-p, T-1-p)
+// so the off-diagonal tiles are exactly k < T-1 (known once unrolled), and
+// each column is walked bottom-up with its diagonal tile after the rest.
+// `second` tells which column of the pair (slot 0 or 1) a tile belongs to.
 template <int T16, int W>
 struct CausalSplit {
-  static_assert(T16 % 2 == 0 && (T16 / 2) % W == 0, "pairs must split evenly over the waves");
-  static constexpr int PPW = T16 / 2 / W;        // pairs per wave
-  static constexpr int NOWN = PPW * (T16 + 1);   // causal tiles per wave
-  static constexpr int NCOL = 2 * PPW;           // owned column tiles per wave
-  // column tile of owned slot a (slots 2q, 2q+1 are the two columns of pair q)
-  static __device__ __forceinline__ int col(int w, int a) {
-    const int p = w + W * (a >> 1);
-    return (a & 1) ? T16 - 1 - p : p;
-  }
-  // tile k of wave w: column J, row tile I, each column walked from the
-  // bottom (I = T-1) up to its diagonal tile (I = J); `second` tells which
-  // column of its pair (slot 2q + second) the tile belongs to (wave-uniform)
+  static_assert(T16 % 2 == 0 && T16 / 2 == W, "one column pair per wave");
+  static constexpr int NOWN = T16 + 1;   // causal tiles per wave
+  static constexpr int NCOL = 2;         // owned column tiles per wave
+  static constexpr int NOFF = T16 - 1;   // off-diagonal tiles per wave
+  // column tile of owned slot a
+  static __device__ __forceinline__ int col(int w, int a) { return a ? T16 - 1 - w : w; }
   static __device__ __forceinline__ void tile(int w, int k, int& I, int& J, bool& second) {
-    const int q = k / (T16 + 1), kk = k % (T16 + 1);
-    const int p = w + W * q;
-    second = kk >= T16 - p;
-    if (!second) {
+    const int p = w;
+    if (k == T16 - 1) {
+      I = J = p;
+      second = false;
+    } else if (k == T16) {
+      I = J = T16 - 1 - p;
+      second = true;
+    } else if (k < T16 - 1 - p) {
       J = p;
-      I = T16 - 1 - kk;
+      I = T16 - 1 - k;
+      second = false;
     } else {
       J = T16 - 1 - p;
-      I = T16 - 1 - (kk - (T16 - p));
+      I = T16 - 1 - (k - (T16 - 1 - p));
+      second = true;
     }
   }
 };
