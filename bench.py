@@ -25,7 +25,7 @@ METRIC = "SSD bwd ms/layer + tokens/s at L=16K (1 GPU); bitwise repeat + % roofl
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_head.hip", "ssd_device.h",
+KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_head.hip", "ssd_device.h",
                   "ssd_tiles.h", "ssd_problem.h"]
 
 

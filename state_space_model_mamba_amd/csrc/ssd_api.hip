@@ -37,7 +37,8 @@ int check_shape(const ssd_shape* s) {
   const int ntg_w = ssd::group_ntile(static_cast<int>(N), is_bf16(s));
   const size_t lim = 160 * 1024;
   if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
-      ssd::group_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim)
+      ssd::dcb_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
+      ssd::dbdc_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim)
     return SSD_ERR_UNSUPPORTED_SHAPE;
   return SSD_OK;
 }

@@ -78,7 +78,8 @@ hipError_t launch_reduce(const Problem& pb, hipStream_t s);
 // Shape support (host side): true when kernels exist for this combination
 // and fit the LDS of one workgroup.
 int group_ntile(int N, bool io_bf16);
-size_t group_lds_bytes(int Q, int P, int NTG, bool io_bf16);
+size_t dcb_lds_bytes(int Q, int P, bool io_bf16);
+size_t dbdc_lds_bytes(int Q, int P, int NTG, bool io_bf16);
 size_t head_lds_bytes(int Q, int P, bool io_bf16);
 
 }  // namespace ssd

@@ -29,6 +29,26 @@ template <typename T> __device__ __forceinline__ float vget(const uint4& v, int 
   return Elem<T>::to_f(vraw<T>(v, e));
 }
 
+// 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as floats,
+// and the reverse with round-to-nearest-even
+template <typename T> __device__ __forceinline__ f32x4_t load4f(const T* p);
+template <> __device__ __forceinline__ f32x4_t load4f<bf16_t>(const bf16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+template <> __device__ __forceinline__ f32x4_t load4f<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <typename T> __device__ __forceinline__ void store4f(T* p, f32x4_t v);
+template <> __device__ __forceinline__ void store4f<bf16_t>(bf16_t* p, f32x4_t v) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4_t));
+}
+template <> __device__ __forceinline__ void store4f<float>(float* p, f32x4_t v) {
+  *reinterpret_cast<f32x4_t*>(p) = v;
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide staging of a ROWS x COLS tile from global memory (rows given by
 // a functor returning the row's first element, or nullptr for a zero row)
@@ -77,6 +97,21 @@ struct RowStage {
       }
     }
   }
+  // row-major with conversion from fp32, 4 elements per store:
+  // lds[r * ld + c] = TOUT(x)  (ld and the row starts keep 4-element groups
+  // 8-byte aligned for bf16 and 16-byte aligned for fp32)
+  template <typename TOUT>
+  __device__ __forceinline__ void store_rows_f32(TOUT* lds, int ld) const {
+    static_assert(sizeof(TIN) == 4 && VEC == 4, "fp32 rows");
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      if (NV % NTHR == 0 || v < NV) {
+        const f32x4_t f = __builtin_bit_cast(f32x4_t, buf[k]);
+        store4f<TOUT>(lds + (v / CV) * ld + (v % CV) * VEC, f);
+      }
+    }
+  }
   // transposed with conversion: lds[c * ld + r] = TOUT(x)
   template <typename TOUT>
   __device__ __forceinline__ void store_transposed(TOUT* lds, int ld) const {
@@ -91,26 +126,6 @@ struct RowStage {
     }
   }
 };
-
-// 4 consecutive elements (8-byte aligned for bf16, 16-byte for fp32) as floats,
-// and the reverse with round-to-nearest-even
-template <typename T> __device__ __forceinline__ f32x4_t load4f(const T* p);
-template <> __device__ __forceinline__ f32x4_t load4f<bf16_t>(const bf16_t* p) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-}
-template <> __device__ __forceinline__ f32x4_t load4f<float>(const float* p) {
-  return *reinterpret_cast<const f32x4_t*>(p);
-}
-template <typename T> __device__ __forceinline__ void store4f(T* p, f32x4_t v);
-template <> __device__ __forceinline__ void store4f<bf16_t>(bf16_t* p, f32x4_t v) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4_t));
-}
-template <> __device__ __forceinline__ void store4f<float>(float* p, f32x4_t v) {
-  *reinterpret_cast<f32x4_t*>(p) = v;
-}
 
 // MFMA fragments of an operand stored with k as the row index ("kn" layout:
 // X[k][m], m contiguous; X points at column m0), k in [k0, k0 + KSTEP):
@@ -142,6 +157,18 @@ __device__ __forceinline__ f32x4_t tile_mma_kn(f32x4_t acc, const T* a, int lda,
                                                int k_begin, int k_end) {
   for (int k = k_begin; k < k_end; k += Mma<T>::KSTEP)
     acc = Mma<T>::mma(load_kn<T>(a, lda, k), load_kn<T>(b, ldb, k), acc);
+  return acc;
+}
+
+// 16x16 tile product with A stored K-major (A(m, k) = a_base[m * lda + k])
+// and B in the kn layout (B(k, n) = b[k * ldb + n]).
+template <typename T>
+__device__ __forceinline__ f32x4_t tile_mma_kk_kn(f32x4_t acc, const T* a_base, int lda, const T* b, int ldb,
+                                                  int k_begin, int k_end) {
+  const int l = lane_id();
+  const T* ap = a_base + (l & 15) * lda + (l >> 4) * Mma<T>::KW;
+  for (int k = k_begin; k < k_end; k += Mma<T>::KSTEP)
+    acc = Mma<T>::mma(Mma<T>::load_k(ap + k), load_kn<T>(b, ldb, k), acc);
   return acc;
 }
 
