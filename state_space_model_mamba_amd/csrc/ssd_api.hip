@@ -26,7 +26,8 @@ int check_shape(const ssd_shape* s) {
   if (s->io_dtype != SSD_IO_BF16 && s->io_dtype != SSD_IO_F32) return SSD_ERR_INVALID_ARG;
   if (s->nheads % s->ngroups) return SSD_ERR_UNSUPPORTED_SHAPE;
   const int64_t Q = s->chunk_size, P = s->headdim, N = s->dstate;
-  if (N % 16 || N > 256) return SSD_ERR_UNSUPPORTED_SHAPE;
+  // dstate slabs are 32 (bf16) or 16 (fp32) columns wide
+  if (N % (is_bf16(s) ? 32 : 16) || N > 256) return SSD_ERR_UNSUPPORTED_SHAPE;
   if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) == ~size_t(0))
     return SSD_ERR_UNSUPPORTED_SHAPE;
   // index arithmetic inside the kernels uses int for positions and block counts

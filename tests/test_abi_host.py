@@ -60,6 +60,8 @@ def test_workspace_size_and_regions():
     (dict(headdim=48), -2),
     (dict(headdim=16), -2),          # bf16 needs headdim % 32 == 0
     (dict(dstate=24), -2),
+    (dict(dstate=48), -2),           # bf16 needs dstate % 32 == 0
+    (dict(io_dtype=ssd.SSD_IO_F32, chunk_size=64, headdim=16, dstate=40), -2),
     (dict(dstate=512), -2),
     (dict(io_dtype=7), -1),
     (dict(batch=0), -1),
