@@ -47,16 +47,17 @@ struct HeadCfg {
   static_assert(NTHR >= Q, "one thread per chunk position");
   static constexpr int PT = P / 16;
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab (divides N)
-  static constexpr int LDN = NS + VEC;
+  static constexpr int NBLK = 128;                      // dstate columns per phase-B2 round
+  static constexpr int LDSN = NBLK + VEC;               // dS rows [p][n] of one round
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
-  static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(Q + P) * LDN) * sizeof(T);  // x, dy rows + B, dS slabs
+  static constexpr int DSV = (P * NBLK / 4 + NTHR - 1) / NTHR;   // fp32 dS vectors per thread per round
+  static constexpr int NKB = NBLK / Mma<T>::KSTEP;      // B fragments per owned column per round
+  static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(P) * LDSN) * sizeof(T);  // x, dy, dS rows
   // da shares: [column tile J][position]
   static constexpr size_t RS_FLOATS = size_t(T16) * Q;
   // vectors: acs dt w ee ddacs ddtp sj dd daint er (10 Q floats) + seg (Q ints) + red (W + 8)
   static constexpr size_t RV_FLOATS = size_t(11) * Q + W + 8;
-  static constexpr int NSB = 4;   // B / dS slabs of phase B2 in flight
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
@@ -66,10 +67,60 @@ struct HeadCfg {
 // ddt_intra partials, da shares and dx_intra.  UNI: the chunk has a single
 // segment (off-diagonal decays factored through the per-row table er); the
 // two versions keep the unrolled tile sequence free of branches on it.
-template <typename T, int Q, int P, bool UNI>
+// PF: the dS rows of the first phase-B2 round (see B2Operands) are requested
+// in the middle of the tile sequence, into registers the CB tiles already
+// used have freed (every tile sequence reaches that point).
+// Operands of phase B2 (Z^T = dS B^T) for one round of NBLK dstate columns:
+// dS (P x NBLK fp32, one 16-byte piece per thread and slot) and this lane's B
+// fragments of the two owned column tiles (bf16: one 16-byte piece per k-step).
+template <typename T, int Q, int P>
+struct B2Operands {
+  using Cf = HeadCfg<T, Q, P>;
+  static constexpr int KS = Mma<T>::KSTEP, KW = Mma<T>::KW;
+  uint4 dsr[Cf::DSV];
+  typename Mma<T>::frag bf[2][KW == 8 ? Cf::NKB : 1];
+  const float* ds_base;   // dS of this (b, h, c): [P][N]
+  const T* brow[2];       // this lane's B row of each owned column tile, at k = 8 (lane / 16) (nullptr past L)
+  int N;
+  __device__ __forceinline__ int cols(int nb) const { return N - nb * Cf::NBLK < Cf::NBLK ? N - nb * Cf::NBLK : Cf::NBLK; }
+  __device__ __forceinline__ void load_ds(int nb) {
+    const int vr = cols(nb) / 4, nv = P * vr;
+#pragma unroll
+    for (int q = 0; q < Cf::DSV; ++q) {
+      const int v = static_cast<int>(threadIdx.x) + q * Cf::NTHR;
+      dsr[q] = zero_u4();
+      if (v < nv) dsr[q] = ld_global16(ds_base + (v / vr) * N + nb * Cf::NBLK + 4 * (v % vr));
+    }
+  }
+  __device__ __forceinline__ void load_b(int nb) {
+    if constexpr (KW == 8) {
+#pragma unroll
+      for (int kb = 0; kb < Cf::NKB; ++kb)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          bf[a][kb] = Mma<T>::zero();
+          if (brow[a] && kb * KS < cols(nb))
+            bf[a][kb] = __builtin_bit_cast(typename Mma<T>::frag, ld_global16(brow[a] + nb * Cf::NBLK + kb * KS));
+        }
+    }
+  }
+  // dS round nb -> LDS rows [p][n] in the I/O dtype
+  __device__ __forceinline__ void store_ds(int nb, T* s_dsk) const {
+    const int vr = cols(nb) / 4, nv = P * vr;
+#pragma unroll
+    for (int q = 0; q < Cf::DSV; ++q) {
+      const int v = static_cast<int>(threadIdx.x) + q * Cf::NTHR;
+      if (v < nv)
+        store4f<T>(s_dsk + (v / vr) * Cf::LDSN + 4 * (v % vr), __builtin_bit_cast(f32x4_t, dsr[q]));
+    }
+  }
+};
+
+template <typename T, int Q, int P, bool UNI, bool PF>
 __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&dxt)[2][P / 16], float (&ddti)[2],
                                            const T* s_xk, const T* s_dyk, const float* s_acs, const float* s_dt,
-                                           const float* s_er, const int* s_seg, float* s_share, int w) {
+                                           const float* s_er, const int* s_seg, float* s_share, int w,
+                                           B2Operands<T, Q, P>& b2) {
   using Cf = HeadCfg<T, Q, P>;
   using Split = typename Cf::Split;
   constexpr int PT = Cf::PT, LDP = Cf::LDP;
@@ -157,32 +208,41 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
     const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
-    // dx^T of the tile's column: slot 0 or 1 (a wave-uniform choice)
-    if (!second) {
-      ddti[0] += gms;
+    // dx^T of the tile's column, slot 0 or 1.  For the off-diagonal tiles the
+    // slot is a run-time (wave-uniform) choice: both slots take a product, one
+    // of them with a zero G, so the unrolled tile sequence has no branches and
+    // neighbouring tiles can overlap.
+    if (diag) {
+      const int sl = k == Split::NOFF ? 0 : 1;   // a constant once unrolled
+      ddti[sl] += gms;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) dxt[0][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[0][pt]);
+      for (int pt = 0; pt < PT; ++pt) dxt[sl][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[sl][pt]);
     } else {
-      ddti[1] += gms;
+      const typename Mma<T>::rfrag zf = Mma<T>::rfrag_zero();
+      const typename Mma<T>::rfrag g0 = second ? zf : gfrag, g1 = second ? gfrag : zf;
+      ddti[0] += second ? 0.f : gms;
+      ddti[1] += second ? gms : 0.f;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) dxt[1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[1][pt]);
+      for (int pt = 0; pt < PT; ++pt) {
+        dxt[0][pt] = Mma<T>::mma_rd(av[pt], g0, dxt[0][pt]);
+        dxt[1][pt] = Mma<T>::mma_rd(av[pt], g1, dxt[1][pt]);
+      }
     }
+    if (PF && k == (Split::NOFF + 1) / 2) b2.load_ds(0);
     __builtin_amdgcn_sched_barrier(0);
   }
-
 }
 
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
-  constexpr int NS = Cf::NS, LDN = Cf::LDN, LDP = Cf::LDP;
+  constexpr int LDP = Cf::LDP, LDSN = Cf::LDSN;
   constexpr int R = Q / WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* s_xk = reinterpret_cast<T*>(smem);
   T* s_dyk = s_xk + Q * LDP;
-  T* s_bz = s_dyk + Q * LDP;
-  T* s_dsz = s_bz + Q * LDN;
+  T* s_dsk = s_dyk + Q * LDP;   // dS rows [p][n] in the I/O dtype
   float* s_share = reinterpret_cast<float*>(smem + Cf::OFF_RS);
   float* s_acs = reinterpret_cast<float*>(smem + Cf::OFF_RV);
   float* s_dt = s_acs + Q;
@@ -228,20 +288,11 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
 
   // Row sources of the global tiles this block stages (nullptr = zero row).
-  auto bc_row = [&](const T* base, int n0) {
-    return [=](int i) -> const T* {
-      const int t = c * Q + i;
-      return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 : nullptr;
-    };
-  };
   auto head_row = [&](const T* base) {
     return [=](int i) -> const T* {
       const int t = c * Q + i;
       return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
     };
-  };
-  auto ds_row = [&](int n0) {
-    return [=](int p) -> const float* { return pb.dstate + (bhc * P + p) * pb.N + n0; };
   };
 
   // ---- phase A: the CB tiles of this wave (formed once per group by the
@@ -277,17 +328,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   st_x.store(s_xk, LDP);
   st_dy.store(s_dyk, LDP);
   __syncthreads();
-  // the first NSB slabs of phase B2 in flight during phase B
-  constexpr int NSB = Cf::NSB;
-  RowStage<T, Q, NS, NTHR> st_bz[NSB];
-  RowStage<float, P, NS, NTHR> st_ds[NSB];
-#pragma unroll
-  for (int sl = 0; sl < NSB; ++sl) {
-    if (sl * NS < pb.N) {
-      st_bz[sl].load(bc_row(Bg, sl * NS));
-      st_ds[sl].load(ds_row(sl * NS));
-    }
-  }
   {
     float dd = 0.f;
     for (int v = tid; v < Q * P / VEC; v += NTHR) {
@@ -309,39 +349,60 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   float ddti[Cf::NCOL];   // per-lane partial sums of G o M over a column's tiles
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a) ddti[a] = 0.f;
+  B2Operands<T, Q, P> b2;
+  b2.ds_base = pb.dstate + bhc * P * pb.N;
+  b2.N = pb.N;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = c * Q + 16 * Cf::Split::col(w, a) + r16;
+    b2.brow[a] = t < pb.L ? Bg + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + kg * Mma<T>::KW
+                          : nullptr;
+  }
+  constexpr bool PF = Mma<T>::KW == 8;   // bf16: first B2 round prefetched during phase B
   if (uniform)
-    head_tiles<T, Q, P, true>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w);
+    head_tiles<T, Q, P, true, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2);
   else
-    head_tiles<T, Q, P, false>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w);
+    head_tiles<T, Q, P, false, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2);
 
-  // ---- phase B2: Z^T = dS B^T for the owned column tiles, slab by slab over N
-  // (x and dy rows stay in LDS; B and dS slabs go to the region behind them)
+  // ---- phase B2: Z^T = dS B^T for the owned column tiles, in rounds of NBLK
+  // dstate columns: dS rows from LDS (A operand), the owned columns' B rows
+  // straight from memory (B operand)
   f32x4_t zt[Cf::NCOL][PT];
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a)
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) zt[a][pt] = zero4();
-  for (int nb = 0; nb < pb.N; nb += NSB * NS) {
+  {
+    constexpr int KS = Mma<T>::KSTEP, KW = Mma<T>::KW;
+    for (int nb = 0; nb * Cf::NBLK < pb.N; ++nb) {
+      if (!PF || nb > 0) b2.load_ds(nb);
+      b2.load_b(nb);
+      if (nb > 0) __syncthreads();   // the previous round's dS rows are read
+      b2.store_ds(nb, s_dsk);
+      __syncthreads();
+      const int ncols = b2.cols(nb);
+      if constexpr (KW == 8) {
 #pragma unroll
-    for (int sl = 0; sl < NSB; ++sl) {
-      const int n0 = nb + sl * NS;
-      if (n0 < pb.N) {
-        __syncthreads();
-        st_bz[sl].store(s_bz, LDN);
-        st_ds[sl].template store_convert<T>(s_dsz, LDN);
-        __syncthreads();
-        if (n0 + NSB * NS < pb.N) {
-          st_bz[sl].load(bc_row(Bg, n0 + NSB * NS));
-          st_ds[sl].load(ds_row(n0 + NSB * NS));
+        for (int kb = 0; kb < Cf::NKB; ++kb) {
+          if (kb * KS >= ncols) break;
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            const auto af = Mma<T>::load_k(s_dsk + (16 * pt + r16) * LDSN + kg * KW + kb * KS);
+#pragma unroll
+            for (int a = 0; a < Cf::NCOL; ++a) zt[a][pt] = Mma<T>::mma(af, b2.bf[a][kb], zt[a][pt]);
+          }
         }
-        const int z = opaque_zero();
-        const int wz = w + z;
+      } else {
+        for (int k0 = 0; k0 < ncols; k0 += KS) {
+          typename Mma<T>::frag bf[Cf::NCOL];
 #pragma unroll
-        for (int a = 0; a < Cf::NCOL; ++a) {
-          const int J = Cf::Split::col(wz, a);
+          for (int a = 0; a < Cf::NCOL; ++a) bf[a] = b2.brow[a] ? b2.brow[a][nb * Cf::NBLK + k0] : 0.f;
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-            zt[a][pt] = tile_mma_kk<T>(zt[a][pt], s_dsz + z + 16 * pt * LDN, LDN, s_bz + z + 16 * J * LDN, LDN, 0, NS);
+          for (int pt = 0; pt < PT; ++pt) {
+            const auto af = Mma<T>::load_k(s_dsk + (16 * pt + r16) * LDSN + kg * KW + k0);
+#pragma unroll
+            for (int a = 0; a < Cf::NCOL; ++a) zt[a][pt] = Mma<T>::mma(af, bf[a], zt[a][pt]);
+          }
         }
       }
     }

@@ -105,6 +105,7 @@ template <> struct Mma<bf16_t> {
   static __device__ __forceinline__ f32x4_t mma_rd(rfrag a, rfrag x, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, x, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ rfrag rfrag_zero() { return rfrag{0, 0, 0, 0}; }
   // rd-fragment of a row-major 16 x 16 block M (LDS, rows = k):
   // lane gets M[4 * (lane / 16) + r][lane % 16], r = 0..3
   static __device__ __forceinline__ rfrag rfrag_load_kn(const bf16_t* blk, int ld) {
@@ -128,6 +129,7 @@ template <> struct Mma<float> {
   static __device__ __forceinline__ rfrag rfrag_load(const float* p, int stride) {
     return f32x4_t{p[0], p[stride], p[2 * stride], p[3 * stride]};
   }
+  static __device__ __forceinline__ rfrag rfrag_zero() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
   static __device__ __forceinline__ rfrag rfrag_load_kn(const float* blk, int ld) {
     const int l = static_cast<int>(threadIdx.x) & 63;
     return rfrag_load(blk + 4 * (l >> 4) * ld + (l & 15), ld);
