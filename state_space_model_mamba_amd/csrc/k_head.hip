@@ -286,6 +286,11 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   }
   const float acs_end = pb.acs[bhc * Q + Q - 1];
   const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
+  const float Dh = pb.D ? pb.D[h] : 0.f;
+  const float Ah = pb.A[h];
+  float endd = 0.f;   // the chunk-end term's dstate-tile partials, in tile order (used by wave 0)
+  if (tid < WAVE)
+    for (int nt = 0; nt < pb.ntg; ++nt) endd += pb.endd[bhc * pb.ntg + nt];
 
   // Row sources of the global tiles this block stages (nullptr = zero row).
   auto head_row = [&](const T* base) {
@@ -409,7 +414,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   }
 
   // ---- phase C: dx, and per column the ddt parts and s_j
-  const float Dh = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a) {
     const int J = Cf::Split::col(w, a);
@@ -457,8 +461,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 #pragma unroll
     for (int e = 0; e < R; ++e) v += s_sj[l * R + e];
     const float sum_s = wave_sum(v);
-    float endd = 0.f;
-    for (int nt = 0; nt < pb.ntg; ++nt) endd += pb.endd[bhc * pb.ntg + nt];
     tail = sum_s + Elem<T>::exp(acs_end) * endd;
   }
   __syncthreads();
@@ -500,7 +502,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
     float carry = __shfl_down(vl, 1, WAVE);
     if (l == WAVE - 1) carry = 0.f;
     int seen = 0;
-    const float Ah = pb.A[h];
     float dap = 0.f;
 #pragma unroll
     for (int e = R - 1; e >= 0; --e) {
