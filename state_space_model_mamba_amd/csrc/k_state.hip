@@ -28,11 +28,15 @@ struct StateCfg {
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int LDX = kn_pitch<T>(P);   // x / dy chunk rows [j][p]
   static constexpr int LDB = kn_pitch<T>(NT);  // B / C tile rows [j][n]
+  static constexpr int NTHR = NT * 8;          // 4 waves for 32 state columns, 8 for 64
+  static constexpr int NW = NTHR / WAVE;
   static constexpr int XV = Q * P / VEC;       // 16-byte vectors of one x/dy chunk
-  static constexpr int NXV = (XV + 255) / 256;
+  static constexpr int NXV = (XV + NTHR - 1) / NTHR;
   static constexpr int BV = Q * NT / VEC;      // vectors of one B/C chunk tile
-  static constexpr int NBV = (BV + 255) / 256;
-  static constexpr int PT = P / 16, NTT = NT / 16, NTILE = PT * NTT, TPW = (NTILE + 3) / 4;
+  static constexpr int NBV = (BV + NTHR - 1) / NTHR;
+  static constexpr int PT = P / 16, NTT = NT / 16, NTILE = PT * NTT, TPW = (NTILE + NW - 1) / NW;
+  static_assert(NW % NTT == 0, "a wave's tiles share their state-column tile");
+  static_assert(NTHR >= Q, "one thread per chunk position");
   static_assert(P % 16 == 0 && NT % 16 == 0 && Q % Mma<T>::KSTEP == 0, "tile shape");
 };
 
@@ -47,7 +51,7 @@ __device__ __forceinline__ void load_chunk_rows(const Problem& pb, const void* s
   const T* bs = static_cast<const T*>(src_gn);
 #pragma unroll
   for (int k = 0; k < Cf::NXV; ++k) {
-    const int v = tid + 256 * k;
+    const int v = tid + Cf::NTHR * k;
     xr[k] = zero_u4();
     if (v < Cf::XV) {
       const int j = v / (P / Cf::VEC), pv = v % (P / Cf::VEC), t = c * Q + j;
@@ -57,7 +61,7 @@ __device__ __forceinline__ void load_chunk_rows(const Problem& pb, const void* s
   }
 #pragma unroll
   for (int k = 0; k < Cf::NBV; ++k) {
-    const int v = tid + 256 * k;
+    const int v = tid + Cf::NTHR * k;
     br[k] = zero_u4();
     if (v < Cf::BV) {
       const int j = v / (NT / Cf::VEC), nv = v % (NT / Cf::VEC), t = c * Q + j;
@@ -103,7 +107,7 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < Cf::NXV; ++k) {
-    const int v = tid + 256 * k;
+    const int v = tid + Cf::NTHR * k;
     if (v < Cf::XV) {
       const int j = v / (P / VEC), pv = v % (P / VEC);
       const float sc = s_scale[j];
@@ -115,7 +119,7 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
   }
 #pragma unroll
   for (int k = 0; k < Cf::NBV; ++k) {
-    const int v = tid + 256 * k;
+    const int v = tid + Cf::NTHR * k;
     if (v < Cf::BV) {
       const int j = v / (NT / VEC), nv = v % (NT / VEC);
       *reinterpret_cast<uint4*>(s_b + j * Cf::LDB + nv * VEC) = br[k];
@@ -124,7 +128,7 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
 }
 
 template <typename T, int Q, int P, int NT>
-__global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
   __shared__ __attribute__((aligned(16))) T s_xt[Q * Cf::LDX];
   __shared__ __attribute__((aligned(16))) T s_bt[Q * Cf::LDB];
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
     const int s_last = clamp_seq(cur.seqbase + nstart - 1, pb.nseqs);
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
-      const int tile = w + 4 * k;
+      const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const f32x4_t S = tile_mma_kn<T>(zero4(), s_xt + pt * 16, Cf::LDX, s_bt + nt * 16, Cf::LDB, kb, Q);
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) void k_state_fwd(Problem pb) {
 }
 
 template <typename T, int Q, int P, int NT>
-__global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
+__global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
   __shared__ __attribute__((aligned(16))) T s_dyt[Q * Cf::LDX];
   __shared__ __attribute__((aligned(16))) T s_ct[Q * Cf::LDB];
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
     const float decay = Elem<T>::exp(cur.acs_end);
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
-      const int tile = w + 4 * k;
+      const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const int n = n0 + nt * 16 + r16;
@@ -283,23 +287,26 @@ __global__ __launch_bounds__(256) void k_state_bwd(Problem pb) {
 // N-tile width of the state kernels.
 static int state_nt(int N, bool bf16) {
   (void)bf16;
-  return (N % 32 == 0) ? 32 : 16;
+  return (N % 64 == 0) ? 64 : (N % 32 == 0) ? 32 : 16;
 }
 
 template <typename T, int Q, int P, int NT>
 static hipError_t launch_state_t(const Problem& pb, bool fwd, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * (pb.N / NT);
   if (fwd)
-    hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pb);
+    hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), 0, s, pb);
   else
-    hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pb);
+    hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), 0, s, pb);
   return hipGetLastError();
 }
 
 template <typename T, int Q, int P>
 static hipError_t launch_state_qp(const Problem& pb, bool fwd, hipStream_t s) {
-  if (state_nt(pb.N, sizeof(T) == 2) == 32) return launch_state_t<T, Q, P, 32>(pb, fwd, s);
-  return launch_state_t<T, Q, P, 16>(pb, fwd, s);
+  const int nt = state_nt(pb.N, sizeof(T) == 2);
+  if (nt == 64) return launch_state_t<T, Q, P, 64>(pb, fwd, s);
+  if (nt == 32) return launch_state_t<T, Q, P, 32>(pb, fwd, s);
+  if constexpr (Q <= 128) return launch_state_t<T, Q, P, 16>(pb, fwd, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
