@@ -26,8 +26,8 @@ namespace ssd {
 template <typename T, int Q, int P, int NT>
 struct StateCfg {
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int LDX = kn_pitch<T>(P);   // x / dy chunk rows [j][p]
-  static constexpr int LDB = kn_pitch<T>(NT);  // B / C tile rows [j][n]
+  using XTile = KnTile<T, P>;                  // x / dy chunk rows [j][p]
+  using BTile = KnTile<T, NT>;                 // B / C tile rows [j][n]
   static constexpr int NTHR = NT * 8;          // 4 waves for 32 state columns, 8 for 64
   static constexpr int NW = NTHR / WAVE;
   static constexpr int XV = Q * P / VEC;       // 16-byte vectors of one x/dy chunk
@@ -114,7 +114,7 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
       T o[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) o[e] = Elem<T>::from_f(vget<T>(xr[k], e) * sc);
-      *reinterpret_cast<uint4*>(s_x + j * Cf::LDX + pv * VEC) = *reinterpret_cast<const uint4*>(o);
+      *reinterpret_cast<uint4*>(s_x + Cf::XTile::at(j, pv * VEC)) = *reinterpret_cast<const uint4*>(o);
     }
   }
 #pragma unroll
@@ -122,7 +122,7 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
     const int v = tid + Cf::NTHR * k;
     if (v < Cf::BV) {
       const int j = v / (NT / VEC), nv = v % (NT / VEC);
-      *reinterpret_cast<uint4*>(s_b + j * Cf::LDB + nv * VEC) = br[k];
+      *reinterpret_cast<uint4*>(s_b + Cf::BTile::at(j, nv * VEC)) = br[k];
     }
   }
 }
@@ -130,8 +130,8 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_xt[Q * Cf::LDX];
-  __shared__ __attribute__((aligned(16))) T s_bt[Q * Cf::LDB];
+  __shared__ __attribute__((aligned(16))) T s_xt[Q * Cf::XTile::LD];
+  __shared__ __attribute__((aligned(16))) T s_bt[Q * Cf::BTile::LD];
   __shared__ float s_w[Q];
 
   const int ntiles = pb.N / NT;
@@ -173,7 +173,9 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
       const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
-        const f32x4_t S = tile_mma_kn<T>(zero4(), s_xt + pt * 16, Cf::LDX, s_bt + nt * 16, Cf::LDB, kb, Q);
+        f32x4_t S = zero4();
+        for (int k0 = kb; k0 < Q; k0 += Mma<T>::KSTEP)
+          S = Mma<T>::mma(Cf::XTile::frag(s_xt, pt * 16, k0), Cf::BTile::frag(s_bt, nt * 16, k0), S);
         const int n = n0 + nt * 16 + r16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -197,8 +199,8 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_dyt[Q * Cf::LDX];
-  __shared__ __attribute__((aligned(16))) T s_ct[Q * Cf::LDB];
+  __shared__ __attribute__((aligned(16))) T s_dyt[Q * Cf::XTile::LD];
+  __shared__ __attribute__((aligned(16))) T s_ct[Q * Cf::BTile::LD];
   __shared__ float s_e[Q];
   __shared__ int s_seg[Q];
   __shared__ int s_segstart[Q + 1];
@@ -247,20 +249,25 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const int n = n0 + nt * 16 + r16;
-        const T* ab = s_dyt + pt * 16;
-        const T* bb = s_ct + nt * 16;
+
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           pb.dstate[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = dout[k][r];
         if (nstart == 0) {
-          const f32x4_t R = tile_mma_kn<T>(zero4(), ab, Cf::LDX, bb, Cf::LDB, 0, Q);
+          f32x4_t R = zero4();
+#pragma unroll
+          for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
+            R = Mma<T>::mma(Cf::XTile::frag(s_dyt, pt * 16, k0), Cf::BTile::frag(s_ct, nt * 16, k0), R);
 #pragma unroll
           for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + decay * dout[k][r];
         } else {
           f32x4_t dhoff = zero4();
           for (int m = 0; m < nseg; ++m) {
             const int lo = s_segstart[m], hi = s_segstart[m + 1];
-            const f32x4_t R = tile_mma_kn_range<T>(zero4(), ab, Cf::LDX, bb, Cf::LDB, lo, hi);
+            f32x4_t R = zero4();
+            for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
+              R = Mma<T>::mma(mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi),
+                              Cf::BTile::frag(s_ct, nt * 16, k0), R);
             const int rank = seg_rank(s_seg[lo]);
             if (rank == 0) {
               dhoff = R;

@@ -203,6 +203,55 @@ constexpr int kn_pitch(int cols) {
   return sizeof(T) == 2 ? ((cols * 2) % 128 == 32 || (cols * 2) % 128 == 96 ? cols : cols + 16) : cols + 4;
 }
 
+// A row-major LDS tile of COLS columns read with the transpose reads.
+// 128-byte rows of 16-bit elements are stored unpadded, their 32-byte
+// segments XOR-swizzled by (row mod 4): the four rows of one transpose read
+// then cover all banks once.  Other widths are padded (kn_pitch).
+template <typename T, int COLS>
+struct KnTile {
+  static constexpr bool SWZ = sizeof(T) == 2 && COLS * 2 == 128;
+  static constexpr int LD = SWZ ? COLS : kn_pitch<T>(COLS);
+  // element offset of (row, col); 8 consecutive columns from a multiple of 8
+  // stay contiguous
+  static __device__ __forceinline__ int at(int row, int col) {
+    if constexpr (SWZ)
+      return row * LD + ((((col >> 4) ^ (row & 3))) << 4) + (col & 15);
+    else
+      return row * LD + col;
+  }
+  // MFMA fragment of the 16 columns from m0 (a multiple of 16), k rows from k0
+  // (the load_kn layout)
+  static __device__ __forceinline__ typename Mma<T>::frag frag(const T* base, int m0, int k0) {
+    const int l = lane_id();
+    if constexpr (sizeof(T) == 2) {
+      const int row = k0 + 8 * (l >> 4) + ((l & 15) >> 2);
+      const int col = m0 + 4 * (l & 3);
+      const s16x4_t lo = lds_read_tr16(base + at(row, col));
+      const s16x4_t hi = lds_read_tr16(base + at(row + 4, col));
+      return __builtin_bit_cast(typename Mma<T>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return base[at(k0 + (l >> 4), m0 + (l & 15))];
+    }
+  }
+};
+
+// A fragment (k values k0 + KW (lane / 16) + e) with the k values outside
+// [lo, hi) zeroed.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag mask_k(typename Mma<T>::frag f, int k0, int lo, int hi) {
+  constexpr int KW = Mma<T>::KW;
+  const int kg = lane_id() >> 4;
+  if constexpr (KW == 1) {
+    return (k0 + kg < lo || k0 + kg >= hi) ? 0.f : f;
+  } else {
+    u16x8_t v = __builtin_bit_cast(u16x8_t, f);
+#pragma unroll
+    for (int e = 0; e < KW; ++e)
+      if (k0 + KW * kg + e < lo || k0 + KW * kg + e >= hi) v[e] = 0;
+    return __builtin_bit_cast(typename Mma<T>::frag, v);
+  }
+}
+
 // Masked KW-fragment of a K-major operand: elements whose k index falls
 // outside [lo, hi) read as zero.
 template <typename T>
