@@ -28,7 +28,7 @@ struct StateCfg {
   static constexpr int VEC = Vec16<T>::N;
   using XTile = KnTile<T, P>;                  // x / dy chunk rows [j][p]
   using BTile = KnTile<T, NT>;                 // B / C tile rows [j][n]
-  static constexpr int NTHR = NT * 8;          // 4 waves for 32 state columns, 8 for 64
+  static constexpr int NTHR = NT * 16;         // 8 waves for 32 state columns, 16 for 64
   static constexpr int NW = NTHR / WAVE;
   static constexpr int XV = Q * P / VEC;       // 16-byte vectors of one x/dy chunk
   static constexpr int NXV = (XV + NTHR - 1) / NTHR;
