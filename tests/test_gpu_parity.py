@@ -85,6 +85,16 @@ def test_bf16_chunk_sizes_packed(chunk):
     check(inputs, chunk, TOL["bf16"], f"bf16 Q{chunk}")
 
 
+@pytest.mark.parametrize("dstate,chunk", [(96, 64), (160, 128)])
+def test_bf16_dstate_not_multiple_of_64(dstate, chunk):
+    # 32-column state tiles, 32-column dB/dC tiles, and a partial (and, at
+    # dstate 160, a second) round of the head kernel's dS B^T product
+    w = Workload("bf16_n%d" % dstate, batch=1, seqlen=300, nheads=4, headdim=64, ngroups=2, dstate=dstate,
+                 chunk=chunk, dtype="bf16", seed=13)
+    inputs = packed(make_inputs(w), [[120, 180]])
+    check(inputs, chunk, TOL["bf16"], f"bf16 N{dstate} Q{chunk}")
+
+
 def test_bf16_headdim32_dstate64():
     w = Workload("bf16_p32", batch=1, seqlen=520, nheads=6, headdim=32, ngroups=3, dstate=64,
                  chunk=128, dtype="bf16", seed=12)
