@@ -4,10 +4,14 @@
 // bwd kernel for mamba2"): per (batch, chunk) it finds the sequence starts,
 // records each position's segment, and for every head writes
 //   Acs_i = sum of dt_k * A_h over k from the start of i's segment to i,
-// restarted at the chunk start and at every sequence start.  The scan order
-// is fixed by the chunk size alone: each lane adds its Q/64 consecutive
-// elements in order, then a 64-lane Hillis-Steele segmented scan over lane
-// totals (shuffle offsets 1, 2, ..., 32) supplies the carry.  That page
+// restarted at the chunk start and at every sequence start.  Every kernel
+// downstream takes exp(Acs_i - Acs_j) from these values, and gradients such
+// as dA add many such terms with heavy cancellation, so Acs is scanned in
+// double and rounded to float once.  The scan order is fixed by the chunk
+// size alone: the chunk is scanned as Q/64 runs of 64 positions, each with a
+// 64-lane Hillis-Steele segmented scan (shuffle offsets 1, 2, ..., 32) that
+// starts from the previous run's last value.
+// A block handles 32 heads of one (batch, chunk).  That page
 // reports that a cumsum whose result changes with the block shape broke
 // run-to-run reproducibility; here the result does not depend on how many
 // heads a block handles or on the launch shape.
@@ -16,14 +20,24 @@
 
 namespace ssd {
 
+constexpr int PREP_HEADS = 32;   // heads per block of k_prep
+
 template <int Q>
 __global__ __launch_bounds__(256) void k_prep(Problem pb) {
   static_assert(Q % WAVE == 0 && Q <= 256, "chunk size");
   constexpr int R = Q / WAVE;
-  const int c = blockIdx.x, b = blockIdx.y;
+  constexpr int LDD = PREP_HEADS + 1;   // dt rows in LDS, padded
+  const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * PREP_HEADS;
   const int tid = threadIdx.x;
   __shared__ int s_flag[Q], s_lo[Q], s_rank[Q];
+  __shared__ float s_dt[Q * LDD];
 
+  // this block's heads of the chunk's dt rows, coalesced (zeros past L and past H)
+  for (int v = tid; v < Q * PREP_HEADS; v += 256) {
+    const int i = v / PREP_HEADS, hh = v % PREP_HEADS, t = c * Q + i;
+    s_dt[i * LDD + hh] =
+        (t < pb.L && h0 + hh < pb.H) ? pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h0 + hh] : 0.f;
+  }
   if (tid < Q) {
     const int t = c * Q + tid;
     int st = 0;
@@ -55,58 +69,46 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
     __syncthreads();
   }
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-  if (tid < Q) pb.segpos[bc * Q + tid] = s_lo[tid] | (s_rank[tid] << 16);
-  if (tid == 0) {
-    pb.cinfo[bc * CINFO + 0] = s_rank[Q - 1];
-    pb.cinfo[bc * CINFO + 1] = 0;
-    pb.cinfo[bc * CINFO + 2] = 0;
+  if (blockIdx.z == 0) {
+    if (tid < Q) pb.segpos[bc * Q + tid] = s_lo[tid] | (s_rank[tid] << 16);
+    if (tid == 0) {
+      pb.cinfo[bc * CINFO + 0] = s_rank[Q - 1];
+      pb.cinfo[bc * CINFO + 1] = 0;
+      pb.cinfo[bc * CINFO + 2] = 0;
+    }
   }
 
-  const int w = wave_id(), l = lane_id(), nw = blockDim.x / WAVE;
-  for (int h = w; h < pb.H; h += nw) {
-    const float Ah = pb.A[h];
-    float loc[R], d[R];
-    int f[R];
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const int i = l * R + e, t = c * Q + i;
-      d[e] = (t < pb.L) ? pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] : 0.f;
-      f[e] = (i == 0) || s_flag[i];
-    }
-    float run = 0.f;
-    int any = 0;
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const float a = d[e] * Ah;
-      if (f[e]) {
-        run = a;
-        any = 1;
-      } else {
-        run += a;
-      }
-      loc[e] = run;
-    }
-    float v = run;
-    int fl = any;
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-      const float vu = __shfl_up(v, off, WAVE);
-      const int fu = __shfl_up(fl, off, WAVE);
-      if (l >= off) {
-        if (!fl) v = vu + v;
-        fl |= fu;
-      }
-    }
-    float carry = __shfl_up(v, 1, WAVE);
-    if (l == 0) carry = 0.f;
-    int seen = 0;
+  // Segmented inclusive cumsum of a = dt A over the chunk, per head, in one
+  // order fixed by Q alone: the chunk is cut into R runs of 64 positions
+  // (lane l holds position 64 e + l); each run is scanned across the wave
+  // with a Hillis-Steele segmented scan (shuffle offsets 1, 2, ..., 32), and
+  // each run starts from the carry of the previous one.
+  const int w = wave_id(), l = lane_id();
+  for (int hh = w; hh < PREP_HEADS && h0 + hh < pb.H; hh += 4) {
+    const int h = h0 + hh;
+    const double Ah = pb.A[h];
     const int64_t out = ((static_cast<int64_t>(b) * pb.H + h) * pb.nc + c) * Q;
+    double carry = 0.0;
 #pragma unroll
     for (int e = 0; e < R; ++e) {
-      const int i = l * R + e;
-      if (f[e]) seen = 1;
-      pb.acs[out + i] = seen ? loc[e] : loc[e] + carry;
-      pb.dtc[out + i] = d[e];
+      const int i = 64 * e + l;
+      const float d = s_dt[i * LDD + hh];
+      int fl = (i == 0) || s_flag[i];
+      double v = static_cast<double>(d) * Ah;
+#pragma unroll
+      for (int off = 1; off < WAVE; off <<= 1) {
+        const double vu = __shfl_up(v, off, WAVE);
+        const int fu = __shfl_up(fl, off, WAVE);
+        if (l >= off) {
+          if (!fl) v = vu + v;
+          fl |= fu;
+        }
+      }
+      // positions not preceded by a start within this run continue the carry
+      const double acs = fl ? v : carry + v;
+      pb.acs[out + i] = static_cast<float>(acs);
+      pb.dtc[out + i] = d;
+      carry = __shfl(acs, WAVE - 1, WAVE);
     }
   }
 }
@@ -138,24 +140,38 @@ __global__ __launch_bounds__(256) void k_seqbase(Problem pb) {
   }
 }
 
-// dA_h = sum over (b, c) of slot_dA[b, c, h], dD likewise: one thread per
-// head, summing in ascending (b, c) order.
+// dA_h = sum over (b, c) of slot_dA[b, c, h], dD likewise.  The slots of a
+// head can cancel heavily, so they are added in double and rounded once:
+// lane l sums the slots l, l + 64, ... in ascending order, then the 64 lane
+// sums meet in a fixed xor butterfly (offsets 32, 16, ..., 1).  The double
+// sum's own error is at most about n 2^-53 times the slots' absolute sum,
+// far below the rounding already in each float slot.  One wave per head.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = WAVE / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_reduce(Problem pb) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.x * 4 + wave_id();
   if (h >= pb.H) return;
-  float a = 0.f, d = 0.f;
-  for (int b = 0; b < pb.B; ++b)
-    for (int c = 0; c < pb.nc; ++c) {
-      const int64_t k = (static_cast<int64_t>(b) * pb.nc + c) * pb.H + h;
-      a += pb.slot_dA[k];
-      d += pb.slot_dD[k];
-    }
-  pb.dA[h] = a;
-  if (pb.dD) pb.dD[h] = d;
+  const int l = lane_id();
+  const int n = pb.B * pb.nc;
+  double a = 0.0, d = 0.0;
+  for (int k = l; k < n; k += WAVE) {
+    a += static_cast<double>(pb.slot_dA[static_cast<int64_t>(k) * pb.H + h]);
+    d += static_cast<double>(pb.slot_dD[static_cast<int64_t>(k) * pb.H + h]);
+  }
+  a = wave_sum_f64(a);
+  d = wave_sum_f64(d);
+  if (l == 0) {
+    pb.dA[h] = static_cast<float>(a);
+    if (pb.dD) pb.dD[h] = static_cast<float>(d);
+  }
 }
 
 hipError_t launch_prep(const Problem& pb, hipStream_t s) {
-  const dim3 grid(pb.nc, pb.B);
+  const dim3 grid(pb.nc, pb.B, (pb.H + PREP_HEADS - 1) / PREP_HEADS);
   switch (pb.Q) {
     case 64: hipLaunchKernelGGL(k_prep<64>, grid, dim3(256), 0, s, pb); break;
     case 128: hipLaunchKernelGGL(k_prep<128>, grid, dim3(256), 0, s, pb); break;
@@ -169,7 +185,7 @@ hipError_t launch_prep(const Problem& pb, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const Problem& pb, hipStream_t s) {
-  hipLaunchKernelGGL(k_reduce, dim3((pb.H + 255) / 256), dim3(256), 0, s, pb);
+  hipLaunchKernelGGL(k_reduce, dim3((pb.H + 3) / 4), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 
