@@ -51,6 +51,7 @@ struct HeadCfg {
   static constexpr int LDSN = NBLK + VEC;               // dS rows [p][n] of one round
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
+  static constexpr int CBD = NOWN < 2 ? NOWN : 2;   // CB tiles requested ahead of their use
   static constexpr int DSV = (P * NBLK / 4 + NTHR - 1) / NTHR;   // fp32 dS vectors per thread per round
   static constexpr int NKB = NBLK / Mma<T>::KSTEP;      // B fragments per owned column per round
   static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(P) * LDSN) * sizeof(T);  // x, dy, dS rows
@@ -116,42 +117,104 @@ struct B2Operands {
   }
 };
 
+// LDS operands of one causal tile, requested one tile ahead so that their
+// latency hides behind the previous tile's arithmetic.
+template <typename T, int Q, int P, bool UNI>
+struct TileIn {
+  static constexpr int MK = P / Mma<T>::KSTEP;   // k-steps of M = dy x^T
+  typename Mma<T>::frag ma[MK], mb[MK];           // dy rows of tile I, x rows of tile J
+  typename Mma<T>::rfrag av[P / 16];              // dy^T of rows I (the dx product's A operand)
+  f32x4_t rowv;   // UNI off-diagonal: er of rows I; otherwise Acs of rows I
+  int4 seg4;      // segments of rows I (not UNI off-diagonal)
+  float acs_i0;   // Acs at row 16 I (UNI off-diagonal)
+  float aj, dtj;  // Acs, dt of this lane's column
+  int segj;       // segment of this lane's column (not UNI off-diagonal)
+};
+
+template <typename T, int Q, int P, bool UNI, bool DIAG>
+__device__ __forceinline__ void tile_load(TileIn<T, Q, P, UNI>& in, int I, int J, const T* s_xk, const T* s_dyk,
+                                          const float* s_acs, const float* s_dt, const float* s_er,
+                                          const int* s_seg) {
+  using Cf = HeadCfg<T, Q, P>;
+  constexpr int LDP = Cf::LDP, KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* ap = s_dyk + (16 * I + r16) * LDP + kg * KW;
+  const T* bp = s_xk + (16 * J + r16) * LDP + kg * KW;
+#pragma unroll
+  for (int s = 0; s < TileIn<T, Q, P, UNI>::MK; ++s) {
+    in.ma[s] = Mma<T>::load_k(ap + s * KS);
+    in.mb[s] = Mma<T>::load_k(bp + s * KS);
+  }
+#pragma unroll
+  for (int pt = 0; pt < P / 16; ++pt) in.av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
+  const int j = 16 * J + r16;
+  in.aj = s_acs[j];
+  in.dtj = s_dt[j];
+  if constexpr (UNI && !DIAG) {
+    in.acs_i0 = s_acs[16 * I];
+    in.rowv = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
+  } else {
+    in.segj = s_seg[j];
+    in.rowv = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
+    in.seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+  }
+}
+
 template <typename T, int Q, int P, bool UNI, bool PF>
 __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&dxt)[2][P / 16], float (&ddti)[2],
                                            const T* s_xk, const T* s_dyk, const float* s_acs, const float* s_dt,
                                            const float* s_er, const int* s_seg, float* s_share, int w,
-                                           B2Operands<T, Q, P>& b2) {
+                                           B2Operands<T, Q, P>& b2, const float* cbsrc) {
   using Cf = HeadCfg<T, Q, P>;
   using Split = typename Cf::Split;
-  constexpr int PT = Cf::PT, LDP = Cf::LDP;
+  using In = TileIn<T, Q, P, UNI>;
+  constexpr int CBD = Cf::CBD;
+  constexpr int PT = Cf::PT;
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
   float below0 = 0.f, below1 = 0.f;   // this lane's column sums of V over the tiles passed (per column slot)
+  In cur;
+  {
+    int I, J;
+    bool second;
+    Split::tile(w, 0, I, J, second);
+    tile_load<T, Q, P, UNI, Split::NOFF == 0>(cur, I, J, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+  }
 #pragma clang loop unroll(full)
   for (int k = 0; k < Split::NOWN; ++k) {
     int I, J;
     bool second;
     Split::tile(w, k, I, J, second);
     const bool diag = k >= Split::NOFF;   // a constant once unrolled
-    const f32x4_t m = tile_mma_kk<T>(zero4(), s_dyk + 16 * I * LDP, LDP, s_xk + 16 * J * LDP, LDP, 0, P);
+    if (k + CBD < Split::NOWN) cb[k + CBD] = *reinterpret_cast<const f32x4_t*>(cbsrc + (k + CBD) * 256);
+    In nxt;
+    if (k + 1 < Split::NOWN) {
+      int In_, Jn;
+      bool sn;
+      Split::tile(w, k + 1, In_, Jn, sn);
+      if (k + 1 >= Split::NOFF)
+        tile_load<T, Q, P, UNI, true>(nxt, In_, Jn, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+      else
+        tile_load<T, Q, P, UNI, false>(nxt, In_, Jn, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+    }
+    f32x4_t m = zero4();
+#pragma unroll
+    for (int s = 0; s < In::MK; ++s) m = Mma<T>::mma(cur.ma[s], cur.mb[s], m);
     const int j = 16 * J + r16;
-    const float aj = s_acs[j], dtj = s_dt[j];
+    const float aj = cur.aj, dtj = cur.dtj;
     f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
     if (UNI && !diag) {
-      const float ec = Elem<T>::exp(s_acs[16 * I] - aj);
-      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
+      const float ec = Elem<T>::exp(cur.acs_i0 - aj);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
+      for (int r = 0; r < 4; ++r) e4[r] = cur.rowv[r] * ec;
     } else {
-      const int loj = seg_lo(s_seg[j]);
-      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
-      const int4 seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
+      const int loj = seg_lo(cur.segj);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * kg + r;
-        const int sgi = r == 0 ? seg4.x : (r == 1 ? seg4.y : (r == 2 ? seg4.z : seg4.w));
+        const int sgi = r == 0 ? cur.seg4.x : (r == 1 ? cur.seg4.y : (r == 2 ? cur.seg4.z : cur.seg4.w));
         const bool ok = (j <= i) & (seg_lo(sgi) == loj);
         // exp of a non-positive argument only; masked entries use a zero argument
-        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
+        const float e = Elem<T>::exp(ok ? cur.rowv[r] - aj : 0.f);
         e4[r] = ok ? e : 0.f;
       }
     }
@@ -204,9 +267,7 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum;
     }
     // register-direct operands: dy^T values (raw) and the G tile (converted once)
-    typename Mma<T>::rfrag av[PT];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
+    const typename Mma<T>::rfrag(&av)[PT] = cur.av;
     const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
     // dx^T of the tile's column, slot 0 or 1.  For the off-diagonal tiles the
     // slot is a run-time (wave-uniform) choice: both slots take a product, one
@@ -229,6 +290,7 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       }
     }
     if (PF && k == (Split::NOFF + 1) / 2) b2.load_ds(0);
+    if (k + 1 < Split::NOWN) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -266,7 +328,7 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const int g = static_cast<int>(rest % pb.G);
   const int b = static_cast<int>(rest / pb.G);
   const int h = g * pb.hpg + hh;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
   const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
   const T* xg = static_cast<const T*>(pb.x);
@@ -302,11 +364,11 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 
   // ---- phase A: the CB tiles of this wave (formed once per group by the
   // dCB kernel, same split) and the x, dy rows, all requested up front
-  f32x4_t cb[Cf::NOWN];
+  f32x4_t cb[Cf::NOWN];   // the first CBD now, the others during phase B
+  const float* cbsrc = pb.cbt + (bgc * W + w) * Cf::NOWN * 256 + l * 4;
   {
-    const float* src = pb.cbt + (bgc * W + w) * Cf::NOWN * 256 + l * 4;
 #pragma unroll
-    for (int k = 0; k < Cf::NOWN; ++k) cb[k] = *reinterpret_cast<const f32x4_t*>(src + k * 256);
+    for (int k = 0; k < Cf::CBD; ++k) cb[k] = *reinterpret_cast<const f32x4_t*>(cbsrc + k * 256);
   }
   RowStage<T, Q, P, NTHR> st_x, st_dy;
   st_x.load(head_row(xg));
@@ -365,9 +427,9 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   }
   constexpr bool PF = Mma<T>::KW == 8;   // bf16: first B2 round prefetched during phase B
   if (uniform)
-    head_tiles<T, Q, P, true, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2);
+    head_tiles<T, Q, P, true, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
   else
-    head_tiles<T, Q, P, false, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2);
+    head_tiles<T, Q, P, false, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
 
   // ---- phase B2: Z^T = dS B^T for the owned column tiles, in rounds of NBLK
   // dstate columns: dS rows from LDS (A operand), the owned columns' B rows
