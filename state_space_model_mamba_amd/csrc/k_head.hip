@@ -117,6 +117,22 @@ struct B2Operands {
   }
 };
 
+// Row sums over the 16 lanes of a row group (the columns of a tile) of a
+// tile's 4 values per lane: a butterfly that halves the values per lane at
+// each step; lane r16 < 4 ends with row 2 (r16 & 1) + (r16 >> 1) of its group.
+__device__ __forceinline__ float rowsum_quads(const float (&x)[4], int r16) {
+  const bool odd = (r16 & 1) != 0, hi = (r16 & 2) != 0;
+  const float k0 = odd ? x[2] : x[0], k1 = odd ? x[3] : x[1];
+  const float t0 = odd ? x[0] : x[2], t1 = odd ? x[1] : x[3];
+  const float a0 = k0 + dpp_move<0xB1>(t0);   // quad_perm [1,0,3,2]
+  const float a1 = k1 + dpp_move<0xB1>(t1);
+  const float kk = hi ? a1 : a0, tt = hi ? a0 : a1;
+  float rsum = kk + dpp_move<0x4E>(tt);      // quad_perm [2,3,0,1]
+  rsum += dpp_move<0x124>(rsum);             // row_ror:4
+  rsum += dpp_move<0x128>(rsum);             // row_ror:8
+  return rsum;
+}
+
 // LDS operands of one causal tile, requested one tile ahead so that their
 // latency hides behind the previous tile's arithmetic.
 template <typename T, int Q, int P, bool UNI>
@@ -171,7 +187,9 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   constexpr int CBD = Cf::CBD;
   constexpr int PT = Cf::PT;
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
-  float below0 = 0.f, below1 = 0.f;   // this lane's column sums of V over the tiles passed (per column slot)
+  // per owned column: this lane's part (its 4 rows) of the column sums of V
+  // over the tiles passed, and the totals of those tiles
+  float colp0 = 0.f, colp1 = 0.f, bsum0 = 0.f, bsum1 = 0.f;
   In cur;
   {
     int I, J;
@@ -228,43 +246,47 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       gms += gm;
       v[r] = gm * dtj;
     }
-    // column tile J's share of da at the rows of tile I (see the top of the file):
-    // sh[r] = sum over rows i >= 16I + 4kg + r of V[i][j], then summed over j
-    const float below = second ? below1 : below0;
-    float sfx[4];
+    // column tile J's share of da at the rows of tile I (see the top of the file)
+    float sfx[4];   // in-lane suffix sums over the lane's 4 rows
     sfx[3] = v[3];
     sfx[2] = v[2] + sfx[3];
     sfx[1] = v[1] + sfx[2];
     sfx[0] = v[0] + sfx[1];
-    float grp[4];
-    gather_kgroups(sfx[0], grp);   // the 4 row groups' sums of column j
-    const float s2 = grp[3], s1 = s2 + grp[2], s0 = s1 + grp[1];
-    const float lower = kg == 0 ? s0 : (kg == 1 ? s1 : (kg == 2 ? s2 : 0.f));
-    const float base = below + lower;
-    float sh[4];
+    if (diag) {
+      // S[kappa][j] = sum over rows i >= kappa of V[i][j] (all of column j's
+      // tiles below included), kept for j < kappa only, then summed over j
+      const int sl = k == Split::NOFF ? 0 : 1;   // a constant once unrolled
+      const float below = sum_kgroups(sl ? colp1 : colp0);
+      float grp[4];
+      gather_kgroups(sfx[0], grp);   // the 4 row groups' sums of column j
+      const float s2 = grp[3], s1 = s2 + grp[2], s0 = s1 + grp[1];
+      const float lower = kg == 0 ? s0 : (kg == 1 ? s1 : (kg == 2 ? s2 : 0.f));
+      const float base = below + lower;
+      float sh[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sh[r] = base + sfx[r];
-      if (diag) sh[r] = (r16 < 4 * kg + r) ? sh[r] : 0.f;   // diagonal tile: columns j < k only
-    }
-    if (!diag) {   // (a column's diagonal tile is its last)
-      const float nb = below + (s0 + grp[0]);
-      below0 = second ? below0 : nb;
-      below1 = second ? nb : below1;
-    }
-    // row sums over the 16 lanes (columns): a butterfly that halves the values
-    // per lane at each step; lane r16 < 4 ends with row 2 (r16 & 1) + (r16 >> 1)
-    {
-      const bool odd = (r16 & 1) != 0, hi = (r16 & 2) != 0;
-      const float k0 = odd ? sh[2] : sh[0], k1 = odd ? sh[3] : sh[1];
-      const float t0 = odd ? sh[0] : sh[2], t1 = odd ? sh[1] : sh[3];
-      const float a0 = k0 + dpp_move<0xB1>(t0);   // quad_perm [1,0,3,2]
-      const float a1 = k1 + dpp_move<0xB1>(t1);
-      const float kk = hi ? a1 : a0, tt = hi ? a0 : a1;
-      float rsum = kk + dpp_move<0x4E>(tt);      // quad_perm [2,3,0,1]
-      rsum += dpp_move<0x124>(rsum);             // row_ror:4
-      rsum += dpp_move<0x128>(rsum);             // row_ror:8
+      for (int r = 0; r < 4; ++r) sh[r] = (r16 < 4 * kg + r) ? base + sfx[r] : 0.f;
+      const float rsum = rowsum_quads(sh, r16);
       if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum;
+    } else {
+      // Every column of an off-diagonal tile lies before every row, so the
+      // share at row kappa is the tile's row-suffix sum at kappa plus the
+      // totals of the column's tiles below: row sums of the in-lane suffixes,
+      // then the later row groups' totals (read from one lane each) and the
+      // running total below, all in one fixed order.
+      colp0 += second ? 0.f : sfx[0];   // this lane's part of its column's sum
+      colp1 += second ? sfx[0] : 0.f;
+      const float rsum = rowsum_quads(sfx, r16);
+      const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 0));
+      const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 16));
+      const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 32));
+      const float t3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 48));
+      const float u2 = t3, u1 = u2 + t2, u0 = u1 + t1;
+      const float lower = kg == 0 ? u0 : (kg == 1 ? u1 : (kg == 2 ? u2 : 0.f));
+      const float btot = second ? bsum1 : bsum0;
+      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum + (lower + btot);
+      const float tot = u0 + t0;
+      bsum0 = second ? bsum0 : bsum0 + tot;
+      bsum1 = second ? bsum1 + tot : bsum1;
     }
     // register-direct operands: dy^T values (raw) and the G tile (converted once)
     const typename Mma<T>::rfrag(&av)[PT] = cur.av;
