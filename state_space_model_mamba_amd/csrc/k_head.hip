@@ -187,9 +187,12 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   constexpr int CBD = Cf::CBD;
   constexpr int PT = Cf::PT;
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
-  // per owned column: this lane's part (its 4 rows) of the column sums of V
-  // over the tiles passed, and the totals of those tiles
-  float colp0 = 0.f, colp1 = 0.f, bsum0 = 0.f, bsum1 = 0.f;
+  // per owned column (slot 1 for the column being walked, slot 0 for the
+  // first column once it ends): this lane's part (its 4 rows) of the column
+  // sums of V over the tiles passed; and the totals of the walked column's
+  // tiles passed
+  float colp0 = 0.f, colp1 = 0.f, bsum = 0.f;
+  const int n0 = Cf::T16 - 1 - w;   // off-diagonal tiles of the first column
   In cur;
   {
     int I, J;
@@ -273,8 +276,7 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       // totals of the column's tiles below: row sums of the in-lane suffixes,
       // then the later row groups' totals (read from one lane each) and the
       // running total below, all in one fixed order.
-      colp0 += second ? 0.f : sfx[0];   // this lane's part of its column's sum
-      colp1 += second ? sfx[0] : 0.f;
+      colp1 += sfx[0];   // this lane's part of its column's sum
       const float rsum = rowsum_quads(sfx, r16);
       const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 0));
       const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 16));
@@ -282,33 +284,38 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       const float t3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsum), 48));
       const float u2 = t3, u1 = u2 + t2, u0 = u1 + t1;
       const float lower = kg == 0 ? u0 : (kg == 1 ? u1 : (kg == 2 ? u2 : 0.f));
-      const float btot = second ? bsum1 : bsum0;
-      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum + (lower + btot);
-      const float tot = u0 + t0;
-      bsum0 = second ? bsum0 : bsum0 + tot;
-      bsum1 = second ? bsum1 + tot : bsum1;
+      if (r16 < 4) s_share[J * Q + 16 * I + 4 * kg + 2 * (r16 & 1) + (r16 >> 1)] = rsum + (lower + bsum);
+      bsum += u0 + t0;
     }
     // register-direct operands: dy^T values (raw) and the G tile (converted once)
     const typename Mma<T>::rfrag(&av)[PT] = cur.av;
     const typename Mma<T>::rfrag gfrag = Mma<T>::rfrag_from_acc(cb[k]);
-    // dx^T of the tile's column, slot 0 or 1.  For the off-diagonal tiles the
-    // slot is a run-time (wave-uniform) choice: both slots take a product, one
-    // of them with a zero G, so the unrolled tile sequence has no branches and
-    // neighbouring tiles can overlap.
+    // dx^T of the tile's column: the off-diagonal tiles of both columns
+    // accumulate into slot 1, whose content moves to slot 0 when the first
+    // column ends (see below); the diagonal tiles come last, one per slot.
     if (diag) {
       const int sl = k == Split::NOFF ? 0 : 1;   // a constant once unrolled
       ddti[sl] += gms;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) dxt[sl][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[sl][pt]);
     } else {
-      const typename Mma<T>::rfrag zf = Mma<T>::rfrag_zero();
-      const typename Mma<T>::rfrag g0 = second ? zf : gfrag, g1 = second ? gfrag : zf;
-      ddti[0] += second ? 0.f : gms;
-      ddti[1] += second ? gms : 0.f;
+      ddti[1] += gms;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        dxt[0][pt] = Mma<T>::mma_rd(av[pt], g0, dxt[0][pt]);
-        dxt[1][pt] = Mma<T>::mma_rd(av[pt], g1, dxt[1][pt]);
+      for (int pt = 0; pt < PT; ++pt) dxt[1][pt] = Mma<T>::mma_rd(av[pt], gfrag, dxt[1][pt]);
+      // The wave's first column ends after tile n0 - 1 (a wave-uniform
+      // branch, taken once): its sums move to slot 0 and slot 1 restarts for
+      // the second column.
+      if (k >= Cf::T16 / 2 - 1 && k + 1 == n0) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          dxt[0][pt] = dxt[1][pt];
+          dxt[1][pt] = zero4();
+        }
+        ddti[0] = ddti[1];
+        ddti[1] = 0.f;
+        colp0 = colp1;
+        colp1 = 0.f;
+        bsum = 0.f;
       }
     }
     if (PF && k == (Split::NOFF + 1) / 2) b2.load_ds(0);
