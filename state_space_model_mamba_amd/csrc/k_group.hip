@@ -33,49 +33,139 @@ struct DcbCfg {
   static constexpr int NV = Q * P / VEC;                 // vectors of x (or dy) per head
   static constexpr int NVT = (NV + NTHR - 1) / NTHR;     // per thread
   static constexpr size_t LDS = size_t(2) * Q * LDP * sizeof(T) + size_t(4) * Q * 4;
+  // dCB output staging: RB rows of LDR elements in the x / dy rows' LDS
+  static constexpr int LDR = Q + VEC;
+  static constexpr int RB_FIT = (2 * Q * LDP / LDR) / 16 * 16;
+  static constexpr int RB = RB_FIT >= Q ? Q : (RB_FIT >= 128 ? 128 : (RB_FIT >= 64 ? 64 : (RB_FIT >= 32 ? 32 : 16)));
+  static_assert(RB >= 16 && Q % RB == 0 && size_t(RB) * LDR <= size_t(2) * Q * LDP, "dCB staging rows");
 };
+
+// Row operands of one causal tile of one head, requested one tile ahead so
+// that their latency hides behind the previous tile's arithmetic.
+template <typename T, int P>
+struct DcbTileIn {
+  static constexpr int MK = P / Mma<T>::KSTEP;   // k-steps of dy x^T
+  typename Mma<T>::frag ma[MK];                   // dy rows of tile I
+  f32x4_t rowv;   // UNI off-diagonal: er of rows I; otherwise Acs of rows I
+  int4 lo4;       // segment starts of rows I (not UNI off-diagonal)
+  float acs_i0;   // Acs at row 16 I (UNI off-diagonal)
+};
+
+template <typename T, int Q, int P, bool UNI, bool DIAG>
+__device__ __forceinline__ void dcb_tile_load(DcbTileIn<T, P>& in, int I, const T* dyk, const float* acs,
+                                              const float* erv, const int* lov) {
+  constexpr int LDP = DcbCfg<T, Q, P>::LDP, KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* ap = dyk + (16 * I + r16) * LDP + kg * KW;
+#pragma unroll
+  for (int s = 0; s < DcbTileIn<T, P>::MK; ++s) in.ma[s] = Mma<T>::load_k(ap + s * KS);
+  if constexpr (UNI && !DIAG) {
+    in.acs_i0 = acs[16 * I];
+    in.rowv = *reinterpret_cast<const f32x4_t*>(erv + 16 * I + 4 * kg);
+  } else {
+    in.rowv = *reinterpret_cast<const f32x4_t*>(acs + 16 * I + 4 * kg);
+    in.lo4 = *reinterpret_cast<const int4*>(lov + 16 * I + 4 * kg);
+  }
+}
+
+// Column operands of the column tile being walked: the x rows (B operand of
+// dy x^T) and this lane's column's Acs, dt and segment start.
+template <typename T, int P>
+struct DcbColumn {
+  typename Mma<T>::frag mb[P / Mma<T>::KSTEP];
+  float aj, dtj;
+  int loj;
+};
+
+template <typename T, int Q, int P>
+__device__ __forceinline__ void dcb_column_load(DcbColumn<T, P>& cl, int J, const T* xk, const float* acs,
+                                                const float* dtv, const int* lov) {
+  constexpr int LDP = DcbCfg<T, Q, P>::LDP, KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* bp = xk + (16 * J + r16) * LDP + kg * KW;
+#pragma unroll
+  for (int s = 0; s < P / KS; ++s) cl.mb[s] = Mma<T>::load_k(bp + s * KS);
+  const int j = 16 * J + r16;
+  cl.aj = acs[j];
+  cl.dtj = dtv[j];
+  cl.loj = lov[j];
+}
 
 // One head's contribution to the owned dCB tiles: dcb[k] += W o (dy x^T) on
 // tile k.  UNI: the chunk has a single segment (the off-diagonal decays are
 // factored through the per-row table er); the two versions keep the unrolled
-// tile sequence free of branches.
+// tile sequence free of branches on it.  The wave walks its first column's
+// off-diagonal tiles, then its second column's, then the two diagonal tiles;
+// the column operands are reloaded where the column changes (a wave-uniform
+// branch at a wave-dependent tile, taken once).
 template <typename T, int Q, int P, bool UNI, int NOWN>
 __device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, const T* dyk,
                                           const float* acs, const float* dtv, const float* erv, const int* lov,
                                           int wz) {
   using Cf = DcbCfg<T, Q, P>;
-  constexpr int LDP = Cf::LDP;
+  using Split = typename Cf::Split;
+  using In = DcbTileIn<T, P>;
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int n0 = Cf::T16 - 1 - wz;   // off-diagonal tiles of the first column
+  In cur;
+  DcbColumn<T, P> col;
+  {
+    int I, J;
+    bool second;
+    Split::tile(wz, 0, I, J, second);
+    dcb_tile_load<T, Q, P, UNI, Split::NOFF == 0>(cur, I, dyk, acs, erv, lov);
+    dcb_column_load<T, Q, P>(col, J, xk, acs, dtv, lov);
+  }
 #pragma clang loop unroll(full)
   for (int k = 0; k < Cf::NOWN; ++k) {
     int I, J;
     bool second;
-    Cf::Split::tile(wz, k, I, J, second);
-    const f32x4_t m = tile_mma_kk<T>(zero4(), dyk + 16 * I * LDP, LDP, xk + 16 * J * LDP, LDP, 0, P);
-    const int j = 16 * J + r16;
-    const float aj = acs[j], dtj = dtv[j];
-    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
-    if (UNI && k < Cf::Split::NOFF) {
-      const float ec = Elem<T>::exp(acs[16 * I] - aj);
-      const f32x4_t er = *reinterpret_cast<const f32x4_t*>(erv + 16 * I + 4 * kg);
+    Split::tile(wz, k, I, J, second);
+    In nxt;
+    if (k + 1 < Cf::NOWN) {
+      int In_, Jn;
+      bool sn;
+      Split::tile(wz, k + 1, In_, Jn, sn);
+      if (k + 1 >= Split::NOFF)
+        dcb_tile_load<T, Q, P, UNI, true>(nxt, In_, dyk, acs, erv, lov);
+      else
+        dcb_tile_load<T, Q, P, UNI, false>(nxt, In_, dyk, acs, erv, lov);
+    }
+    f32x4_t m = zero4();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) e4[r] = er[r] * ec;
+    for (int s = 0; s < In::MK; ++s) m = Mma<T>::mma(cur.ma[s], col.mb[s], m);
+    const int j = 16 * J + r16;
+    const float aj = col.aj, dtj = col.dtj;
+    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+    if (UNI && k < Split::NOFF) {
+      const float ec = Elem<T>::exp(cur.acs_i0 - aj);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = cur.rowv[r] * ec;
     } else {
-      const int loj = lov[j];
-      const f32x4_t acs4 = *reinterpret_cast<const f32x4_t*>(acs + 16 * I + 4 * kg);
-      const int4 lo4 = *reinterpret_cast<const int4*>(lov + 16 * I + 4 * kg);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * kg + r;
-        const int loi = r == 0 ? lo4.x : (r == 1 ? lo4.y : (r == 2 ? lo4.z : lo4.w));
-        const bool ok = (j <= i) & (loi == loj);
+        const int loi = r == 0 ? cur.lo4.x : (r == 1 ? cur.lo4.y : (r == 2 ? cur.lo4.z : cur.lo4.w));
+        const bool ok = (j <= i) & (loi == col.loj);
         // exp of a non-positive argument only; masked entries use a zero argument
-        const float e = Elem<T>::exp(ok ? acs4[r] - aj : 0.f);
+        const float e = Elem<T>::exp(ok ? cur.rowv[r] - aj : 0.f);
         e4[r] = ok ? e : 0.f;
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) dcb[k][r] += (e4[r] * dtj) * m[r];
+    // the tile's sums are complete here: keeps them from being sunk past the
+    // column branches below (which would hold every tile's products live)
+    asm volatile("" : "+v"(dcb[k]));
+    if (k + 1 < Cf::NOWN) {
+      cur = nxt;
+      // column of tile k + 1
+      if (k + 1 >= Split::NOFF) {
+        dcb_column_load<T, Q, P>(col, k + 1 == Split::NOFF ? wz : Cf::T16 - 1 - wz, xk, acs, dtv, lov);
+      } else if (k >= Cf::T16 / 2 - 1 && k + 1 == n0) {
+        dcb_column_load<T, Q, P>(col, Cf::T16 - 1 - wz, xk, acs, dtv, lov);
+      }
+    }
     // keep the scheduler from hoisting every tile's fragment loads at once
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -225,32 +315,45 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
       dcb_tiles<T, Q, P, false, Cf::NOWN>(dcb, xk, dyk, acs, dtv, erv, lov, wz);
   }
 
-  // write dCB (row-major) and dCB^T, the owned columns in full (zeros above the diagonal)
+  // write dCB (row-major) and dCB^T in full (zeros above the diagonal), RB
+  // rows at a time through the LDS that held the x / dy rows: the block is
+  // cleared, each wave writes its tiles into it, and the rows leave with
+  // 16-byte stores
+  constexpr int RB = Cf::RB, LDR = Cf::LDR, CPR = Q / VEC;   // 16-byte chunks per row
+  T* s_out = s_xk;
   T* dcb_out = static_cast<T*>(pb.dcb) + bgc * Q * Q;
   T* dcbt_out = static_cast<T*>(pb.dcbt) + bgc * Q * Q;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 * (Q / RB); ++pass) {
+    const bool trans = pass >= Q / RB;
+    const int r0 = (trans ? pass - Q / RB : pass) * RB;   // first output row of the pass
+    __syncthreads();   // the x / dy rows (first pass) or the previous pass's rows are read
+    for (int v = tid; v < RB * CPR; v += NTHR)
+      *reinterpret_cast<uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC) = zero_u4();
+    __syncthreads();
 #pragma clang loop unroll(full)
-  for (int k = 0; k < Cf::NOWN; ++k) {
-    int I, J;
-    bool second;
-    Cf::Split::tile(w, k, I, J, second);
-    const int j = 16 * J + r16;
-    T tv[4];
+    for (int k = 0; k < Cf::NOWN; ++k) {
+      int I, J;
+      bool second;
+      Cf::Split::tile(w, k, I, J, second);
+      if (!trans && 16 * I >= r0 && 16 * I < r0 + RB) {
+        // rows 16 I + 4 kg + r of dCB, column 16 J + r16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      tv[r] = Elem<T>::from_f(dcb[k][r]);
-      dcb_out[static_cast<int64_t>(16 * I + 4 * kg + r) * Q + j] = tv[r];
-      dcbt_out[static_cast<int64_t>(j) * Q + 16 * I + 4 * kg + r] = tv[r];
-    }
-  }
-  // zeros above the diagonal of the owned columns
-  for (int a = 0; a < Cf::Split::NCOL; ++a) {
-    const int J = Cf::Split::col(w, a);
-    const int j = 16 * J + r16;
-    for (int I = 0; I < J; ++I)
-      for (int r = 0; r < 4; ++r) {
-        dcb_out[static_cast<int64_t>(16 * I + 4 * kg + r) * Q + j] = Elem<T>::from_f(0.f);
-        dcbt_out[static_cast<int64_t>(j) * Q + 16 * I + 4 * kg + r] = Elem<T>::from_f(0.f);
+        for (int r = 0; r < 4; ++r)
+          s_out[(16 * I + 4 * kg + r - r0) * LDR + 16 * J + r16] = Elem<T>::from_f(dcb[k][r]);
       }
+      if (trans && 16 * J >= r0 && 16 * J < r0 + RB) {
+        // row 16 J + r16 of dCB^T, columns 16 I + 4 kg .. + 3
+        T* dst = s_out + (16 * J + r16 - r0) * LDR + 16 * I + 4 * kg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[r] = Elem<T>::from_f(dcb[k][r]);
+      }
+    }
+    __syncthreads();
+    T* gout = (trans ? dcbt_out : dcb_out) + static_cast<int64_t>(r0) * Q;
+    for (int v = tid; v < RB * CPR; v += NTHR)
+      *reinterpret_cast<uint4*>(gout + static_cast<int64_t>(v / CPR) * Q + (v % CPR) * VEC) =
+          *reinterpret_cast<const uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC);
   }
 }
 
