@@ -138,39 +138,51 @@ __device__ __forceinline__ float rowsum_quads(const float (&x)[4], int r16) {
 template <typename T, int Q, int P, bool UNI>
 struct TileIn {
   static constexpr int MK = P / Mma<T>::KSTEP;   // k-steps of M = dy x^T
-  typename Mma<T>::frag ma[MK], mb[MK];           // dy rows of tile I, x rows of tile J
+  typename Mma<T>::frag ma[MK];                   // dy rows of tile I
   typename Mma<T>::rfrag av[P / 16];              // dy^T of rows I (the dx product's A operand)
   f32x4_t rowv;   // UNI off-diagonal: er of rows I; otherwise Acs of rows I
   int4 seg4;      // segments of rows I (not UNI off-diagonal)
   float acs_i0;   // Acs at row 16 I (UNI off-diagonal)
-  float aj, dtj;  // Acs, dt of this lane's column
-  int segj;       // segment of this lane's column (not UNI off-diagonal)
 };
 
+// Column operands of the column tile being walked: the x rows (B operand of
+// M = dy x^T) and this lane's column's Acs, dt and segment.
+template <typename T, int P>
+struct HeadColumn {
+  typename Mma<T>::frag mb[P / Mma<T>::KSTEP];
+  float aj, dtj;
+  int segj;
+};
+
+template <typename T, int Q, int P>
+__device__ __forceinline__ void head_column_load(HeadColumn<T, P>& cl, int J, const T* s_xk, const float* s_acs,
+                                                 const float* s_dt, const int* s_seg) {
+  constexpr int LDP = HeadCfg<T, Q, P>::LDP, KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
+  const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* bp = s_xk + (16 * J + r16) * LDP + kg * KW;
+#pragma unroll
+  for (int s = 0; s < P / KS; ++s) cl.mb[s] = Mma<T>::load_k(bp + s * KS);
+  const int j = 16 * J + r16;
+  cl.aj = s_acs[j];
+  cl.dtj = s_dt[j];
+  cl.segj = s_seg[j];
+}
+
 template <typename T, int Q, int P, bool UNI, bool DIAG>
-__device__ __forceinline__ void tile_load(TileIn<T, Q, P, UNI>& in, int I, int J, const T* s_xk, const T* s_dyk,
-                                          const float* s_acs, const float* s_dt, const float* s_er,
-                                          const int* s_seg) {
+__device__ __forceinline__ void tile_load(TileIn<T, Q, P, UNI>& in, int I, const T* s_dyk, const float* s_acs,
+                                          const float* s_er, const int* s_seg) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int LDP = Cf::LDP, KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
   const T* ap = s_dyk + (16 * I + r16) * LDP + kg * KW;
-  const T* bp = s_xk + (16 * J + r16) * LDP + kg * KW;
 #pragma unroll
-  for (int s = 0; s < TileIn<T, Q, P, UNI>::MK; ++s) {
-    in.ma[s] = Mma<T>::load_k(ap + s * KS);
-    in.mb[s] = Mma<T>::load_k(bp + s * KS);
-  }
+  for (int s = 0; s < TileIn<T, Q, P, UNI>::MK; ++s) in.ma[s] = Mma<T>::load_k(ap + s * KS);
 #pragma unroll
   for (int pt = 0; pt < P / 16; ++pt) in.av[pt] = Mma<T>::rfrag_load_kn(s_dyk + 16 * I * LDP + 16 * pt, LDP);
-  const int j = 16 * J + r16;
-  in.aj = s_acs[j];
-  in.dtj = s_dt[j];
   if constexpr (UNI && !DIAG) {
     in.acs_i0 = s_acs[16 * I];
     in.rowv = *reinterpret_cast<const f32x4_t*>(s_er + 16 * I + 4 * kg);
   } else {
-    in.segj = s_seg[j];
     in.rowv = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * I + 4 * kg);
     in.seg4 = *reinterpret_cast<const int4*>(s_seg + 16 * I + 4 * kg);
   }
@@ -194,11 +206,13 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   float colp0 = 0.f, colp1 = 0.f, bsum = 0.f;
   const int n0 = Cf::T16 - 1 - w;   // off-diagonal tiles of the first column
   In cur;
+  HeadColumn<T, P> col;
   {
     int I, J;
     bool second;
     Split::tile(w, 0, I, J, second);
-    tile_load<T, Q, P, UNI, Split::NOFF == 0>(cur, I, J, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+    tile_load<T, Q, P, UNI, Split::NOFF == 0>(cur, I, s_dyk, s_acs, s_er, s_seg);
+    head_column_load<T, Q, P>(col, J, s_xk, s_acs, s_dt, s_seg);
   }
 #pragma clang loop unroll(full)
   for (int k = 0; k < Split::NOWN; ++k) {
@@ -213,22 +227,22 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
       bool sn;
       Split::tile(w, k + 1, In_, Jn, sn);
       if (k + 1 >= Split::NOFF)
-        tile_load<T, Q, P, UNI, true>(nxt, In_, Jn, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+        tile_load<T, Q, P, UNI, true>(nxt, In_, s_dyk, s_acs, s_er, s_seg);
       else
-        tile_load<T, Q, P, UNI, false>(nxt, In_, Jn, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg);
+        tile_load<T, Q, P, UNI, false>(nxt, In_, s_dyk, s_acs, s_er, s_seg);
     }
     f32x4_t m = zero4();
 #pragma unroll
-    for (int s = 0; s < In::MK; ++s) m = Mma<T>::mma(cur.ma[s], cur.mb[s], m);
+    for (int s = 0; s < In::MK; ++s) m = Mma<T>::mma(cur.ma[s], col.mb[s], m);
     const int j = 16 * J + r16;
-    const float aj = cur.aj, dtj = cur.dtj;
+    const float aj = col.aj, dtj = col.dtj;
     f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
     if (UNI && !diag) {
       const float ec = Elem<T>::exp(cur.acs_i0 - aj);
 #pragma unroll
       for (int r = 0; r < 4; ++r) e4[r] = cur.rowv[r] * ec;
     } else {
-      const int loj = seg_lo(cur.segj);
+      const int loj = seg_lo(col.segj);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * I + 4 * kg + r;
@@ -316,8 +330,12 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
         colp0 = colp1;
         colp1 = 0.f;
         bsum = 0.f;
+        head_column_load<T, Q, P>(col, Cf::T16 - 1 - w, s_xk, s_acs, s_dt, s_seg);
       }
     }
+    // the diagonal tiles: the first column's, then the second's
+    if (k + 1 == Split::NOFF) head_column_load<T, Q, P>(col, w, s_xk, s_acs, s_dt, s_seg);
+    if (k + 1 == Split::NOFF + 1) head_column_load<T, Q, P>(col, Cf::T16 - 1 - w, s_xk, s_acs, s_dt, s_seg);
     if (PF && k == (Split::NOFF + 1) / 2) b2.load_ds(0);
     if (k + 1 < Split::NOWN) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
