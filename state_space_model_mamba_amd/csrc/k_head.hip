@@ -342,13 +342,14 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   }
 }
 
+// One (batch, head, chunk) work item, logical index lb.
 template <typename T, int Q, int P>
-__global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
+__device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* smem) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
   constexpr int LDP = Cf::LDP, LDSN = Cf::LDSN;
   constexpr int R = Q / WAVE;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  smem += opaque_zero();   // keeps the item's LDS addresses from being hoisted out of the item loop
   T* s_xk = reinterpret_cast<T*>(smem);
   T* s_dyk = s_xk + Q * LDP;
   T* s_dsk = s_dyk + Q * LDP;   // dS rows [p][n] in the I/O dtype
@@ -366,8 +367,6 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   int* s_seg = reinterpret_cast<int*>(s_er + Q);
   float* s_red = reinterpret_cast<float*>(s_seg + Q);
 
-  const int64_t total = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
-  const int64_t lb = xcd_logical_block(blockIdx.x, total);
   const int hh = static_cast<int>(lb % pb.hpg);
   int64_t rest = lb / pb.hpg;
   const int c = static_cast<int>(rest % pb.nc);
@@ -633,17 +632,47 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   }
 }
 
+// Persistent blocks: the blocks on one XCD (block i runs on XCD i % 8) take
+// the logical items of that XCD's contiguous share in order, so the heads of
+// one (group, chunk), which read the same CB tiles, run on one XCD at about
+// the same time.  Every item is computed the same way whichever block takes
+// it.
+template <typename T, int Q, int P>
+__global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int64_t NXCD = 8;
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
+  const int64_t nblk = gridDim.x;
+  const int64_t xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
+  const int64_t nb_x = nblk / NXCD + (xcd < nblk % NXCD ? 1 : 0);   // blocks on this XCD
+  const int64_t q = total / NXCD, r = total % NXCD;
+  const int64_t begin = xcd * q + (xcd < r ? xcd : r), count = q + (xcd < r ? 1 : 0);
+  for (int64_t k = slot; k < count; k += nb_x) {
+    __syncthreads();   // the previous item's LDS reads are done
+    head_item<T, Q, P>(pb, begin + k, smem);
+  }
+}
+
 template <typename T, int Q, int P>
 static hipError_t launch_head_t(const Problem& pb, hipStream_t s) {
   using Cf = HeadCfg<T, Q, P>;
   static bool attr_set = false;
+  static int resident = 0;   // blocks that fit on the device at once
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_head_bwd<T, Q, P>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
     if (e != hipSuccess) return e;
+    int dev = 0, ncu = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_head_bwd<T, Q, P>),
+                                                          Cf::NTHR, Cf::LDS)) != hipSuccess)
+      return e;
+    resident = ncu * (per_cu > 0 ? per_cu : 1);
     attr_set = true;
   }
-  const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
+  const int64_t items = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
+  const int64_t blocks = items < resident ? items : resident;
   hipLaunchKernelGGL((k_head_bwd<T, Q, P>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
   return hipGetLastError();
 }
