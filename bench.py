@@ -41,7 +41,7 @@ def sizes(w, ntg):
         INIT=(S * w.nheads * w.headdim * w.dstate * 4) if w.h0_std > 0 else 0,
         DINIT=S * w.nheads * w.headdim * w.dstate * 4,
         SEQ=w.batch * w.seqlen * 4 if w.nseqs_packed else 0,
-        T=w.batch * w.nheads * nc * w.headdim * w.dstate * 4,      # Hin or dS (fp32)
+        T=w.batch * w.nheads * nc * w.headdim * w.dstate * s,      # Hin or dS (I/O dtype)
         CH=w.batch * w.nheads * nc * w.chunk * 4,                  # one per-chunk fp32 vector
         OFFD=w.batch * w.nheads * nc * ntg * w.chunk * 4,
         SEG=w.batch * nc * w.chunk * 4,
@@ -52,7 +52,7 @@ def sizes(w, ntg):
 
 
 def step_alg_bytes(z):
-    """Compulsory I/O plus one write and one read of the fp32 chunk states and state gradients."""
+    """Compulsory I/O plus one write and one read of the chunk states and state gradients."""
     return 3 * z["X"] + 4 * z["BC"] + 2 * z["DT"] + z["INIT"] + z["DINIT"] + z["SEQ"] + 4 * z["T"]
 
 

@@ -123,9 +123,10 @@ const char* ssd_status_string(int status);
  * (tests, profiling).  Offsets are in bytes from the workspace start.
  *   SSD_WS_ACS    float32 (batch, nheads, nchunks, Q): in-chunk inclusive cumsum of
  *                 dt*A, restarted at chunk and sequence starts
- *   SSD_WS_HIN    float32 (batch, nheads, nchunks, P, N): state entering each chunk
- *   SSD_WS_DSTATE float32 (batch, nheads, nchunks, P, N): gradient w.r.t. the state at
+ *   SSD_WS_HIN    I/O dtype (batch, nheads, nchunks, P, N): state entering each chunk
+ *   SSD_WS_DSTATE I/O dtype (batch, nheads, nchunks, P, N): gradient w.r.t. the state at
  *                 the end of each chunk, through later positions only
+ *                 (both are carried in fp32 and rounded once when stored)
  * Returns SSD_OK and fills offset/bytes, or a negative status.
  */
 enum { SSD_WS_ACS = 0, SSD_WS_HIN = 1, SSD_WS_DSTATE = 2 };

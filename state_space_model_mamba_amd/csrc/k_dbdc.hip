@@ -204,26 +204,40 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     st_cm.store(s_c, LDK);
   }
 
-  // entering state of segment m of head h (nullptr: zero)
-  auto e_src = [&](int h, int m) -> const float* {
+  // entering state of segment m of head h: Hin (I/O dtype) for a segment
+  // that continues the chunk's sequence, h0[s] (fp32) for one that starts
+  // sequence s, none (zero) when h0 is not given
+  struct ERows {
+    const void* p;
+    bool h0;
+  };
+  auto e_src = [&](int h, int m) -> ERows {
     const int64_t bhc = (static_cast<int64_t>(k.b) * pb.H + h) * pb.nc + k.c;
     const int rank = seg_rank(s_seg[s_segstart[m]]);
-    if (rank == 0) return pb.hin + bhc * P * pb.N;
-    if (!pb.h0) return nullptr;
+    if (rank == 0) return {static_cast<const T*>(pb.hin) + bhc * P * pb.N, false};
+    if (!pb.h0) return {nullptr, true};
     const int s = clamp_seq(k.seqbase + rank - 1, pb.nseqs);
-    return pb.h0 + (static_cast<int64_t>(s) * pb.H + h) * P * pb.N;
+    return {pb.h0 + (static_cast<int64_t>(s) * pb.H + h) * P * pb.N, true};
   };
-  auto state_row = [&](const float* base) {
-    return [=, &pb](int p) -> const float* { return base + static_cast<int64_t>(p) * pb.N + k.n0; };
+  auto state_row = [&](const auto* base) {
+    return [=, &pb](int p) { return base + static_cast<int64_t>(p) * pb.N + k.n0; };
   };
-  auto zero_row = [](int) -> const float* { return nullptr; };
+  auto zero_row = [](int) -> const T* { return nullptr; };
+  auto load_e = [&](RowStage<T, P, NTG, NTHR>& st, ERows e) {
+    if (!e.p)
+      st.load(zero_row);
+    else if (!e.h0)
+      st.load(state_row(static_cast<const T*>(e.p)));
+    else
+      st.load_from_f32(state_row(static_cast<const float*>(e.p)));
+  };
   // the last segment's <dS, E> feeds endd unless it starts a sequence without a
   // given initial state (E = 0)
   const bool single = k.nseg == 1;
 
   // next head's rows: dy, segment 0's E, and (single segment) dS
   RowStage<T, Q, P, NTHR> st_dy;
-  RowStage<float, P, NTG, NTHR> st_e, st_s;
+  RowStage<T, P, NTG, NTHR> st_e, st_s;
   float acs_n = 0.f;
   auto load_head = [&](int hh) {
     const int h = k.g * pb.hpg + hh;
@@ -232,14 +246,13 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
       const int t = k.c * Q + i;
       return t < pb.L ? dyg + ((static_cast<int64_t>(k.b) * pb.L + t) * pb.H + h) * P : nullptr;
     });
-    const float* e0 = e_src(h, 0);
-    if (e0) st_e.load(state_row(e0)); else st_e.load(zero_row);
-    if (single) st_s.load(state_row(pb.dstate + bhc * P * pb.N));
+    load_e(st_e, e_src(h, 0));
+    if (single) st_s.load(state_row(static_cast<const T*>(pb.dstate) + bhc * P * pb.N));
     if (tid < Q) acs_n = pb.acs[bhc * Q + tid];
   };
   // prefetch the next head only where its registers fit, and only for a
   // single-segment chunk (the segment loop below reuses the same registers)
-  constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + 2 * RowStage<float, P, NTG, NTHR>::IT <= 16;
+  constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + 2 * RowStage<T, P, NTG, NTHR>::IT <= 16;
   const bool pf = PF && single;
   if (pf) load_head(0);
 
@@ -250,12 +263,12 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     if (!pf) load_head(hh);
     __syncthreads();
     st_dy.store(s_rows, LDP);
-    st_e.template store_rows_f32<T>(s_e, LDE);
-    if (single && e_src(h, 0)) {
+    st_e.store(s_e, LDE);
+    if (single && e_src(h, 0).p) {
 #pragma unroll
       for (int kk = 0; kk < st_e.IT; ++kk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) endp += vget<float>(st_s.buf[kk], e) * vget<float>(st_e.buf[kk], e);
+        for (int e = 0; e < st_e.VEC; ++e) endp += vget<T>(st_s.buf[kk], e) * vget<T>(st_e.buf[kk], e);
     }
     if (tid < Q) s_v[tid] = Elem<T>::exp(acs_n);
     __syncthreads();
@@ -268,22 +281,22 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
       for (int r = 0; r < 4; ++r) offp[a][r] = 0.f;
     for (int m = 0; m < k.nseg; ++m) {
       const int lo = s_segstart[m], hi = s_segstart[m + 1];
-      const float* esrc = e_src(h, m);
+      const ERows esrc = e_src(h, m);
       if (m > 0) {
         // further segments (a sequence starts inside the chunk): stage their E here
         __syncthreads();
-        if (esrc) st_e.load(state_row(esrc)); else st_e.load(zero_row);
-        if (hi == Q && esrc) {
-          st_s.load(state_row(pb.dstate + bhc * P * pb.N));
+        load_e(st_e, esrc);
+        if (hi == Q && esrc.p) {
+          st_s.load(state_row(static_cast<const T*>(pb.dstate) + bhc * P * pb.N));
 #pragma unroll
           for (int kk = 0; kk < st_e.IT; ++kk)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) endp += vget<float>(st_s.buf[kk], e) * vget<float>(st_e.buf[kk], e);
+            for (int e = 0; e < st_e.VEC; ++e) endp += vget<T>(st_s.buf[kk], e) * vget<T>(st_e.buf[kk], e);
         }
-        st_e.template store_rows_f32<T>(s_e, LDE);
+        st_e.store(s_e, LDE);
         __syncthreads();
       }
-      if (!esrc) continue;
+      if (!esrc.p) continue;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int I = own[a];
@@ -372,7 +385,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
 
   // next head's rows: x, dS, and this thread's Acs / dt
   RowStage<T, Q, P, NTHR> st_x;
-  RowStage<float, P, NTG, NTHR> st_s;
+  RowStage<T, P, NTG, NTHR> st_s;
   float acs_n = 0.f, dt_n = 0.f, acs_end_n = 0.f;
   auto load_head = [&](int hh) {
     const int h = k.g * pb.hpg + hh;
@@ -381,15 +394,15 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
       const int t = k.c * Q + i;
       return t < pb.L ? xg + ((static_cast<int64_t>(k.b) * pb.L + t) * pb.H + h) * P : nullptr;
     });
-    const float* ds = pb.dstate + bhc * P * pb.N;
-    st_s.load([=, &pb](int p) -> const float* { return ds + static_cast<int64_t>(p) * pb.N + k.n0; });
+    const T* ds = static_cast<const T*>(pb.dstate) + bhc * P * pb.N;
+    st_s.load([=, &pb](int p) -> const T* { return ds + static_cast<int64_t>(p) * pb.N + k.n0; });
     if (tid < Q) {
       acs_n = pb.acs[bhc * Q + tid];
       dt_n = pb.dtc[bhc * Q + tid];
     }
     acs_end_n = pb.acs[bhc * Q + Q - 1];
   };
-  constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + RowStage<float, P, NTG, NTHR>::IT <= 16;
+  constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + RowStage<T, P, NTG, NTHR>::IT <= 16;
   __syncthreads();   // the slab phase is done with the LDS the head phase reuses
   if (PF) load_head(0);
 
@@ -397,7 +410,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
     if (!PF) load_head(hh);
     __syncthreads();
     st_x.store(s_rows, LDP);
-    st_s.template store_rows_f32<T>(s_e, LDE);
+    st_s.store(s_e, LDE);
     if (tid < Q) s_v[tid] = (tid >= k.lolast) ? Elem<T>::exp(acs_end_n - acs_n) * dt_n : 0.f;
     __syncthreads();
     if (PF && hh + 1 < pb.hpg) load_head(hh + 1);

@@ -52,7 +52,7 @@ struct HeadCfg {
   static constexpr int LDP = P + VEC;
   static constexpr int NOWN = Split::NOWN;
   static constexpr int CBD = NOWN < 2 ? NOWN : 2;   // CB tiles requested ahead of their use
-  static constexpr int DSV = (P * NBLK / 4 + NTHR - 1) / NTHR;   // fp32 dS vectors per thread per round
+  static constexpr int DSV = (P * NBLK / VEC + NTHR - 1) / NTHR;   // 16-byte dS vectors per thread per round
   static constexpr int NKB = NBLK / Mma<T>::KSTEP;      // B fragments per owned column per round
   static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(P) * LDSN) * sizeof(T);  // x, dy, dS rows
   // da shares: [column tile J][position]
@@ -72,7 +72,7 @@ struct HeadCfg {
 // in the middle of the tile sequence, into registers the CB tiles already
 // used have freed (every tile sequence reaches that point).
 // Operands of phase B2 (Z^T = dS B^T) for one round of NBLK dstate columns:
-// dS (P x NBLK fp32, one 16-byte piece per thread and slot) and this lane's B
+// dS (P x NBLK in the I/O dtype, one 16-byte piece per thread and slot) and this lane's B
 // fragments of the two owned column tiles (bf16: one 16-byte piece per k-step).
 template <typename T, int Q, int P>
 struct B2Operands {
@@ -80,17 +80,18 @@ struct B2Operands {
   static constexpr int KS = Mma<T>::KSTEP, KW = Mma<T>::KW;
   uint4 dsr[Cf::DSV];
   typename Mma<T>::frag bf[2][KW == 8 ? Cf::NKB : 1];
-  const float* ds_base;   // dS of this (b, h, c): [P][N]
+  const T* ds_base;       // dS of this (b, h, c): [P][N]
   const T* brow[2];       // this lane's B row of each owned column tile, at k = 8 (lane / 16) (nullptr past L)
   int N;
   __device__ __forceinline__ int cols(int nb) const { return N - nb * Cf::NBLK < Cf::NBLK ? N - nb * Cf::NBLK : Cf::NBLK; }
   __device__ __forceinline__ void load_ds(int nb) {
-    const int vr = cols(nb) / 4, nv = P * vr;
+    constexpr int VEC = Cf::VEC;
+    const int vr = cols(nb) / VEC, nv = P * vr;
 #pragma unroll
     for (int q = 0; q < Cf::DSV; ++q) {
       const int v = static_cast<int>(threadIdx.x) + q * Cf::NTHR;
       dsr[q] = zero_u4();
-      if (v < nv) dsr[q] = ld_global16(ds_base + (v / vr) * N + nb * Cf::NBLK + 4 * (v % vr));
+      if (v < nv) dsr[q] = ld_global16(ds_base + (v / vr) * N + nb * Cf::NBLK + VEC * (v % vr));
     }
   }
   __device__ __forceinline__ void load_b(int nb) {
@@ -105,14 +106,14 @@ struct B2Operands {
         }
     }
   }
-  // dS round nb -> LDS rows [p][n] in the I/O dtype
+  // dS round nb -> LDS rows [p][n]
   __device__ __forceinline__ void store_ds(int nb, T* s_dsk) const {
-    const int vr = cols(nb) / 4, nv = P * vr;
+    constexpr int VEC = Cf::VEC;
+    const int vr = cols(nb) / VEC, nv = P * vr;
 #pragma unroll
     for (int q = 0; q < Cf::DSV; ++q) {
       const int v = static_cast<int>(threadIdx.x) + q * Cf::NTHR;
-      if (v < nv)
-        store4f<T>(s_dsk + (v / vr) * Cf::LDSN + 4 * (v % vr), __builtin_bit_cast(f32x4_t, dsr[q]));
+      if (v < nv) *reinterpret_cast<uint4*>(s_dsk + (v / vr) * Cf::LDSN + VEC * (v % vr)) = dsr[q];
     }
   }
 };
@@ -463,7 +464,7 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
 #pragma unroll
   for (int a = 0; a < Cf::NCOL; ++a) ddti[a] = 0.f;
   B2Operands<T, Q, P> b2;
-  b2.ds_base = pb.dstate + bhc * P * pb.N;
+  b2.ds_base = static_cast<const T*>(pb.dstate) + bhc * P * pb.N;
   b2.N = pb.N;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {

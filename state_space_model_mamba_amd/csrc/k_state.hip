@@ -180,7 +180,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int p = pt * 16 + 4 * kg + r;
-          pb.hin[(bhc * P + p) * pb.N + n] = st[k][r];
+          static_cast<T*>(pb.hin)[(bhc * P + p) * pb.N + n] = Elem<T>::from_f(st[k][r]);
           if (nstart == 0) {
             st[k][r] = decay * st[k][r] + S[r];
           } else {
@@ -252,7 +252,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
 
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pb.dstate[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = dout[k][r];
+          static_cast<T*>(pb.dstate)[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = Elem<T>::from_f(dout[k][r]);
         if (nstart == 0) {
           f32x4_t R = zero4();
 #pragma unroll

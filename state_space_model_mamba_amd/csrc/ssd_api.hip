@@ -59,9 +59,9 @@ Layout make_layout(const ssd_shape* s) {
   L.cinfo = take(B * nc * ssd::CINFO * 4);
   L.acs = take(B * H * nc * Q * 4);
   L.dtc = take(B * H * nc * Q * 4);
-  L.hin = take(B * H * nc * P * N * 4);
-  L.dstate = take(B * H * nc * P * N * 4);
   const size_t es = is_bf16(s) ? 2 : 4;
+  L.hin = take(B * H * nc * P * N * es);
+  L.dstate = take(B * H * nc * P * N * es);
   L.dcb = take(B * s->ngroups * nc * Q * Q * es);
   L.dcbt = take(B * s->ngroups * nc * Q * Q * es);
   L.cbt = take(B * s->ngroups * nc * (Q * (Q + 16) / 2) * 4);
@@ -96,8 +96,8 @@ extern "C" int ssd_bwd_workspace_region(const ssd_shape* shape, int region, size
                N = shape->dstate, nc = L.nc;
   switch (region) {
     case SSD_WS_ACS: *offset = L.acs; *bytes = B * H * nc * Q * 4; return SSD_OK;
-    case SSD_WS_HIN: *offset = L.hin; *bytes = B * H * nc * P * N * 4; return SSD_OK;
-    case SSD_WS_DSTATE: *offset = L.dstate; *bytes = B * H * nc * P * N * 4; return SSD_OK;
+    case SSD_WS_HIN: *offset = L.hin; *bytes = B * H * nc * P * N * (is_bf16(shape) ? 2 : 4); return SSD_OK;
+    case SSD_WS_DSTATE: *offset = L.dstate; *bytes = B * H * nc * P * N * (is_bf16(shape) ? 2 : 4); return SSD_OK;
     default: return SSD_ERR_INVALID_ARG;
   }
 }
@@ -166,8 +166,8 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
   pb.cinfo = reinterpret_cast<int32_t*>(ws + L.cinfo);
   pb.acs = reinterpret_cast<float*>(ws + L.acs);
   pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
-  pb.hin = reinterpret_cast<float*>(ws + L.hin);
-  pb.dstate = reinterpret_cast<float*>(ws + L.dstate);
+  pb.hin = ws + L.hin;
+  pb.dstate = ws + L.dstate;
   pb.dcb = ws + L.dcb;
   pb.dcbt = ws + L.dcbt;
   pb.cbt = reinterpret_cast<float*>(ws + L.cbt);

@@ -47,8 +47,8 @@ struct Problem {
   int32_t* cinfo;    // (B, nc, CINFO)
   float* acs;        // (B, H, nc, Q)
   float* dtc;        // (B, H, nc, Q)
-  float* hin;        // (B, H, nc, P, N)
-  float* dstate;     // (B, H, nc, P, N)
+  void* hin;         // (B, H, nc, P, N), I/O dtype
+  void* dstate;      // (B, H, nc, P, N), I/O dtype
   void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB
   void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose
   float* cbt;        // (B, G, nc, Q(Q+16)/512 tiles, 256): C B^T causal tiles, fp32, in the

@@ -76,6 +76,26 @@ struct RowStage {
       }
     }
   }
+  // The same rows read from fp32 memory and rounded to TIN (to nearest even):
+  // each 16-byte piece takes 16 / sizeof(TIN) floats.  The conversion waits
+  // for the loads, so this is for rarely taken paths.
+  template <typename RowPtr>
+  __device__ __forceinline__ void load_from_f32(RowPtr rowptr) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      buf[k] = zero_u4();
+      if (NV % NTHR == 0 || v < NV) {
+        const float* p = rowptr(v / CV);
+        if (p) {
+          TIN o[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = Elem<TIN>::from_f(p[(v % CV) * VEC + e]);
+          buf[k] = *reinterpret_cast<const uint4*>(o);
+        }
+      }
+    }
+  }
   // row-major into LDS (same element type): lds[r * ld + c]
   __device__ __forceinline__ void store(TIN* lds, int ld) const {
 #pragma unroll

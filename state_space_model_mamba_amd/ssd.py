@@ -193,15 +193,15 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:
-    """A float32 view of one workspace region of a finished call (Acs, Hin or dS)."""
+    """A view of one workspace region of a finished call: Acs (float32), Hin or dS (I/O dtype)."""
     shape = result["shape"]
     off, nb = workspace_region(shape, region)
     ws = result["workspace"]
     nc = -(-shape.seqlen // shape.chunk_size)
-    flat = ws[off:off + nb].view(torch.float32)
     if region == SSD_WS_ACS:
-        return flat.view(shape.batch, shape.nheads, nc, shape.chunk_size)
-    return flat.view(shape.batch, shape.nheads, nc, shape.headdim, shape.dstate)
+        return ws[off:off + nb].view(torch.float32).view(shape.batch, shape.nheads, nc, shape.chunk_size)
+    dt = torch.bfloat16 if shape.io_dtype == SSD_IO_BF16 else torch.float32
+    return ws[off:off + nb].view(dt).view(shape.batch, shape.nheads, nc, shape.headdim, shape.dstate)
 
 
 def stage_names() -> list[str]:

@@ -41,7 +41,7 @@ def test_workspace_size_and_regions():
     s = shape()
     n = ssd.workspace_size(s)
     nc = 8
-    state = 1 * 128 * nc * 64 * 128 * 4
+    state = 1 * 128 * nc * 64 * 128 * 2   # Hin and dS are held in the I/O dtype (bf16 here)
     assert n >= 2 * state
     off_h, nb_h = ssd.workspace_region(s, ssd.SSD_WS_HIN)
     off_d, nb_d = ssd.workspace_region(s, ssd.SSD_WS_DSTATE)
@@ -52,6 +52,9 @@ def test_workspace_size_and_regions():
     assert len({off_h, off_d, off_a}) == 3
     # ragged tail: one more chunk
     assert ssd.workspace_size(shape(seqlen=2049)) > n
+    # fp32 I/O (chunk 128, 16 chunks): fp32 states
+    f = shape(io_dtype=ssd.SSD_IO_F32, chunk_size=128)
+    assert ssd.workspace_region(f, ssd.SSD_WS_HIN)[1] == 1 * 128 * 16 * 64 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,code", [

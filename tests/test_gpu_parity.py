@@ -63,6 +63,23 @@ def test_tiny_fp32_workload_and_chunk_states():
     assert e_h <= TOL["f32"] and e_d <= TOL["f32"]
 
 
+def test_bf16_chunk_states_held_in_bf16():
+    # Hin and dS live in the workspace in the I/O dtype; they must still match
+    # the oracle's chunk states within the bf16 bound
+    w = Workload("bf16_states", batch=1, seqlen=512, nheads=8, headdim=64, ngroups=2, dstate=64, chunk=128,
+                 dtype="bf16", seed=5)
+    inputs = make_inputs(w)
+    res, got, ref = check(inputs, w.chunk, TOL["bf16"], "bf16 chunk states", oracle_kw=dict(chunk=w.chunk))
+    hin = ssd.workspace_view(res, ssd.SSD_WS_HIN)
+    dst = ssd.workspace_view(res, ssd.SSD_WS_DSTATE)
+    assert hin.dtype == torch.bfloat16 and dst.dtype == torch.bfloat16
+    from tests.gpu_helpers import normwise_err
+    e_h = normwise_err(hin.double().cpu().numpy().transpose(0, 2, 1, 3, 4), ref["chunk_states"])
+    e_d = normwise_err(dst.double().cpu().numpy().transpose(0, 2, 1, 3, 4), ref["chunk_dout"])
+    print(f"bf16 chunk states err {e_h:.2e}, state grads err {e_d:.2e}", flush=True)
+    assert e_h <= TOL["bf16"] and e_d <= TOL["bf16"]
+
+
 def test_fp32_packed_ragged_tail_chunk_aligned_start():
     # row 0: starts at 0, 64 (chunk aligned), 104, 105 (length-1 sequence); row 1: one sequence
     w = small("f32_packed", batch=2, seqlen=200, nheads=4, ngroups=2, headdim=16, dstate=32, chunk=64)
