@@ -166,8 +166,6 @@ __device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, con
         dcb_column_load<T, Q, P>(col, Cf::T16 - 1 - wz, xk, acs, dtv, lov);
       }
     }
-    // keep the scheduler from hoisting every tile's fragment loads at once
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
