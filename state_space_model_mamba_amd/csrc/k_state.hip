@@ -111,10 +111,19 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
     if (v < Cf::XV) {
       const int j = v / (P / VEC), pv = v % (P / VEC);
       const float sc = s_scale[j];
-      T o[VEC];
+      uint4 o;
+      if constexpr (sizeof(T) == 2) {
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = Elem<T>::from_f(vget<T>(xr[k], e) * sc);
-      *reinterpret_cast<uint4*>(s_x + Cf::XTile::at(j, pv * VEC)) = *reinterpret_cast<const uint4*>(o);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(vget<T>(xr[k], 2 * e) * sc, vget<T>(xr[k], 2 * e + 1) * sc);
+        o = uint4{w[0], w[1], w[2], w[3]};
+      } else {
+        f32x4_t f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = vget<T>(xr[k], e) * sc;
+        o = __builtin_bit_cast(uint4, f);
+      }
+      *reinterpret_cast<uint4*>(s_x + Cf::XTile::at(j, pv * VEC)) = o;
     }
   }
 #pragma unroll

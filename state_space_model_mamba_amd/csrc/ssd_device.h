@@ -38,6 +38,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, low
+// half first: one v_cvt_pk_bf16_f32 (a 4-wide vector conversion compiles to
+// single conversions plus permutes).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_f32(v); }
@@ -92,8 +101,8 @@ template <> struct Mma<bf16_t> {
   //   X: the tile's own 4 values per lane.
   typedef s16x4_t rfrag;
   static __device__ __forceinline__ rfrag rfrag_from_acc(f32x4_t x) {
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(rfrag, __builtin_convertvector(x, bf16x4_t));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(rfrag, u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
   }
   // 4 values at p, p + stride, p + 2 stride, p + 3 stride
   static __device__ __forceinline__ rfrag rfrag_load(const bf16_t* p, int stride) {

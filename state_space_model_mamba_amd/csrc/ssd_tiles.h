@@ -42,8 +42,7 @@ template <> __device__ __forceinline__ f32x4_t load4f<float>(const float* p) {
 }
 template <typename T> __device__ __forceinline__ void store4f(T* p, f32x4_t v);
 template <> __device__ __forceinline__ void store4f<bf16_t>(bf16_t* p, f32x4_t v) {
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4_t));
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 template <> __device__ __forceinline__ void store4f<float>(float* p, f32x4_t v) {
   *reinterpret_cast<f32x4_t*>(p) = v;
