@@ -343,9 +343,35 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   }
 }
 
-// One (batch, head, chunk) work item, logical index lb.
+// x and dy rows of item lb -> registers (rows past L read as zero).
 template <typename T, int Q, int P>
-__device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* smem) {
+__device__ __forceinline__ void load_item_rows(const Problem& pb, int64_t lb,
+                                               RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_x,
+                                               RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy) {
+  const int hh = static_cast<int>(lb % pb.hpg);
+  int64_t rest = lb / pb.hpg;
+  const int c = static_cast<int>(rest % pb.nc);
+  rest /= pb.nc;
+  const int g = static_cast<int>(rest % pb.G), b = static_cast<int>(rest / pb.G);
+  const int h = g * pb.hpg + hh;
+  auto row = [&](const void* base) {
+    return [=, &pb](int i) -> const T* {
+      const int t = c * Q + i;
+      return t < pb.L ? static_cast<const T*>(base) + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
+    };
+  };
+  st_x.load(row(pb.x));
+  st_dy.load(row(pb.dy));
+}
+
+// One (batch, head, chunk) work item, logical index lb, whose x and dy rows
+// are already requested into st_x / st_dy.  At the start of phase D (those
+// rows are in LDS by then, and few registers are live) it requests item
+// lb_next's rows into the same registers.
+template <typename T, int Q, int P>
+__device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* smem,
+                                          RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_x,
+                                          RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy, int64_t lb_next) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
   constexpr int LDP = Cf::LDP, LDSN = Cf::LDSN;
@@ -378,8 +404,6 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
   const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-  const T* xg = static_cast<const T*>(pb.x);
-  const T* dyg = static_cast<const T*>(pb.dy);
   const T* Bg = static_cast<const T*>(pb.Bm);
   const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
 
@@ -401,25 +425,15 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   if (tid < WAVE)
     for (int nt = 0; nt < pb.ntg; ++nt) endd += pb.endd[bhc * pb.ntg + nt];
 
-  // Row sources of the global tiles this block stages (nullptr = zero row).
-  auto head_row = [&](const T* base) {
-    return [=](int i) -> const T* {
-      const int t = c * Q + i;
-      return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
-    };
-  };
-
   // ---- phase A: the CB tiles of this wave (formed once per group by the
-  // dCB kernel, same split) and the x, dy rows, all requested up front
+  // dCB kernel, same split); the x, dy rows were requested by the previous
+  // item (or before the item loop)
   f32x4_t cb[Cf::NOWN];   // the first CBD now, the others during phase B
   const float* cbsrc = pb.cbt + (bgc * W + w) * Cf::NOWN * 256 + l * 4;
   {
 #pragma unroll
     for (int k = 0; k < Cf::CBD; ++k) cb[k] = *reinterpret_cast<const f32x4_t*>(cbsrc + k * 256);
   }
-  RowStage<T, Q, P, NTHR> st_x, st_dy;
-  st_x.load(head_row(xg));
-  st_dy.load(head_row(dyg));
 
   // A chunk without sequence starts after position 0 has one segment, and its
   // Acs never increases; there exp(Acs_i - Acs_j) of an off-diagonal tile is
@@ -552,6 +566,8 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   }
   __syncthreads();
 
+  load_item_rows<T, Q, P>(pb, lb_next, st_x, st_dy);
+
   // ---- phase D: da and its consumers
   if (tid < Q) {
     const int k = tid, K = k / 16;
@@ -648,9 +664,14 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const int64_t nb_x = nblk / NXCD + (xcd < nblk % NXCD ? 1 : 0);   // blocks on this XCD
   const int64_t q = total / NXCD, r = total % NXCD;
   const int64_t begin = xcd * q + (xcd < r ? xcd : r), count = q + (xcd < r ? 1 : 0);
+  RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR> st_x, st_dy;
+  if (slot < count) load_item_rows<T, Q, P>(pb, begin + slot, st_x, st_dy);
   for (int64_t k = slot; k < count; k += nb_x) {
     __syncthreads();   // the previous item's LDS reads are done
-    head_item<T, Q, P>(pb, begin + k, smem);
+    // (after the last item the rows requested are its own again: unused, but
+    // keeps the request unconditional)
+    const int64_t next = k + nb_x < count ? begin + k + nb_x : begin + k;
+    head_item<T, Q, P>(pb, begin + k, smem, st_x, st_dy, next);
   }
 }
 
