@@ -115,6 +115,28 @@ int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
             void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
             float* d_initial_states, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The forward of the same layer (the kernels chunk_cumsum, chunk_state, state
+ * passing and chunk_scan named on the page "Deterministic bwd kernel for
+ * mamba2", whose backward twins are above), for callers that pair it with
+ * ssd_bwd (an autograd function, a training step):
+ *   y_t = h_t C_t + D_h x_t,  h_t = exp(dt_t A_h) h_{t-1} + dt_t x_t (outer) B_t
+ * with h entering each sequence as its initial state (zeros when
+ * initial_states is NULL).  Output y (B, L, H, P) in the I/O dtype.
+ * final_states (nseqs, H, P, N) fp32, optional: the state after each
+ * sequence's last position (sequences numbered as for ssd_bwd).
+ * Required: x, dt, A, B, C, y, workspace.  Optional: D (zeros),
+ * initial_states, seq_idx, final_states.  nseqs must be right whenever
+ * initial_states or final_states is given (same clamping as ssd_bwd).
+ * The workspace is sized by ssd_bwd_workspace_size; its contents on entry do
+ * not matter.  Asynchronous on `stream`; deterministic like ssd_bwd.
+ * Returns SSD_OK or a negative status.
+ */
+int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+            const void* B, const void* C, const float* D, const float* initial_states,
+            const int32_t* seq_idx, void* y, float* final_states,
+            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);
 

@@ -12,7 +12,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, total;
+  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, seqstart, total;
   int nc, ntg;
 };
 
@@ -39,7 +39,8 @@ int check_shape(const ssd_shape* s) {
   const size_t lim = 160 * 1024;
   if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
       ssd::dcb_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
-      ssd::dbdc_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim)
+      ssd::dbdc_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim ||
+      ssd::fwd_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim)
     return SSD_ERR_UNSUPPORTED_SHAPE;
   return SSD_OK;
 }
@@ -69,6 +70,7 @@ Layout make_layout(const ssd_shape* s) {
   L.endd = take(B * H * nc * ntg * 4);
   L.slot_dA = take(B * nc * H * 4);
   L.slot_dD = take(B * nc * H * 4);
+  L.seqstart = take((s->nseqs > 0 ? s->nseqs : 1) * 4);
   L.total = off;
   L.nc = static_cast<int>(nc);
   L.ntg = static_cast<int>(ntg);
@@ -121,6 +123,37 @@ namespace {
 const char* const kStageNames[] = {"prep", "state_fwd", "state_bwd", "dcb", "dbdc", "head_bwd", "reduce"};
 constexpr int kStages = 7;
 
+// Shape and workspace fields of the kernels' problem descriptor.
+void fill_problem(const ssd_shape* shape, const Layout& L, void* workspace, ssd::Problem& pb) {
+  memset(&pb, 0, sizeof(pb));
+  pb.B = static_cast<int>(shape->batch);
+  pb.L = static_cast<int>(shape->seqlen);
+  pb.H = static_cast<int>(shape->nheads);
+  pb.P = static_cast<int>(shape->headdim);
+  pb.G = static_cast<int>(shape->ngroups);
+  pb.N = static_cast<int>(shape->dstate);
+  pb.Q = static_cast<int>(shape->chunk_size);
+  pb.nc = L.nc;
+  pb.hpg = pb.H / pb.G;
+  pb.nseqs = shape->nseqs > 0 ? static_cast<int>(shape->nseqs) : 1;
+  pb.ntg = L.ntg;
+  char* ws = static_cast<char*>(workspace);
+  pb.segpos = reinterpret_cast<int32_t*>(ws + L.segpos);
+  pb.cinfo = reinterpret_cast<int32_t*>(ws + L.cinfo);
+  pb.acs = reinterpret_cast<float*>(ws + L.acs);
+  pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
+  pb.hin = ws + L.hin;
+  pb.dstate = ws + L.dstate;
+  pb.dcb = ws + L.dcb;
+  pb.dcbt = ws + L.dcbt;
+  pb.cbt = reinterpret_cast<float*>(ws + L.cbt);
+  pb.offd = reinterpret_cast<float*>(ws + L.offd);
+  pb.endd = reinterpret_cast<float*>(ws + L.endd);
+  pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
+  pb.slot_dD = reinterpret_cast<float*>(ws + L.slot_dD);
+  pb.seqstart = reinterpret_cast<int32_t*>(ws + L.seqstart);
+}
+
 int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
             const void* C, const float* D, const void* dy, const float* initial_states,
             const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
@@ -145,36 +178,11 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
   if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
 
   ssd::Problem pb;
-  memset(&pb, 0, sizeof(pb));
-  pb.B = static_cast<int>(shape->batch);
-  pb.L = static_cast<int>(shape->seqlen);
-  pb.H = static_cast<int>(shape->nheads);
-  pb.P = static_cast<int>(shape->headdim);
-  pb.G = static_cast<int>(shape->ngroups);
-  pb.N = static_cast<int>(shape->dstate);
-  pb.Q = static_cast<int>(shape->chunk_size);
-  pb.nc = L.nc;
-  pb.hpg = pb.H / pb.G;
-  pb.nseqs = shape->nseqs > 0 ? static_cast<int>(shape->nseqs) : 1;
-  pb.ntg = L.ntg;
+  fill_problem(shape, L, workspace, pb);
   pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D; pb.dy = dy;
   pb.h0 = initial_states; pb.seq_idx = seq_idx;
   pb.dx = dx; pb.ddt = ddt; pb.dA = dA; pb.dB = dB; pb.dC = dC; pb.dD = dD;
   pb.dinit = d_initial_states;
-  char* ws = static_cast<char*>(workspace);
-  pb.segpos = reinterpret_cast<int32_t*>(ws + L.segpos);
-  pb.cinfo = reinterpret_cast<int32_t*>(ws + L.cinfo);
-  pb.acs = reinterpret_cast<float*>(ws + L.acs);
-  pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
-  pb.hin = ws + L.hin;
-  pb.dstate = ws + L.dstate;
-  pb.dcb = ws + L.dcb;
-  pb.dcbt = ws + L.dcbt;
-  pb.cbt = reinterpret_cast<float*>(ws + L.cbt);
-  pb.offd = reinterpret_cast<float*>(ws + L.offd);
-  pb.endd = reinterpret_cast<float*>(ws + L.endd);
-  pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
-  pb.slot_dD = reinterpret_cast<float*>(ws + L.slot_dD);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = is_bf16(shape);
@@ -212,6 +220,33 @@ extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const flo
   if (!events) return SSD_ERR_INVALID_ARG;
   return run_bwd(shape, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
                  d_initial_states, workspace, workspace_bytes, stream, events);
+}
+
+extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
+                       void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!x || !dt || !A || !B || !C || !y || !workspace) return SSD_ERR_INVALID_ARG;
+  if (!seq_idx && (initial_states || final_states) && shape->nseqs != shape->batch) return SSD_ERR_INVALID_ARG;
+  if ((initial_states || final_states) && shape->nseqs < 1) return SSD_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
+  const Layout L = make_layout(shape);
+  if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+  ssd::Problem pb;
+  fill_problem(shape, L, workspace, pb);
+  pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D;
+  pb.h0 = initial_states; pb.seq_idx = seq_idx;
+  pb.y = y; pb.final = final_states;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = is_bf16(shape);
+  if (ssd::launch_prep(pb, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  if (final_states && ssd::launch_seqstart(pb, s) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_fwd_out(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
 }
 
 extern "C" int ssd_bwd_stage_count(void) { return kStages; }

@@ -42,6 +42,9 @@ struct Problem {
   void* dC;
   float* dD;
   float* dinit;
+  // forward outputs
+  void* y;           // (B, L, H, P), I/O dtype
+  float* final;      // (nseqs, H, P, N) fp32, nullable
   // workspace
   int32_t* segpos;   // (B, nc, Q)
   int32_t* cinfo;    // (B, nc, CINFO)
@@ -57,6 +60,7 @@ struct Problem {
   float* endd;       // (B, H, nc, ntg)
   float* slot_dA;    // (B, nc, H)
   float* slot_dD;    // (B, nc, H)
+  int32_t* seqstart; // (nseqs): b * L + t of each sequence's first position (forward)
 };
 
 // Launchers (defined next to their kernels).  Return hipSuccess or the
@@ -68,6 +72,10 @@ hipError_t launch_dcb(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_dbdc(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_head_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_reduce(const Problem& pb, hipStream_t s);
+// forward: sequence start table, then C B^T tiles, y and (if requested) the
+// sequences' final states
+hipError_t launch_seqstart(const Problem& pb, hipStream_t s);
+hipError_t launch_fwd_out(const Problem& pb, bool io_bf16, hipStream_t s);
 
 // The (chunk_size, headdim) pairs compiled for each io dtype.  bf16 needs
 // headdim % 32 == 0 (one MFMA k-step over P); fp32 stops at chunk 128 so that
@@ -81,5 +89,6 @@ int group_ntile(int N, bool io_bf16);
 size_t dcb_lds_bytes(int Q, int P, bool io_bf16);
 size_t dbdc_lds_bytes(int Q, int P, int NTG, bool io_bf16);
 size_t head_lds_bytes(int Q, int P, bool io_bf16);
+size_t fwd_lds_bytes(int Q, int P, bool io_bf16);
 
 }  // namespace ssd

@@ -21,7 +21,7 @@ SSD_IO_F32 = 1
 SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
-            "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name")
+            "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd")
 
 
 class SsdShape(ctypes.Structure):
@@ -63,6 +63,8 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp]
     lib.ssd_bwd_profiled.restype = ctypes.c_int
     lib.ssd_bwd_profiled.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp, ctypes.POINTER(vp)]
+    lib.ssd_fwd.restype = ctypes.c_int
+    lib.ssd_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
     lib.ssd_bwd_stage_count.restype = ctypes.c_int
     lib.ssd_bwd_stage_count.argtypes = []
     lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
@@ -190,6 +192,55 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     res["workspace"] = workspace
     res["shape"] = shape
     return res
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
+            nseqs: Optional[int] = None, want_final_states: bool = False,
+            workspace: Optional[torch.Tensor] = None):
+    """The SSD layer's forward, computed by libssd_bwd: y, and optionally the
+    state after each sequence's last position.
+
+    Same argument conventions as ssd_bwd.  Returns a dict with y (the I/O
+    dtype, shaped like x) and final_states ((S, H, P, N) fp32, or None).
+    """
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd runs on a HIP device; got tensors on " + str(dev))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = x.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported io dtype {io}")
+    if initial_states is not None:
+        S = initial_states.shape[0]
+    elif seq_idx is None:
+        S = b
+    else:
+        if nseqs is None and want_final_states:
+            raise ValueError("pass nseqs (number of sequence starts) with seq_idx")
+        S = nseqs or 0
+    _check(x, "x", io, (b, L, H, P), dev)
+    _check(B, "B", io, (b, L, G, N), dev)
+    _check(C, "C", io, (b, L, G, N), dev)
+    _check(dt, "dt", torch.float32, (b, L, H), dev)
+    _check(A, "A", torch.float32, (H,), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
+    _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
+    shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
+    nbytes = workspace_size(shape)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    fin = (torch.empty((S, H, P, N), dtype=torch.float32, device=dev) if want_final_states and S > 0 else None)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_fwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                     _ptr(initial_states), _ptr(seq_idx), _ptr(y), _ptr(fin), _ptr(workspace),
+                     ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if rc:
+        raise SsdError(rc, "ssd_fwd")
+    return {"y": y, "final_states": fin, "workspace": workspace, "shape": shape}
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:
