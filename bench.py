@@ -198,6 +198,37 @@ def cpu_baseline(w, inputs, groups=1):
                        f"tokens/s scaled by {h1}/{w.nheads} of the heads")}
 
 
+def measure_forward(torch, ssd, w, d, S, ws, z, steps, warmup):
+    """ssd_fwd (y and the final states) on the same workload, timed like the backward.
+
+    Algorithmic bytes: read x, B, C, dt (and h0); write y and the final
+    states; one write and one read of the chunk states."""
+    def call():
+        return ssd.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d.get("initial_states"),
+                           d.get("seq_idx"), chunk_size=w.chunk, nseqs=S, want_final_states=True, workspace=ws)
+    for _ in range(warmup):
+        ref = call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        last = call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    fin = S * w.nheads * w.headdim * w.dstate * 4
+    alg = 2 * z["X"] + 2 * z["BC"] + z["DT"] + z["INIT"] + 2 * z["T"] + fin + z["SEQ"]
+    gbs = alg / (ms * 1e-3) / 1e9
+    bitwise = (torch.equal(ref["y"].view(torch.int16) if ref["y"].dtype == torch.bfloat16 else ref["y"].view(torch.int32),
+                           last["y"].view(torch.int16) if last["y"].dtype == torch.bfloat16 else last["y"].view(torch.int32))
+               and torch.equal(ref["final_states"].view(torch.int32), last["final_states"].view(torch.int32)))
+    return {"ms_per_call": ms, "tokens_per_s": w.tokens / (ms * 1e-3), "calls": steps, "warmup": warmup,
+            "roofline": {"bound": "hbm", "alg_bytes": alg, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS},
+            "bitwise_repeat": bitwise}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +236,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-forward", action="store_true", help="skip the forward (ssd_fwd) measurement")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -310,6 +342,9 @@ def main():
         "stages_ms": stage_ms,
         "bitwise_repeat": bitwise,
     }
+    if not args.no_forward:
+        res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=min(args.steps, 100),
+                                         warmup=min(args.warmup, 10))
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
