@@ -74,6 +74,26 @@ struct RowSplit {
   }
 };
 
+// One CB^T tile as a lane holds it between k_cbf and k_y: the accumulator's
+// four values, as bf16 pairs on the bf16 path (the MFMA operand they scale
+// is rounded to bf16 anyway) and as fp32 on the fp32 path.
+template <typename T> struct CbPack;
+template <> struct CbPack<bf16_t> {
+  using type = uint2;
+  static __device__ __forceinline__ type pack(f32x4_t v) {
+    return uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+  static __device__ __forceinline__ f32x4_t unpack(type u) {
+    return f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+  }
+};
+template <> struct CbPack<float> {
+  using type = f32x4_t;
+  static __device__ __forceinline__ type pack(f32x4_t v) { return v; }
+  static __device__ __forceinline__ f32x4_t unpack(type v) { return v; }
+};
+
 template <typename T, int Q>
 struct CbfCfg {
   static constexpr int T16 = Q / 16;
@@ -86,7 +106,8 @@ struct CbfCfg {
 };
 
 // CB^T tiles: tile (I, J) holds CB^T[j][i] = B_j . C_i in the accumulator
-// layout (lane: rows j = 16 J + 4 (lane / 16) + r, column i = 16 I + lane % 16).
+// layout (lane: rows j = 16 J + 4 (lane / 16) + r, column i = 16 I + lane % 16),
+// stored per lane in the CbPack format.
 template <typename T, int Q>
 __global__ __launch_bounds__((CbfCfg<T, Q>::NTHR)) void k_cbf(Problem pb) {
   using Cf = CbfCfg<T, Q>;
@@ -130,216 +151,353 @@ __global__ __launch_bounds__((CbfCfg<T, Q>::NTHR)) void k_cbf(Problem pb) {
     }
   }
   const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
-  float* dst = pb.cbt + (bgc * W + w) * (T16 + 1) * 256 + l * 4;
+  using Pk = CbPack<T>;
+  typename Pk::type* dst = reinterpret_cast<typename Pk::type*>(pb.cbt) + (bgc * W + w) * (T16 + 1) * WAVE + l;
 #pragma unroll
-  for (int k = 0; k < T16 + 1; ++k) *reinterpret_cast<f32x4_t*>(dst + k * 256) = acc[k];
+  for (int k = 0; k < T16 + 1; ++k) dst[k * WAVE] = Pk::pack(acc[k]);
 }
 
 // ----------------------------------------------------------------------------
-// k_y
+// k_y: one block per (batch, group, chunk, slice of the group's heads).  The
+// group's C rows and C B^T tiles do not depend on the head, so the block
+// stages them once (C in LDS when one dstate slab holds all of N, the wave's
+// CB^T tiles in registers) and walks its heads, reading per head only x, the
+// entering state and the per-position tables, and requesting the next head's
+// while it computes the current one.
 // ----------------------------------------------------------------------------
-template <typename T, int Q, int P>
+template <typename T, int Q, int P, int NS>
 struct YCfg {
   static constexpr int T16 = Q / 16;
   static constexpr int W = Q / 32;
   static constexpr int NTHR = W * WAVE;
   static constexpr int PT = P / 16;
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int LDX = P + VEC;                   // dt-scaled x rows [j][p]
-  static constexpr int NS = sizeof(T) == 2 ? 32 : 16;   // dstate slab of the state term (divides N)
-  static constexpr int LDC = NS + VEC;                  // C rows [i][n] of one slab
-  static constexpr int LDE = NS + VEC;                  // E rows [p][n] of one slab
+  static constexpr int LDX = P + VEC;    // x rows [j][p]
+  static constexpr int LDC = NS + VEC;   // C rows [i][n] of one dstate slab
+  static constexpr int LDE = NS + VEC;   // E rows [p][n] of one dstate slab
+  static constexpr int NOWN = T16 + 1;
   using Split = RowSplit<T16>;
+  // x, C, E; acs, dt, exp-table, segpos (Q each) and segment starts (Q + 1)
   static constexpr size_t LDS =
       (size_t(Q) * LDX + size_t(Q) * LDC + size_t(P) * LDE) * sizeof(T) + size_t(5 * Q + 1) * 4;
 };
 
-template <typename T, int Q, int P>
-__global__ __launch_bounds__((YCfg<T, Q, P>::NTHR)) void k_y(Problem pb) {
-  using Cf = YCfg<T, Q, P>;
-  constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
-  constexpr int LDX = Cf::LDX, NS = Cf::NS, LDC = Cf::LDC, LDE = Cf::LDE;
+// The intra-chunk term over the wave's tiles (row split order), added to the
+// y^T tiles of the wave's two row tiles: ya (row w) and yb (row T-1-w).  The
+// decay and dt_j multiply the CB^T tile before it becomes the MFMA operand:
+// G^T[j][i] = CB[i,j] exp(Acs_i - Acs_j) dt_j.  Row w's off-diagonal tiles
+// come first, then row T-1-w's, then the two diagonal tiles; which
+// accumulator an early tile feeds is a wave-uniform branch around its MFMAs.
+// UNI: the chunk has one segment, so an off-diagonal decay factors through the
+// column table ejdt[j] = exp(Acs_{16J+15} - Acs_j) dt_j; the two versions keep
+// the unrolled sequence free of branches on it.
+template <typename T, int P, bool UNI>
+struct YTileOps {   // a tile's LDS operands, requested one tile ahead
+  float aref;        // UNI: Acs at the end of the column tile
+  f32x4_t t0;        // UNI: ejdt of the lane's 4 columns; else their Acs
+  f32x4_t dt4;       // (general) dt of the lane's 4 columns
+  int4 sj;           // (general) segpos of the lane's 4 columns
+  typename Mma<T>::rfrag xf[P / 16];
+};
+
+template <typename T, int Q, int P, int NS, bool UNI>
+__device__ __forceinline__ void y_tiles(const typename CbPack<T>::type (&cb)[Q / 16 + 1], f32x4_t (&ya)[P / 16],
+                                        f32x4_t (&yb)[P / 16], const T* s_x, const float* s_acs,
+                                        const float* s_dt, const float* s_ejdt, const int* s_seg, int w, int l) {
+  using Cf = YCfg<T, Q, P, NS>;
+  constexpr int T16 = Cf::T16, PT = Cf::PT, LDX = Cf::LDX;
+  const int r16 = l & 15, kg = l >> 4;
+  // per-row values: Acs_i and (general) the segment start of i
+  const int iw = 16 * Cf::Split::row(w, 0) + r16, iv = 16 * Cf::Split::row(w, 1) + r16;
+  const float ai_w = s_acs[iw], ai_v = s_acs[iv];
+  int lo_w = 0, lo_v = 0;
+  if (!UNI) {
+    lo_w = seg_lo(s_seg[iw]);
+    lo_v = seg_lo(s_seg[iv]);
+  }
+  auto load_ops = [&](int k) {
+    int a, I, J;
+    Cf::Split::tile(w, k, a, I, J);
+    const bool diag = k >= T16 - 1;
+    YTileOps<T, P, UNI> o;
+    if (UNI && !diag) {
+      o.aref = s_acs[16 * J + 15];
+      o.t0 = *reinterpret_cast<const f32x4_t*>(s_ejdt + 16 * J + 4 * kg);
+    } else {
+      o.t0 = *reinterpret_cast<const f32x4_t*>(s_acs + 16 * J + 4 * kg);
+      o.dt4 = *reinterpret_cast<const f32x4_t*>(s_dt + 16 * J + 4 * kg);
+      o.sj = *reinterpret_cast<const int4*>(s_seg + 16 * J + 4 * kg);
+    }
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) o.xf[pt] = Mma<T>::rfrag_load_kn(s_x + 16 * J * LDX + 16 * pt, LDX);
+    return o;
+  };
+  YTileOps<T, P, UNI> nxt = load_ops(0);
+#pragma clang loop unroll(full)
+  for (int k = 0; k < Cf::NOWN; ++k) {
+    const YTileOps<T, P, UNI> cur = nxt;
+    if (k + 1 < Cf::NOWN) nxt = load_ops(k + 1);
+    int a, I, J;
+    Cf::Split::tile(w, k, a, I, J);
+    const bool diag = k >= T16 - 1;   // a constant once unrolled
+    const float ai = a ? ai_v : ai_w;
+    f32x4_t e4;
+    if (UNI && !diag) {
+      const float ei = Elem<T>::exp(ai - cur.aref);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e4[r] = ei * cur.t0[r];
+    } else {
+      // causal and same-segment mask
+      const int i = 16 * I + r16;
+      const int loi = UNI ? 0 : (a ? lo_v : lo_w);
+      const int sjv[4] = {cur.sj.x, cur.sj.y, cur.sj.z, cur.sj.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * kg + r;
+        const bool ok = (j <= i) & (UNI || seg_lo(sjv[r]) == loi);
+        const float e = Elem<T>::exp(ok ? ai - cur.t0[r] : 0.f);
+        e4[r] = ok ? e * cur.dt4[r] : 0.f;
+      }
+    }
+    const f32x4_t cbk = CbPack<T>::unpack(cb[k]);
+    f32x4_t gT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gT[r] = cbk[r] * e4[r];
+    const typename Mma<T>::rfrag gf = Mma<T>::rfrag_from_acc(gT);
+    const bool row_w = k == T16 - 1 || (k < T16 / 2 && k < w);
+    if (row_w) {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) ya[pt] = Mma<T>::mma_rd(cur.xf[pt], gf, ya[pt]);
+    } else {
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) yb[pt] = Mma<T>::mma_rd(cur.xf[pt], gf, yb[pt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename T, int Q, int P, int NS, bool MULTI>
+__global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
+  using Cf = YCfg<T, Q, P, NS>;
+  constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT;
+  constexpr int LDX = Cf::LDX, LDC = Cf::LDC, LDE = Cf::LDE;
   constexpr int KW = Mma<T>::KW, KS = Mma<T>::KSTEP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  T* s_xs = reinterpret_cast<T*>(smem);
-  T* s_c = s_xs + Q * LDX;
-  T* s_e = s_c + Q * LDC;
-  float* s_acs = reinterpret_cast<float*>(s_e + P * LDE);
-  float* s_dt = s_acs + Q;
-  float* s_ej = s_dt + Q;
-  int* s_seg = reinterpret_cast<int*>(s_ej + Q);
-  int* s_segstart = s_seg + Q;   // Q + 1 entries (only the chunk's segments are used)
+  T* const s_x0 = reinterpret_cast<T*>(smem);
+  T* const s_c0 = s_x0 + Q * LDX;
+  T* const s_e0 = s_c0 + Q * LDC;
+  float* const s_acs0 = reinterpret_cast<float*>(s_e0 + P * LDE);
+  float* const s_dt0 = s_acs0 + Q;
+  float* const s_ejdt0 = s_dt0 + Q;
+  int* const s_seg0 = reinterpret_cast<int*>(s_ejdt0 + Q);
+  int* const s_segstart0 = s_seg0 + Q;   // Q + 1 entries (only the chunk's segments are used)
 
-  const int64_t total = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
+  // block -> (batch, group, chunk, head slice); the slices of one (b, g, c)
+  // are consecutive logical blocks and so share an XCD's L2
+  const int64_t total = gridDim.x;
+  const int nsplit = static_cast<int>(total / (static_cast<int64_t>(pb.B) * pb.G * pb.nc));
   const int64_t lb = xcd_logical_block(blockIdx.x, total);
-  const int hh = static_cast<int>(lb % pb.hpg);
-  int64_t rest = lb / pb.hpg;
+  const int split = static_cast<int>(lb % nsplit);
+  int64_t rest = lb / nsplit;
   const int c = static_cast<int>(rest % pb.nc);
   rest /= pb.nc;
   const int g = static_cast<int>(rest % pb.G), b = static_cast<int>(rest / pb.G);
-  const int h = g * pb.hpg + hh;
-  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int hper = (pb.hpg + nsplit - 1) / nsplit;
+  const int h_begin = g * pb.hpg + split * hper;
+  const int h_end = g * pb.hpg + min(pb.hpg, (split + 1) * hper);
+  if (h_begin >= h_end) return;   // (uniform)
+  const int tid = threadIdx.x, w0 = wave_id_s(), l0 = lane_id();
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-  const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
   const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
   const T* xg = static_cast<const T*>(pb.x);
   const T* Cg = static_cast<const T*>(pb.Cm);
+  // MULTI: N spans several dstate slabs and C is restaged slab by slab for
+  // every head; otherwise N == NS and C stays in LDS
 
-  // per-position metadata; ej_j = exp(Acs_{16 J + 15} - Acs_j) (j in tile J)
-  if (tid < Q) {
-    const float acs_i = pb.acs[bhc * Q + tid];
-    s_acs[tid] = acs_i;
-    s_dt[tid] = pb.dtc[bhc * Q + tid];
-    const int seg_i = pb.segpos[bc * Q + tid];
-    s_seg[tid] = seg_i;
-    const float acs_ref = __shfl(acs_i, l | 15, WAVE);
-    s_ej[tid] = Elem<T>::exp(acs_ref - acs_i);
-    if (tid > 0 && seg_lo(seg_i) == tid) s_segstart[seg_rank(seg_i) - seg_rank(pb.segpos[bc * Q])] = tid;
-  }
+  // chunk-wide segment structure
   const int nstart = pb.cinfo[bc * CINFO + 0];
   const int seqbase = pb.cinfo[bc * CINFO + 3];
   const int rank0 = seg_rank(pb.segpos[bc * Q]);   // 1 when a sequence starts at position 0
   const int nseg = nstart + 1 - rank0;
   const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
   const bool uniform = __builtin_amdgcn_readfirstlane(lolast) == 0;
-  if (tid == 0) {
-    s_segstart[0] = 0;
-    s_segstart[nseg] = Q;
-  }
-  // x rows -> LDS scaled by dt (rows past L are zero)
-  {
-    RowStage<T, Q, P, NTHR> st_x;
-    st_x.load([&](int i) -> const T* {
-      const int t = c * Q + i;
-      return t < pb.L ? xg + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
-    });
-    __syncthreads();   // s_dt
-#pragma unroll
-    for (int k = 0; k < st_x.IT; ++k) {
-      const int v = tid + k * NTHR;
-      if (v < st_x.NV) {
-        const int i = v / st_x.CV, c0 = (v % st_x.CV) * VEC;
-        const float d = s_dt[i];
-        T o[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = Elem<T>::from_f(vget<T>(st_x.buf[k], e) * d);
-        *reinterpret_cast<uint4*>(s_xs + i * LDX + c0) = *reinterpret_cast<const uint4*>(o);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- intra-chunk term, row tile by row tile (slot a = 0: row w, 1: row T-1-w)
-  f32x4_t y0[PT], y1[PT];   // y^T tiles of the two owned row tiles: [p][i]
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt) y0[pt] = y1[pt] = zero4();
-  const float* cbw = pb.cbt + (bgc * W + w) * (T16 + 1) * 256 + l * 4;
-  auto tile = [&](int a, int I, int J, f32x4_t(&yt)[PT]) {
-    const f32x4_t cbT = *reinterpret_cast<const f32x4_t*>(cbw + Cf::Split::pos(w, a, J) * 256);
-    const int i = 16 * I + r16;
-    const float ai = s_acs[i];
-    f32x4_t e4;
-    if (uniform && J < I) {
-      const float ei = Elem<T>::exp(ai - s_acs[16 * J + 15]);
-      const f32x4_t ej = *reinterpret_cast<const f32x4_t*>(s_ej + 16 * J + 4 * kg);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) e4[r] = ei * ej[r];
-    } else {
-      const int loi = seg_lo(s_seg[i]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * J + 4 * kg + r;
-        const bool ok = (j <= i) & (seg_lo(s_seg[j]) == loi);
-        const float e = Elem<T>::exp(ok ? ai - s_acs[j] : 0.f);
-        e4[r] = ok ? e : 0.f;
-      }
-    }
-    f32x4_t gT;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) gT[r] = cbT[r] * e4[r];
-    const typename Mma<T>::rfrag gf = Mma<T>::rfrag_from_acc(gT);
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-      yt[pt] = Mma<T>::mma_rd(Mma<T>::rfrag_load_kn(s_xs + 16 * J * LDX + 16 * pt, LDX), gf, yt[pt]);
-  };
-  {
-    const int I0 = Cf::Split::row(w, 0), I1 = Cf::Split::row(w, 1);
-    for (int J = 0; J <= I0; ++J) tile(0, I0, J, y0);
-    for (int J = 0; J <= I1; ++J) tile(1, I1, J, y1);
-  }
-
-  // ---- state term: exp(Acs_i) C_i . E_seg(i), segment by segment, dstate slab by slab
-  f32x4_t z0[PT], z1[PT];
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt) z0[pt] = z1[pt] = zero4();
-  for (int m = 0; m < nseg; ++m) {
-    const int lo = s_segstart[m], hi = s_segstart[m + 1];
-    const int rank = seg_rank(s_seg[lo]);
-    // entering state: Hin_c (I/O dtype) or h0[s] (fp32) or none
-    const T* e_t = nullptr;
-    const float* e_f = nullptr;
+  // entering state of segment m for head h: Hin_c (I/O dtype), h0[s] (fp32), or none
+  auto e_src = [&](int h, int m, const T*& e_t, const float*& e_f) {
+    e_t = nullptr;
+    e_f = nullptr;
+    const int rank = m == 0 ? rank0 : rank0 + m;
     if (rank == 0) {
-      e_t = static_cast<const T*>(pb.hin) + bhc * P * pb.N;
+      e_t = static_cast<const T*>(pb.hin) + ((static_cast<int64_t>(b) * pb.H + h) * pb.nc + c) * P * pb.N;
     } else if (pb.h0) {
       const int s = clamp_seq(seqbase + rank - 1, pb.nseqs);
       e_f = pb.h0 + (static_cast<int64_t>(s) * pb.H + h) * P * pb.N;
     }
-    if (!e_t && !e_f) continue;   // (uniform)
-    for (int n0 = 0; n0 < pb.N; n0 += NS) {
-      RowStage<T, Q, NS, NTHR> st_c;
-      RowStage<T, P, NS, NTHR> st_e;
-      st_c.load([&](int i) -> const T* {
-        const int t = c * Q + i;
-        return t < pb.L ? Cg + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 : nullptr;
-      });
-      if (e_t)
-        st_e.load([&](int p) -> const T* { return e_t + static_cast<int64_t>(p) * pb.N + n0; });
-      else
-        st_e.load_from_f32([&](int p) -> const float* { return e_f + static_cast<int64_t>(p) * pb.N + n0; });
-      __syncthreads();   // the previous slab is read
-      st_c.store(s_c, LDC);
-      st_e.store(s_e, LDE);
-      __syncthreads();
+  };
+  auto c_row = [&](int n0) {
+    return [=, &pb](int i) -> const T* {
+      const int t = c * Q + i;
+      return t < pb.L ? Cg + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 : nullptr;
+    };
+  };
+  auto load_e = [&](RowStage<T, P, NS, NTHR>& st, const T* e_t, const float* e_f, int n0) {
+    if (e_t)
+      st.load([=, &pb](int p) -> const T* { return e_t + static_cast<int64_t>(p) * pb.N + n0; });
+    else if (e_f)
+      st.load_from_f32([=, &pb](int p) -> const float* { return e_f + static_cast<int64_t>(p) * pb.N + n0; });
+  };
+  // segment 0 continues the chunk's sequence: its entering state Hin_c comes
+  // with the head's prefetch (any other entering state is staged in the state
+  // loop; a single load path keeps the prefetch free of waits)
+  const bool e0_hin = rank0 == 0;
+
+  // the per-head inputs, requested one head ahead
+  float pf_acs = 0.f, pf_dt = 0.f;
+  RowStage<T, Q, P, NTHR> st_x;
+  RowStage<T, P, NS, NTHR> st_e;
+  auto prefetch = [&](int h) {
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    if (tid < Q) {
+      pf_acs = pb.acs[bhc * Q + tid];
+      pf_dt = pb.dtc[bhc * Q + tid];
+    }
+    st_x.load([&](int i) -> const T* {
+      const int t = c * Q + i;
+      return t < pb.L ? xg + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
+    });
+    if (e0_hin) {
+      const T* e_t = static_cast<const T*>(pb.hin) + bhc * P * pb.N;
+      st_e.load([=, &pb](int p) -> const T* { return e_t + static_cast<int64_t>(p) * pb.N; });
+    }
+  };
+
+  // head-independent inputs: the wave's CB^T tiles, C (one slab), segments
+  typename CbPack<T>::type cb[T16 + 1];
+  {
+    const auto* cbw = reinterpret_cast<const typename CbPack<T>::type*>(pb.cbt) + (bgc * W + w0) * (T16 + 1) * WAVE + l0;
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int I = Cf::Split::row(w, a);
-        if (16 * I + 15 < lo || 16 * I >= hi) continue;   // (uniform)
-        const int i = 16 * I + r16;
-        const bool in_seg = i >= lo && i < hi;
+    for (int k = 0; k < T16 + 1; ++k) cb[k] = cbw[k * WAVE];
+  }
+  RowStage<T, Q, NS, NTHR> st_c;
+  if (!MULTI) st_c.load(c_row(0));
+  prefetch(h_begin);
+  if (tid < Q) {
+    const int v = pb.segpos[bc * Q + tid];
+    s_seg0[tid] = v;
+    if (tid > 0 && seg_lo(v) == tid) s_segstart0[seg_rank(v) - rank0] = tid;
+  }
+  if (tid == 0) {
+    s_segstart0[0] = 0;
+    s_segstart0[nseg] = Q;
+  }
+  if (!MULTI) st_c.store(s_c0, LDC);
+
+  for (int h = h_begin; h < h_end; ++h) {
+    // per-iteration LDS bases keep the compiler from hoisting per-tile
+    // addresses and masks out of the head loop (they would hold registers)
+    const int oz = opaque_zero();
+    T* const s_x = s_x0 + oz;
+    T* const s_c = s_c0 + oz;
+    T* const s_e = s_e0 + oz;
+    float* const s_acs = s_acs0 + oz;
+    float* const s_dt = s_dt0 + oz;
+    float* const s_ejdt = s_ejdt0 + oz;
+    int* const s_seg = s_seg0 + oz;
+    int* const s_segstart = s_segstart0 + oz;
+    const int w = w0 + oz, l = l0 + oz, r16 = l & 15, kg = l >> 4;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          f32x4_t v = a ? z1[pt] : z0[pt];
+    for (int k = 0; k < T16 + 1; ++k) asm volatile("" : "+v"(cb[k]));   // (nor their unpacked values)
+    __syncthreads();   // the previous head is done with the per-head LDS
+    if (tid < Q) {
+      s_acs[tid] = pf_acs;
+      s_dt[tid] = pf_dt;
+      const float acs_ref = __shfl(pf_acs, l | 15, WAVE);   // Acs at the end of the 16-row tile
+      s_ejdt[tid] = Elem<T>::exp(acs_ref - pf_acs) * pf_dt;
+    }
+    st_x.store(s_x, LDX);
+    if (e0_hin) st_e.store(s_e, LDE);
+    __syncthreads();
+    if (h + 1 < h_end) prefetch(h + 1);
+
+    // ---- state term, exp(Acs_i) C_i . E_seg(i), segment by segment and
+    // dstate slab by slab, into the y^T tiles of the wave's rows (ya: row w,
+    // yb: row T-1-w)
+    f32x4_t ya[PT], yb[PT];
 #pragma unroll
-          for (int k0 = 0; k0 < NS; k0 += KS) {
-            const auto af = Mma<T>::load_k(s_e + (16 * pt + r16) * LDE + kg * KW + k0);
-            auto bf = Mma<T>::load_k(s_c + i * LDC + kg * KW + k0);
-            if (!in_seg) bf = Mma<T>::zero();
-            v = Mma<T>::mma(af, bf, v);
+    for (int pt = 0; pt < PT; ++pt) ya[pt] = yb[pt] = zero4();
+    for (int m = 0; m < nseg; ++m) {
+      const int lo = s_segstart[m], hi = s_segstart[m + 1];
+      const T* e_t;
+      const float* e_f;
+      e_src(h, m, e_t, e_f);
+      if (!e_t && !e_f) continue;   // (uniform) no entering state
+      for (int n0 = 0; n0 < pb.N; n0 += NS) {
+        const bool stage_e = m > 0 || n0 > 0 || !e0_hin;   // (Hin's first slab came with the head)
+        if (MULTI || stage_e) {
+          RowStage<T, P, NS, NTHR> st_e2;
+          if (MULTI) st_c.load(c_row(n0));
+          if (stage_e) load_e(st_e2, e_t, e_f, n0);
+          __syncthreads();   // the previous slab is read
+          if (MULTI) st_c.store(s_c, LDC);
+          if (stage_e) st_e2.store(s_e, LDE);
+          __syncthreads();
+        }
+        // rows outside the segment take zero C operands (a row tile wholly
+        // outside it adds nothing)
+        const int iw = 16 * Cf::Split::row(w, 0) + r16, iv = 16 * Cf::Split::row(w, 1) + r16;
+        const bool in_w = iw >= lo && iw < hi, in_v = iv >= lo && iv < hi;
+#pragma unroll
+        for (int k0 = 0; k0 < NS; k0 += KS) {
+          typename Mma<T>::frag af[PT];
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) af[pt] = Mma<T>::load_k(s_e + (16 * pt + r16) * LDE + kg * KW + k0);
+          auto bw = Mma<T>::load_k(s_c + iw * LDC + kg * KW + k0);
+          auto bv = Mma<T>::load_k(s_c + iv * LDC + kg * KW + k0);
+          if (!in_w) bw = Mma<T>::zero();
+          if (!in_v) bv = Mma<T>::zero();
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) {
+            ya[pt] = Mma<T>::mma(af[pt], bw, ya[pt]);
+            yb[pt] = Mma<T>::mma(af[pt], bv, yb[pt]);
           }
-          if (a) z1[pt] = v; else z0[pt] = v;
         }
       }
     }
-  }
+    {
+      // a lane's accumulator values share one row i = 16 I + lane % 16
+      const float e_w = Elem<T>::exp(s_acs[16 * Cf::Split::row(w, 0) + r16]);
+      const float e_v = Elem<T>::exp(s_acs[16 * Cf::Split::row(w, 1) + r16]);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ya[pt][r] *= e_w;
+          yb[pt][r] *= e_v;
+        }
+    }
 
-  // ---- epilogue: y = intra + exp(Acs_i) state + D x
-  const float Dh = pb.D ? pb.D[h] : 0.f;
+    // ---- intra-chunk term
+    if (uniform)
+      y_tiles<T, Q, P, NS, true>(cb, ya, yb, s_x, s_acs, s_dt, s_ejdt, s_seg, w, l);
+    else
+      y_tiles<T, Q, P, NS, false>(cb, ya, yb, s_x, s_acs, s_dt, s_ejdt, s_seg, w, l);
+
+    // ---- epilogue: y = intra + state + D x
+    const float Dv = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int I = Cf::Split::row(w, a);
-    const int i = 16 * I + r16, t = c * Q + i;
-    if (t >= pb.L) continue;
-    const float ei = Elem<T>::exp(s_acs[i]);
-    const int64_t row = ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P;
+    for (int a = 0; a < 2; ++a) {
+      const int I = Cf::Split::row(w, a);
+      const int i = 16 * I + r16, t = c * Q + i;
+      if (t >= pb.L) continue;
+      const int64_t row = ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P;
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      const f32x4_t yv = a ? y1[pt] : y0[pt];
-      const f32x4_t zv = a ? z1[pt] : z0[pt];
-      const f32x4_t xv = load4f<T>(xg + row + 16 * pt + 4 * kg);
-      f32x4_t o;
+      for (int pt = 0; pt < PT; ++pt) {
+        const f32x4_t yv = a ? yb[pt] : ya[pt];
+        const f32x4_t xv = load4f<T>(s_x + i * LDX + 16 * pt + 4 * kg);
+        f32x4_t o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = yv[r] + ei * zv[r] + Dh * xv[r];
-      store4f<T>(static_cast<T*>(pb.y) + row + 16 * pt + 4 * kg, o);
+        for (int r = 0; r < 4; ++r) o[r] = yv[r] + Dv * xv[r];
+        store4f<T>(static_cast<T*>(pb.y) + row + 16 * pt + 4 * kg, o);
+      }
     }
   }
 }
@@ -462,6 +620,35 @@ __global__ __launch_bounds__((FinalCfg<T, Q, P, NT>::NTHR)) void k_final(Problem
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
+template <typename T, int Q, int P, int NS, bool MULTI>
+static hipError_t launch_y(const Problem& pb, hipStream_t s) {
+  using Cf = YCfg<T, Q, P, NS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_y<T, Q, P, NS, MULTI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // heads per block: as many as keep about four blocks per CU in the grid
+  const int64_t bgc = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
+  static int ncu = 0;
+  if (ncu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      ncu = n;
+    else
+      ncu = 256;
+  }
+  const int64_t want = 4 * static_cast<int64_t>(ncu);
+  int nsplit = static_cast<int>(std::min<int64_t>(pb.hpg, (want + bgc - 1) / bgc));
+  const int hper = (pb.hpg + nsplit - 1) / nsplit;
+  nsplit = (pb.hpg + hper - 1) / hper;
+  hipLaunchKernelGGL((k_y<T, Q, P, NS, MULTI>), dim3(static_cast<unsigned>(bgc * nsplit)), dim3(Cf::NTHR), Cf::LDS, s, pb);
+  return hipGetLastError();
+}
+
 template <typename T, int Q, int P>
 static hipError_t launch_fwd_qp(const Problem& pb, hipStream_t s) {
   {
@@ -471,17 +658,13 @@ static hipError_t launch_fwd_qp(const Problem& pb, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   {
-    using Cf = YCfg<T, Q, P>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_y<T, Q, P>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
-    const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
-    hipLaunchKernelGGL((k_y<T, Q, P>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
-    hipError_t e = hipGetLastError();
+    // all of N in one dstate slab up to 128 (bf16) / 64 (fp32) columns, else
+    // slabs of 64 / 32 columns (or 32 / 16 when those do not divide N)
+    constexpr int S = sizeof(T) == 2 ? 32 : 16;
+    hipError_t e = pb.N == 4 * S   ? launch_y<T, Q, P, 4 * S, false>(pb, s)
+                   : pb.N == 2 * S ? launch_y<T, Q, P, 2 * S, false>(pb, s)
+                   : pb.N % (2 * S) == 0 ? launch_y<T, Q, P, 2 * S, true>(pb, s)
+                                         : launch_y<T, Q, P, S, true>(pb, s);
     if (e != hipSuccess) return e;
   }
   if (pb.final) {
@@ -522,9 +705,9 @@ hipError_t launch_fwd_out(const Problem& pb, bool io_bf16, hipStream_t s) {
 
 size_t fwd_lds_bytes(int Q, int P, bool bf16) {
 #define SSD_Y_LDS_B(QQ, PP) \
-  if (bf16 && Q == QQ && P == PP) return YCfg<bf16_t, QQ, PP>::LDS;
+  if (bf16 && Q == QQ && P == PP) return YCfg<bf16_t, QQ, PP, 128>::LDS;
 #define SSD_Y_LDS_F(QQ, PP) \
-  if (!bf16 && Q == QQ && P == PP) return YCfg<float, QQ, PP>::LDS;
+  if (!bf16 && Q == QQ && P == PP) return YCfg<float, QQ, PP, 64>::LDS;
   SSD_BF16_SHAPES(SSD_Y_LDS_B)
   SSD_F32_SHAPES(SSD_Y_LDS_F)
 #undef SSD_Y_LDS_B
