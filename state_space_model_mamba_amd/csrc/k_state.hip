@@ -136,12 +136,38 @@ __device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q
   }
 }
 
+// Forward walk.  The chunk rows are double-buffered in LDS: chunk c's
+// product reads one buffer while chunk c+1's rows, which arrived in registers
+// during chunk c-1, are staged into the other, and chunk c+2's rows and
+// metadata are requested; one barrier per chunk.  Each thread scales the x
+// rows it stages with w_j = exp(Acs_end - Acs_j) dt_j from its own loads.
+// Every load is unconditional (row indices past L are clamped and the values
+// zeroed when staged), so the requests never wait on a branch join.
+template <typename T, int Q, int P, int NT>
+struct StateFwdCfg {
+  using Cf = StateCfg<T, Q, P, NT>;
+  static constexpr int XSZ = Q * Cf::XTile::LD;   // elements of one x buffer
+  static constexpr int BSZ = Q * Cf::BTile::LD;
+  static constexpr size_t LDS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T);
+};
+
+// What a chunk's staging needs, as loaded (nothing derived, so nothing waits
+// for it before the staging itself)
+template <int NXV>
+struct FwdRaw {
+  float acs_end;
+  int seg_last, nstart, seqbase;
+  float acs[NXV], dt[NXV];   // of the rows this thread stages
+};
+
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_xt[Q * Cf::XTile::LD];
-  __shared__ __attribute__((aligned(16))) T s_bt[Q * Cf::BTile::LD];
-  __shared__ float s_w[Q];
+  using Fc = StateFwdCfg<T, Q, P, NT>;
+  constexpr int VEC = Cf::VEC, NTHR = Cf::NTHR, NXV = Cf::NXV, NBV = Cf::NBV;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T* const s_x0 = reinterpret_cast<T*>(smem);
+  T* const s_b0 = s_x0 + 2 * Fc::XSZ;
 
   const int ntiles = pb.N / NT;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
@@ -151,50 +177,116 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
   const int h = static_cast<int>(bh % pb.H), b = static_cast<int>(bh / pb.H);
   const int g = h / pb.hpg, n0 = ntile * NT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* xs = static_cast<const T*>(pb.x);
+  const T* bs = static_cast<const T*>(pb.Bm);
 
-  uint4 xr[Cf::NXV], br[Cf::NBV];
+  // the thread's staged vectors: x vector k is row xrow(k), B vector k row
+  // brow(k); on small shapes some threads have fewer vectors than others
+  auto xrow = [&](int k) { return min((tid + NTHR * k) / (P / VEC), Q - 1); };
+  auto brow = [&](int k) { return min((tid + NTHR * k) / (NT / VEC), Q - 1); };
+  auto xhas = [&](int k) { return Cf::XV % NTHR == 0 || tid + NTHR * k < Cf::XV; };
+  auto bhas = [&](int k) { return Cf::BV % NTHR == 0 || tid + NTHR * k < Cf::BV; };
+
+  uint4 xr[NXV], br[NBV];
+  FwdRaw<NXV> raw;
+  auto request = [&](int c) {
+    c = min(c, pb.nc - 1);   // (past the last chunk: a harmless reload)
+    const int vz = vgpr_zero();
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
+    raw.acs_end = pb.acs[bhc * Q + Q - 1 + vz];
+    raw.seg_last = pb.segpos[bc * Q + Q - 1 + vz];
+    raw.nstart = pb.cinfo[bc * CINFO + 0 + vz];
+    raw.seqbase = pb.cinfo[bc * CINFO + 3 + vz];
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      raw.acs[k] = pb.acs[bhc * Q + xrow(k)];
+      raw.dt[k] = pb.dtc[bhc * Q + xrow(k)];
+      const int t = min(c * Q + xrow(k), pb.L - 1);
+      const int pv = (tid + NTHR * k) % (P / VEC);
+      if (xhas(k)) xr[k] = ld_global16(xs + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * VEC);
+    }
+#pragma unroll
+    for (int k = 0; k < NBV; ++k) {
+      const int t = min(c * Q + brow(k), pb.L - 1);
+      const int nv = (tid + NTHR * k) % (NT / VEC);
+      if (bhas(k)) br[k] = ld_global16(bs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * VEC);
+    }
+  };
+  // per-chunk values the state update needs
+  struct Upd {
+    float decay;
+    int nstart, s_last;
+  };
+  // stage chunk c's rows (arrived in xr / br) into buffer c & 1; returns its update values
+  auto stage = [&](int c) {
+    T* sx = s_x0 + (c & 1) * Fc::XSZ;
+    T* sb = s_b0 + (c & 1) * Fc::BSZ;
+    const int lolast = seg_lo(raw.seg_last);
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      const int j = xrow(k), pv = (tid + NTHR * k) % (P / VEC);
+      const bool ok = j >= lolast && c * Q + j < pb.L;
+      const float sc = ok ? Elem<T>::exp(raw.acs_end - raw.acs[k]) * raw.dt[k] : 0.f;
+      uint4 o;
+      if constexpr (sizeof(T) == 2) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(vget<T>(xr[k], 2 * e) * sc, vget<T>(xr[k], 2 * e + 1) * sc);
+        o = uint4{u[0], u[1], u[2], u[3]};
+      } else {
+        f32x4_t f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = vget<T>(xr[k], e) * sc;
+        o = __builtin_bit_cast(uint4, f);
+      }
+      if (xhas(k)) *reinterpret_cast<uint4*>(sx + Cf::XTile::at(j, pv * VEC)) = o;
+    }
+#pragma unroll
+    for (int k = 0; k < NBV; ++k) {
+      const int j = brow(k), nv = (tid + NTHR * k) % (NT / VEC);
+      if (bhas(k)) *reinterpret_cast<uint4*>(sb + Cf::BTile::at(j, nv * VEC)) = c * Q + j < pb.L ? br[k] : zero_u4();
+    }
+    Upd u;
+    u.decay = Elem<T>::exp(raw.acs_end);
+    u.nstart = raw.nstart;
+    u.s_last = clamp_seq(raw.seqbase + raw.nstart - 1, pb.nseqs);
+    return u;
+  };
+
   f32x4_t st[Cf::TPW];
 #pragma unroll
   for (int k = 0; k < Cf::TPW; ++k) st[k] = zero4();
-
-  // per-chunk metadata, prefetched into registers one chunk ahead together
-  // with the chunk's x / B rows
-  ChunkMeta cur, nxt;
-  cur.load(pb, b, h, 0);
-  load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, 0, xr, br);
+  request(0);
+  Upd cur = stage(0);
+  request(1);
+  __syncthreads();
   for (int c = 0; c < pb.nc; ++c) {
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    if (tid < Q) s_w[tid] = (tid >= cur.lolast) ? Elem<T>::exp(cur.acs_end - cur.acs) * cur.dt : 0.f;
-    __syncthreads();
-    stage_chunk_rows<T, Q, P, NT>(xr, br, s_w, s_xt, s_bt);
-    __syncthreads();
-    if (c + 1 < pb.nc) {
-      nxt.load(pb, b, h, c + 1);
-      load_chunk_rows<T, Q, P, NT>(pb, pb.x, pb.Bm, b, h, g, n0, c + 1, xr, br);
-    }
-
-    const int kb = (cur.lolast / Mma<T>::KSTEP) * Mma<T>::KSTEP;
-    const float decay = Elem<T>::exp(cur.acs_end);
-    const int nstart = cur.nstart;
-    const int s_last = clamp_seq(cur.seqbase + nstart - 1, pb.nseqs);
+    Upd nxt = cur;
+    if (c + 1 < pb.nc) nxt = stage(c + 1);   // (uniform)
+    request(c + 2);
+    const T* sx = s_x0 + (c & 1) * Fc::XSZ;
+    const T* sb = s_b0 + (c & 1) * Fc::BSZ;
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
       const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         f32x4_t S = zero4();
-        for (int k0 = kb; k0 < Q; k0 += Mma<T>::KSTEP)
-          S = Mma<T>::mma(Cf::XTile::frag(s_xt, pt * 16, k0), Cf::BTile::frag(s_bt, nt * 16, k0), S);
+#pragma unroll
+        for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
+          S = Mma<T>::mma(Cf::XTile::frag(sx, pt * 16, k0), Cf::BTile::frag(sb, nt * 16, k0), S);
         const int n = n0 + nt * 16 + r16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int p = pt * 16 + 4 * kg + r;
           static_cast<T*>(pb.hin)[(bhc * P + p) * pb.N + n] = Elem<T>::from_f(st[k][r]);
-          if (nstart == 0) {
-            st[k][r] = decay * st[k][r] + S[r];
+          if (cur.nstart == 0) {
+            st[k][r] = cur.decay * st[k][r] + S[r];
           } else {
             float init = 0.f;
-            if (pb.h0) init = decay * pb.h0[((static_cast<int64_t>(s_last) * pb.H + h) * P + p) * pb.N + n];
+            if (pb.h0) init = cur.decay * pb.h0[((static_cast<int64_t>(cur.s_last) * pb.H + h) * P + p) * pb.N + n];
             st[k][r] = S[r] + init;
           }
         }
@@ -309,9 +401,17 @@ static int state_nt(int N, bool bf16) {
 template <typename T, int Q, int P, int NT>
 static hipError_t launch_state_t(const Problem& pb, bool fwd, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * (pb.N / NT);
-  if (fwd)
-    hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), 0, s, pb);
-  else
+  if (fwd) {
+    constexpr size_t lds = StateFwdCfg<T, Q, P, NT>::LDS;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_state_fwd<T, Q, P, NT>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), lds, s, pb);
+  } else
     hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), 0, s, pb);
   return hipGetLastError();
 }
