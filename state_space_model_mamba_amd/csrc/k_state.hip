@@ -4,8 +4,9 @@
 //
 // Both kernels own one (batch, head, dstate tile) and walk the chunks in
 // order, so every state element is produced by exactly one thread in a fixed
-// order; the next chunk's inputs are prefetched into registers while the
-// current chunk's MFMA contraction runs.
+// order.  The chunk rows are double-buffered in LDS: while chunk c is
+// multiplied from one buffer, the next chunk's rows (requested one chunk
+// earlier) are staged into the other and the rows after it are requested.
 //
 // Forward, chunk c (positions j of the chunk's last segment, Acs restarted at
 // that segment's start):
@@ -39,102 +40,6 @@ struct StateCfg {
   static_assert(NTHR >= Q, "one thread per chunk position");
   static_assert(P % 16 == 0 && NT % 16 == 0 && Q % Mma<T>::KSTEP == 0, "tile shape");
 };
-
-template <typename T, int Q, int P, int NT>
-__device__ __forceinline__ void load_chunk_rows(const Problem& pb, const void* src_hp, const void* src_gn,
-                                                int b, int h, int g, int n0, int c,
-                                                uint4 (&xr)[StateCfg<T, Q, P, NT>::NXV],
-                                                uint4 (&br)[StateCfg<T, Q, P, NT>::NBV]) {
-  using Cf = StateCfg<T, Q, P, NT>;
-  const int tid = threadIdx.x;
-  const T* xs = static_cast<const T*>(src_hp);
-  const T* bs = static_cast<const T*>(src_gn);
-#pragma unroll
-  for (int k = 0; k < Cf::NXV; ++k) {
-    const int v = tid + Cf::NTHR * k;
-    xr[k] = zero_u4();
-    if (v < Cf::XV) {
-      const int j = v / (P / Cf::VEC), pv = v % (P / Cf::VEC), t = c * Q + j;
-      if (t < pb.L)
-        xr[k] = ld_global16(xs + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * Cf::VEC);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < Cf::NBV; ++k) {
-    const int v = tid + Cf::NTHR * k;
-    br[k] = zero_u4();
-    if (v < Cf::BV) {
-      const int j = v / (NT / Cf::VEC), nv = v % (NT / Cf::VEC), t = c * Q + j;
-      if (t < pb.L)
-        br[k] = ld_global16(bs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * Cf::VEC);
-    }
-  }
-}
-
-// Metadata of one (batch, head, chunk): this thread's position (tid < Q) and
-// the chunk-wide values every thread needs.
-struct ChunkMeta {
-  float acs, dt, acs_end;
-  int seg, lolast, nstart, seqbase;
-  __device__ __forceinline__ void load(const Problem& pb, int b, int h, int c) {
-    const int tid = threadIdx.x;
-    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-    acs = 0.f;
-    dt = 0.f;
-    seg = 0;
-    if (tid < pb.Q) {
-      acs = pb.acs[bhc * pb.Q + tid];
-      dt = pb.dtc[bhc * pb.Q + tid];
-      seg = pb.segpos[bc * pb.Q + tid];
-    }
-    acs_end = pb.acs[bhc * pb.Q + pb.Q - 1];
-    lolast = seg_lo(pb.segpos[bc * pb.Q + pb.Q - 1]);
-    nstart = pb.cinfo[bc * CINFO + 0];
-    seqbase = pb.cinfo[bc * CINFO + 3];
-  }
-};
-
-// x (or dy) chunk rows -> LDS [j][p], each row scaled by s_scale[j]; B (or C)
-// tile rows -> LDS [j][n] as they are.  16-byte stores only; the MFMA reads
-// them with LDS transpose reads.
-template <typename T, int Q, int P, int NT>
-__device__ __forceinline__ void stage_chunk_rows(const uint4 (&xr)[StateCfg<T, Q, P, NT>::NXV],
-                                                 const uint4 (&br)[StateCfg<T, Q, P, NT>::NBV],
-                                                 const float* s_scale, T* s_x, T* s_b) {
-  using Cf = StateCfg<T, Q, P, NT>;
-  constexpr int VEC = Cf::VEC;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < Cf::NXV; ++k) {
-    const int v = tid + Cf::NTHR * k;
-    if (v < Cf::XV) {
-      const int j = v / (P / VEC), pv = v % (P / VEC);
-      const float sc = s_scale[j];
-      uint4 o;
-      if constexpr (sizeof(T) == 2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(vget<T>(xr[k], 2 * e) * sc, vget<T>(xr[k], 2 * e + 1) * sc);
-        o = uint4{w[0], w[1], w[2], w[3]};
-      } else {
-        f32x4_t f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = vget<T>(xr[k], e) * sc;
-        o = __builtin_bit_cast(uint4, f);
-      }
-      *reinterpret_cast<uint4*>(s_x + Cf::XTile::at(j, pv * VEC)) = o;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < Cf::NBV; ++k) {
-    const int v = tid + Cf::NTHR * k;
-    if (v < Cf::BV) {
-      const int j = v / (NT / VEC), nv = v % (NT / VEC);
-      *reinterpret_cast<uint4*>(s_b + Cf::BTile::at(j, nv * VEC)) = br[k];
-    }
-  }
-}
 
 // Forward walk.  The chunk rows are double-buffered in LDS: chunk c's
 // product reads one buffer while chunk c+1's rows, which arrived in registers
@@ -297,14 +202,35 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
   }
 }
 
+// Backward walk, chunks from the last down, with the forward walk's
+// pipeline: chunk rows double-buffered in LDS with their segment tables, each
+// thread scaling the dy rows it stages by exp(Acs_i) from its own loads,
+// unconditional requests, one barrier per chunk.
+template <typename T, int Q, int P, int NT>
+struct StateBwdCfg {
+  using Cf = StateCfg<T, Q, P, NT>;
+  static constexpr int XSZ = Q * Cf::XTile::LD;
+  static constexpr int BSZ = Q * Cf::BTile::LD;
+  static constexpr int TSZ = 2 * Q + 1;   // segpos[Q], segment starts[Q + 1]
+  static constexpr size_t LDS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T) + 2 * TSZ * sizeof(int);
+};
+
+template <int NXV>
+struct BwdRaw {
+  float acs_end;
+  int nstart, seqbase, seg0, seg_own;
+  float acs[NXV];   // of the rows this thread stages
+};
+
 template <typename T, int Q, int P, int NT>
 __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Problem pb) {
   using Cf = StateCfg<T, Q, P, NT>;
-  __shared__ __attribute__((aligned(16))) T s_dyt[Q * Cf::XTile::LD];
-  __shared__ __attribute__((aligned(16))) T s_ct[Q * Cf::BTile::LD];
-  __shared__ float s_e[Q];
-  __shared__ int s_seg[Q];
-  __shared__ int s_segstart[Q + 1];
+  using Bc = StateBwdCfg<T, Q, P, NT>;
+  constexpr int VEC = Cf::VEC, NTHR = Cf::NTHR, NXV = Cf::NXV, NBV = Cf::NBV;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T* const s_x0 = reinterpret_cast<T*>(smem);
+  T* const s_b0 = s_x0 + 2 * Bc::XSZ;
+  int* const s_t0 = reinterpret_cast<int*>(s_b0 + 2 * Bc::BSZ);
 
   const int ntiles = pb.N / NT;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
@@ -314,56 +240,126 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
   const int h = static_cast<int>(bh % pb.H), b = static_cast<int>(bh / pb.H);
   const int g = h / pb.hpg, n0 = ntile * NT;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const T* ys = static_cast<const T*>(pb.dy);
+  const T* cs = static_cast<const T*>(pb.Cm);
 
-  uint4 xr[Cf::NXV], br[Cf::NBV];
+  auto xrow = [&](int k) { return min((tid + NTHR * k) / (P / VEC), Q - 1); };
+  auto brow = [&](int k) { return min((tid + NTHR * k) / (NT / VEC), Q - 1); };
+  auto xhas = [&](int k) { return Cf::XV % NTHR == 0 || tid + NTHR * k < Cf::XV; };
+  auto bhas = [&](int k) { return Cf::BV % NTHR == 0 || tid + NTHR * k < Cf::BV; };
+
+  uint4 xr[NXV], br[NBV];
+  BwdRaw<NXV> raw;
+  auto request = [&](int c) {
+    c = max(c, 0);   // (before the first chunk: a harmless reload)
+    const int vz = vgpr_zero();
+    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
+    raw.acs_end = pb.acs[bhc * Q + Q - 1 + vz];
+    raw.nstart = pb.cinfo[bc * CINFO + 0 + vz];
+    raw.seqbase = pb.cinfo[bc * CINFO + 3 + vz];
+    raw.seg0 = pb.segpos[bc * Q + vz];
+    raw.seg_own = pb.segpos[bc * Q + min(tid, Q - 1)];
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      raw.acs[k] = pb.acs[bhc * Q + xrow(k)];
+      const int t = min(c * Q + xrow(k), pb.L - 1);
+      const int pv = (tid + NTHR * k) % (P / VEC);
+      if (xhas(k)) xr[k] = ld_global16(ys + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * VEC);
+    }
+#pragma unroll
+    for (int k = 0; k < NBV; ++k) {
+      const int t = min(c * Q + brow(k), pb.L - 1);
+      const int nv = (tid + NTHR * k) % (NT / VEC);
+      if (bhas(k)) br[k] = ld_global16(cs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * VEC);
+    }
+  };
+  struct Upd {
+    float decay;
+    int nstart, nseg, seqbase;
+  };
+  // stage chunk c (buffer par) from xr / br / raw
+  auto stage = [&](int c, int par) {
+    T* sx = s_x0 + par * Bc::XSZ;
+    T* sb = s_b0 + par * Bc::BSZ;
+    int* s_seg = s_t0 + par * Bc::TSZ;
+    int* s_segstart = s_seg + Q;
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      const int j = xrow(k), pv = (tid + NTHR * k) % (P / VEC);
+      const float sc = c * Q + j < pb.L ? Elem<T>::exp(raw.acs[k]) : 0.f;
+      uint4 o;
+      if constexpr (sizeof(T) == 2) {
+        uint32_t u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(vget<T>(xr[k], 2 * e) * sc, vget<T>(xr[k], 2 * e + 1) * sc);
+        o = uint4{u[0], u[1], u[2], u[3]};
+      } else {
+        f32x4_t f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = vget<T>(xr[k], e) * sc;
+        o = __builtin_bit_cast(uint4, f);
+      }
+      if (xhas(k)) *reinterpret_cast<uint4*>(sx + Cf::XTile::at(j, pv * VEC)) = o;
+    }
+#pragma unroll
+    for (int k = 0; k < NBV; ++k) {
+      const int j = brow(k), nv = (tid + NTHR * k) % (NT / VEC);
+      if (bhas(k)) *reinterpret_cast<uint4*>(sb + Cf::BTile::at(j, nv * VEC)) = c * Q + j < pb.L ? br[k] : zero_u4();
+    }
+    const int start0 = seg_rank(raw.seg0);   // 1 when a sequence starts at position 0
+    Upd u;
+    u.decay = Elem<T>::exp(raw.acs_end);
+    u.nstart = raw.nstart;
+    u.nseg = raw.nstart + 1 - start0;
+    u.seqbase = raw.seqbase;
+    if (tid < Q) {
+      s_seg[tid] = raw.seg_own;
+      if (tid > 0 && seg_lo(raw.seg_own) == tid) s_segstart[seg_rank(raw.seg_own) - start0] = tid;
+    }
+    if (tid == 0) {
+      s_segstart[0] = 0;
+      s_segstart[u.nseg] = Q;
+    }
+    return u;
+  };
+
   f32x4_t dout[Cf::TPW];
 #pragma unroll
   for (int k = 0; k < Cf::TPW; ++k) dout[k] = zero4();
-
-  ChunkMeta cur, nxt;
-  cur.load(pb, b, h, pb.nc - 1);
-  load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, pb.nc - 1, xr, br);
-  for (int c = pb.nc - 1; c >= 0; --c) {
+  request(pb.nc - 1);
+  Upd cur = stage(pb.nc - 1, 0);
+  request(pb.nc - 2);
+  __syncthreads();
+  for (int c = pb.nc - 1, it = 0; c >= 0; --c, ++it) {
+    const int par = it & 1;
+    Upd nxt = cur;
+    if (c > 0) nxt = stage(c - 1, par ^ 1);   // (uniform)
+    request(c - 2);
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    if (tid < Q) {
-      s_e[tid] = Elem<T>::exp(cur.acs);
-      s_seg[tid] = cur.seg;
-    }
-    if (tid == 0) s_segstart[0] = 0;
-    __syncthreads();
-    const int nstart = cur.nstart;
-    const int start0 = seg_rank(s_seg[0]);  // 1 when a sequence starts at position 0
-    const int nseg = nstart + 1 - start0;
-    if (tid < Q && tid > 0 && seg_lo(cur.seg) == tid) s_segstart[seg_rank(cur.seg) - start0] = tid;
-    if (tid == 0) s_segstart[nseg] = Q;
-    stage_chunk_rows<T, Q, P, NT>(xr, br, s_e, s_dyt, s_ct);
-    __syncthreads();
-    if (c > 0) {
-      nxt.load(pb, b, h, c - 1);
-      load_chunk_rows<T, Q, P, NT>(pb, pb.dy, pb.Cm, b, h, g, n0, c - 1, xr, br);
-    }
-
-    const float decay = Elem<T>::exp(cur.acs_end);
+    const T* s_dyt = s_x0 + par * Bc::XSZ;
+    const T* s_ct = s_b0 + par * Bc::BSZ;
+    const int* s_seg = s_t0 + par * Bc::TSZ;
+    const int* s_segstart = s_seg + Q;
 #pragma unroll
     for (int k = 0; k < Cf::TPW; ++k) {
       const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const int n = n0 + nt * 16 + r16;
-
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           static_cast<T*>(pb.dstate)[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = Elem<T>::from_f(dout[k][r]);
-        if (nstart == 0) {
+        if (cur.nstart == 0) {
           f32x4_t R = zero4();
 #pragma unroll
           for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
             R = Mma<T>::mma(Cf::XTile::frag(s_dyt, pt * 16, k0), Cf::BTile::frag(s_ct, nt * 16, k0), R);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + decay * dout[k][r];
+          for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + cur.decay * dout[k][r];
         } else {
           f32x4_t dhoff = zero4();
-          for (int m = 0; m < nseg; ++m) {
+          for (int m = 0; m < cur.nseg; ++m) {
             const int lo = s_segstart[m], hi = s_segstart[m + 1];
             f32x4_t R = zero4();
             for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
@@ -378,7 +374,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
               for (int r = 0; r < 4; ++r) {
                 const int p = pt * 16 + 4 * kg + r;
                 float v = R[r];
-                if (hi == Q) v += decay * dout[k][r];
+                if (hi == Q) v += cur.decay * dout[k][r];
                 pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n] = v;
               }
             }
@@ -411,8 +407,17 @@ static hipError_t launch_state_t(const Problem& pb, bool fwd, hipStream_t s) {
       attr_set = true;
     }
     hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), lds, s, pb);
-  } else
-    hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), 0, s, pb);
+  } else {
+    constexpr size_t lds = StateBwdCfg<T, Q, P, NT>::LDS;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_state_bwd<T, Q, P, NT>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), lds, s, pb);
+  }
   return hipGetLastError();
 }
 
