@@ -25,8 +25,8 @@ METRIC = "SSD bwd ms/layer + tokens/s at L=16K (1 GPU); bitwise repeat + % roofl
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_head.hip", "ssd_device.h",
-                  "ssd_tiles.h", "ssd_problem.h"]
+KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_head.hip", "k_fwd.hip",
+                  "ssd_device.h", "ssd_tiles.h", "ssd_problem.h"]
 
 
 def sizes(w, ntg):
@@ -47,6 +47,7 @@ def sizes(w, ntg):
         SEG=w.batch * nc * w.chunk * 4,
         DCB=w.batch * w.ngroups * nc * w.chunk * w.chunk * s,      # dCB tile (or its transpose)
         CBT=w.batch * w.ngroups * nc * (w.chunk * (w.chunk + 16) // 2) * 4,   # causal C B^T tiles, fp32
+        CBT_FWD=w.batch * w.ngroups * nc * (w.chunk * (w.chunk + 16) // 2) * s,   # the forward's, I/O dtype
     )
     return z
 
@@ -66,6 +67,16 @@ def stage_alg_bytes(z):
         "dbdc": 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"] + 2 * z["DCB"],
         "head_bwd": 3 * z["X"] + z["BC"] + z["T"] + z["CBT"] + 2 * z["CH"] + z["OFFD"] + z["DT"],
         "reduce": 0,
+    }
+
+
+def forward_alg_bytes(z, fin):
+    """Per forward kernel (beyond the shared prep and state walk), each operand counted once;
+    fin = bytes of the final states written."""
+    return {
+        "fwd_cbf": 2 * z["BC"] + z["CBT_FWD"],
+        "fwd_y": 2 * z["X"] + z["BC"] + z["T"] + z["CBT_FWD"] + 2 * z["CH"],
+        "fwd_final": fin,
     }
 
 
@@ -103,7 +114,8 @@ def measured_traffic(workload, stage):
 # stage of each library kernel (kernel name prefix -> stage)
 STAGE_OF_KERNEL = [("k_head_bwd", "head_bwd"), ("k_state_fwd", "state_fwd"), ("k_state_bwd", "state_bwd"),
                    ("k_dcb<", "dcb"), ("k_dc<", "dbdc"), ("k_db<", "dbdc"), ("k_prep", "prep"),
-                   ("k_seqbase", "prep"), ("k_reduce", "reduce")]
+                   ("k_seqbase", "prep"), ("k_reduce", "reduce"),
+                   ("k_cbf<", "fwd_cbf"), ("k_y<", "fwd_y"), ("k_final<", "fwd_final"), ("k_seqstart", "fwd_final")]
 CALIB_BYTES = 1 << 28   # bytes read (and written) by one calibration copy
 
 
@@ -287,21 +299,28 @@ def main():
         step()
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in out.items()}
-    ev_steps = [ssd.make_stage_events(stream) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for k in range(args.steps):
-        step(ev_steps[k])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # per-stage times from a second pass of the same steps, with the library
+    # recording an event between stages (kept out of the timed region above)
+    nprof = min(args.steps, 50)
+    ev_steps = [ssd.make_stage_events(stream) for _ in range(nprof)]
+    torch.cuda.synchronize()
+    for k in range(nprof):
+        step(ev_steps[k])
+    torch.cuda.synchronize()
     stage_ms = {n: 0.0 for n in names}
     for evs in ev_steps:
         for i, n in enumerate(names):
-            stage_ms[n] += evs[i].elapsed_time(evs[i + 1]) / args.steps
+            stage_ms[n] += evs[i].elapsed_time(evs[i + 1]) / nprof
     bitwise = all(torch.equal(out[k].view(torch.uint8) if out[k].dtype != torch.bfloat16 else out[k].view(torch.int16),
                               ref[k].view(torch.uint8) if ref[k].dtype != torch.bfloat16 else ref[k].view(torch.int16))
                   for k in out)

@@ -243,6 +243,35 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     return {"y": y, "final_states": fin, "workspace": workspace, "shape": shape}
 
 
+class SsdChunkScan(torch.autograd.Function):
+    """The SSD layer as an autograd function: ``forward`` is ssd_fwd (y only)
+    and ``backward`` is ssd_bwd, which recomputes the chunk states from the
+    saved inputs, so nothing but the inputs is kept between the two."""
+
+    @staticmethod
+    def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, chunk_size, nseqs):
+        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs)["y"]
+        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx)
+        ctx.chunk_size, ctx.nseqs = chunk_size, nseqs
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, dt, A, B, C, D, h0, seq_idx = ctx.saved_tensors
+        want_h0 = h0 is not None and ctx.needs_input_grad[6]
+        g = ssd_bwd(x, dt, A, B, C, D, dy.contiguous(), h0, seq_idx, chunk_size=ctx.chunk_size, nseqs=ctx.nseqs,
+                    want_d_initial_states=want_h0)
+        return (g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"], g["dD"], g["d_initial_states"] if want_h0 else None,
+                None, None, None)
+
+
+def ssd_chunk_scan(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
+                   nseqs: Optional[int] = None) -> torch.Tensor:
+    """y of the SSD layer with autograd support (see SsdChunkScan); the
+    gradients reach x, dt, A, B, C, D and initial_states."""
+    return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size, nseqs)
+
+
 def workspace_view(result: dict, region: int) -> torch.Tensor:
     """A view of one workspace region of a finished call: Acs (float32), Hin or dS (I/O dtype)."""
     shape = result["shape"]

@@ -111,3 +111,31 @@ def test_forward_bitwise_repeatable_with_garbage_workspace():
         b = run_fwd(inputs, 256, True, fill="garbage")
         assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
         assert torch.equal(a["final_states"].view(torch.int32), b["final_states"].view(torch.int32))
+
+
+def test_autograd_function_matches_entry_points():
+    """ssd_chunk_scan: y is ssd_fwd's y, and y.backward(dy) leaves exactly
+    ssd_bwd's gradients (bitwise) in every input's .grad."""
+    w = Workload("bf16_autograd", batch=1, seqlen=700, nheads=8, headdim=64, ngroups=2, dstate=64, chunk=128,
+                 dtype="bf16", seed=51)
+    inputs = packed(make_inputs(w), [[250, 450]])
+    d = to_device(inputs)
+    h0 = d["initial_states"]
+    print("[case] autograd function", flush=True)
+    leaves = {k: d[k].clone().requires_grad_(True) for k in ("x", "dt", "A", "B", "C", "D")}
+    h0_leaf = h0.clone().requires_grad_(True)
+    y = ssd.ssd_chunk_scan(leaves["x"], leaves["dt"], leaves["A"], leaves["B"], leaves["C"], leaves["D"], h0_leaf,
+                           d["seq_idx"], chunk_size=128, nseqs=2)
+    y.backward(d["dy"])
+    torch.cuda.synchronize()
+    ref_y = ssd.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], h0, d["seq_idx"], chunk_size=128,
+                        nseqs=2)["y"]
+    ref = ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dy"], h0, d["seq_idx"], chunk_size=128,
+                      nseqs=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach().view(torch.int16), ref_y.view(torch.int16))
+    for k, gk in (("x", "dx"), ("B", "dB"), ("C", "dC")):
+        assert torch.equal(leaves[k].grad.view(torch.int16), ref[gk].view(torch.int16)), k
+    for k, gk in (("dt", "ddt"), ("A", "dA"), ("D", "dD")):
+        assert torch.equal(leaves[k].grad.view(torch.int32), ref[gk].view(torch.int32)), k
+    assert torch.equal(h0_leaf.grad.view(torch.int32), ref["d_initial_states"].view(torch.int32))
