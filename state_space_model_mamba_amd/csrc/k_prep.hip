@@ -20,7 +20,7 @@
 
 namespace ssd {
 
-constexpr int PREP_HEADS = 32;   // heads per block of k_prep
+constexpr int PREP_HEADS = 4;    // heads per block of k_prep
 
 template <int Q>
 __global__ __launch_bounds__(256) void k_prep(Problem pb) {
