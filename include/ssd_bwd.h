@@ -137,6 +137,46 @@ int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float*
             const int32_t* seq_idx, void* y, float* final_states,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Optional dt front-end of the layer, applied per (position, head) before the
+ * recurrence: with u = dt[b, t, h] + dt_bias[h] (dt_bias NULL: no bias),
+ *   v      = softplus(u) = ln(1 + e^u) for u <= 20, u above   (dt_softplus != 0)
+ *          = u                                               (dt_softplus == 0)
+ *   dt_eff = min(max(v, dt_min), dt_max)
+ * and dt_eff takes the place of dt in the recurrence stated above.  Pass
+ * dt_min = -INFINITY, dt_max = INFINITY for no clamp; dt_min <= dt_max, no NaN.
+ * The page "Deterministic bwd kernel for mamba2" times chunk_cumsum_bwd (its
+ * "Per-kernel breakdown" tables), the step's own backward, but no page states
+ * the activation; this is the usual parameterisation of the step in Mamba-2
+ * layers, and the synthetic workloads draw dt through it.
+ * Its gradient: d dt_eff / du = [dt_min <= v <= dt_max] * (dt_softplus ?
+ * sigmoid(u), or 1 for u > 20 : 1).
+ */
+typedef struct {
+  const float* dt_bias; /* (nheads) fp32 device pointer, or NULL */
+  int32_t dt_softplus;  /* nonzero: softplus after the bias */
+  float dt_min, dt_max; /* clamp of the activated value */
+} ssd_dt_frontend;
+
+/*
+ * ssd_fwd and ssd_bwd with the dt front-end above (`fe` NULL: none, the same
+ * as ssd_fwd / ssd_bwd).  `dt` is then the raw input and `ddt` the gradient
+ * with respect to it; `ddt_bias` (nheads, fp32, nullable; requires
+ * fe->dt_bias) receives the gradient with respect to dt_bias, summed over
+ * batch and positions in a fixed order.  Everything else is as for
+ * ssd_fwd / ssd_bwd, including the workspace size.
+ */
+int ssd_fwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+               const float* A, const void* B, const void* C, const float* D, const float* initial_states,
+               const int32_t* seq_idx, void* y, float* final_states,
+               void* workspace, size_t workspace_bytes, void* stream);
+int ssd_bwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+               const float* A, const void* B, const void* C, const float* D, const void* dy,
+               const float* initial_states, const int32_t* seq_idx,
+               void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+               float* d_initial_states, float* ddt_bias, void* workspace, size_t workspace_bytes,
+               void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);
 

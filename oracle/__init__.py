@@ -9,6 +9,7 @@ never imports it.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -163,6 +164,50 @@ class Oracle:
 
 
 _DEFAULT = Oracle()
+
+
+# --------------------------------------------------------------------------
+# dt front-end (an elementwise map in front of the recurrence; numpy fp64)
+# --------------------------------------------------------------------------
+def dt_frontend(dt, dt_bias=None, softplus=False, dt_limit=(-math.inf, math.inf)):
+    """The step the recurrence uses, from the raw dt (b, L, H), and its
+    derivative with respect to the raw dt, both in fp64:
+
+        u = dt + dt_bias[h];  v = ln(1 + e^u) (u itself above 20) if softplus else u;
+        dt_eff = clamp(v, dt_min, dt_max);  d dt_eff / du = [dt_min <= v <= dt_max] * (sigmoid(u) or 1)
+    """
+    u = _f64(dt)
+    if dt_bias is not None:
+        u = u + _f64(dt_bias)[None, None, :]
+    if softplus:
+        low = u <= 20.0
+        us = np.where(low, u, 0.0)
+        v = np.where(low, np.log1p(np.exp(us)), u)
+        d = np.where(low, 1.0 / (1.0 + np.exp(-us)), 1.0)
+    else:
+        v, d = u, np.ones_like(u)
+    lo, hi = float(dt_limit[0]), float(dt_limit[1])
+    inside = (v >= lo) & (v <= hi)
+    return np.clip(v, lo, hi), np.where(inside, d, 0.0)
+
+
+def forward_fe(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, dt_bias=None, dt_softplus=False,
+               dt_limit=(-math.inf, math.inf), **kw):
+    """forward() with the dt front-end applied to the raw dt."""
+    dt_eff, _ = dt_frontend(dt, dt_bias, dt_softplus, dt_limit)
+    return forward(x, dt_eff, A, B, C, D, initial_states, seq_idx, **kw)
+
+
+def backward_fe(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, dt_bias=None, dt_softplus=False,
+                dt_limit=(-math.inf, math.inf), **kw):
+    """backward() with the dt front-end: ddt is taken with respect to the raw
+    dt (chain rule through the elementwise map), and ddt_bias[h] is its sum
+    over batch and positions."""
+    dt_eff, d = dt_frontend(dt, dt_bias, dt_softplus, dt_limit)
+    g = backward(x, dt_eff, A, B, C, D, dy, initial_states, seq_idx, **kw)
+    g["ddt"] = g["ddt"] * d
+    g["ddt_bias"] = g["ddt"].sum(axis=(0, 1)) if dt_bias is not None else None
+    return g
 
 
 def forward(*args, **kw):

@@ -627,20 +627,45 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     float carry = __shfl_down(vl, 1, WAVE);
     if (l == WAVE - 1) carry = 0.f;
     int seen = 0;
-    float dap = 0.f;
+    float dap = 0.f, dbp = 0.f;
+    float da_k[R];
 #pragma unroll
     for (int e = R - 1; e >= 0; --e) {
       const int k = l * R + e;
       if (f[e]) seen = 1;
       const float rc = seen ? loc[e] : loc[e] + carry;
-      const float da = s_daint[k] + rc;
-      const float ddt = s_ddtp[k] + Ah * da;
-      const int t = c * Q + k;
-      if (t < pb.L) pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = ddt;
-      dap += s_dt[k] * da;
+      da_k[e] = s_daint[k] + rc;
+      dap += s_dt[k] * da_k[e];
+    }
+    if (!pb.fe) {   // (uniform) ddt with respect to the dt the recurrence uses
+#pragma unroll
+      for (int e = R - 1; e >= 0; --e) {
+        const int k = l * R + e, t = c * Q + k;
+        if (t < pb.L) pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = s_ddtp[k] + Ah * da_k[e];
+      }
+    } else {        // ... and on to the raw dt, through the front-end's derivative
+      float raw[R];
+#pragma unroll
+      for (int e = 0; e < R; ++e) {
+        const int t = min(c * Q + l * R + e, pb.L - 1);
+        raw[e] = pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h];
+      }
+#pragma unroll
+      for (int e = R - 1; e >= 0; --e) {
+        const int k = l * R + e, t = c * Q + k;
+        float dfdu;
+        dt_frontend(pb, raw[e], h, &dfdu);
+        const float ddt = (s_ddtp[k] + Ah * da_k[e]) * dfdu;
+        if (t < pb.L) {
+          pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = ddt;
+          dbp += ddt;
+        }
+      }
     }
     dap = wave_sum(dap);
+    if (pb.ddt_bias) dbp = wave_sum(dbp);
     if (l == 0) {
+      if (pb.ddt_bias) pb.slot_ddtb[bc * pb.H + h] = dbp;
       pb.slot_dA[bc * pb.H + h] = dap;
       float dd = 0.f;
       for (int k = 0; k < W; ++k) dd += s_red[k];

@@ -33,10 +33,15 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
   __shared__ float s_dt[Q * LDD];
 
   // this block's heads of the chunk's dt rows, coalesced (zeros past L and past H)
+  // (through the dt front-end when one is given; zeros stay zeros)
   for (int v = tid; v < Q * PREP_HEADS; v += 256) {
     const int i = v / PREP_HEADS, hh = v % PREP_HEADS, t = c * Q + i;
-    s_dt[i * LDD + hh] =
-        (t < pb.L && h0 + hh < pb.H) ? pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h0 + hh] : 0.f;
+    float d = 0.f;
+    if (t < pb.L && h0 + hh < pb.H) {
+      d = pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h0 + hh];
+      if (pb.fe) d = dt_frontend(pb, d, h0 + hh, nullptr);
+    }
+    s_dt[i * LDD + hh] = d;
   }
   if (tid < Q) {
     const int t = c * Q + tid;
@@ -157,16 +162,19 @@ __global__ __launch_bounds__(256) void k_reduce(Problem pb) {
   if (h >= pb.H) return;
   const int l = lane_id();
   const int n = pb.B * pb.nc;
-  double a = 0.0, d = 0.0;
+  double a = 0.0, d = 0.0, e = 0.0;
   for (int k = l; k < n; k += WAVE) {
     a += static_cast<double>(pb.slot_dA[static_cast<int64_t>(k) * pb.H + h]);
     d += static_cast<double>(pb.slot_dD[static_cast<int64_t>(k) * pb.H + h]);
+    if (pb.ddt_bias) e += static_cast<double>(pb.slot_ddtb[static_cast<int64_t>(k) * pb.H + h]);
   }
   a = wave_sum_f64(a);
   d = wave_sum_f64(d);
+  e = wave_sum_f64(e);
   if (l == 0) {
     pb.dA[h] = static_cast<float>(a);
     if (pb.dD) pb.dD[h] = static_cast<float>(d);
+    if (pb.ddt_bias) pb.ddt_bias[h] = static_cast<float>(e);
   }
 }
 

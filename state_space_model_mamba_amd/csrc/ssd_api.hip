@@ -12,7 +12,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, seqstart, total;
+  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_ddtb, seqstart,
+      total;
   int nc, ntg;
 };
 
@@ -70,6 +71,7 @@ Layout make_layout(const ssd_shape* s) {
   L.endd = take(B * H * nc * ntg * 4);
   L.slot_dA = take(B * nc * H * 4);
   L.slot_dD = take(B * nc * H * 4);
+  L.slot_ddtb = take(B * nc * H * 4);
   L.seqstart = take((s->nseqs > 0 ? s->nseqs : 1) * 4);
   L.total = off;
   L.nc = static_cast<int>(nc);
@@ -151,16 +153,37 @@ void fill_problem(const ssd_shape* shape, const Layout& L, void* workspace, ssd:
   pb.endd = reinterpret_cast<float*>(ws + L.endd);
   pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
   pb.slot_dD = reinterpret_cast<float*>(ws + L.slot_dD);
+  pb.slot_ddtb = reinterpret_cast<float*>(ws + L.slot_ddtb);
   pb.seqstart = reinterpret_cast<int32_t*>(ws + L.seqstart);
 }
 
-int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
-            const void* C, const float* D, const void* dy, const float* initial_states,
+// The dt front-end's fields of the problem (fe NULL: none).
+int fill_frontend(const ssd_dt_frontend* fe, ssd::Problem& pb) {
+  pb.fe = 0;
+  pb.dt_bias = nullptr;
+  pb.dt_softplus = 0;
+  pb.dt_min = -__builtin_inff();
+  pb.dt_max = __builtin_inff();
+  if (!fe) return SSD_OK;
+  if (!(fe->dt_min <= fe->dt_max)) return SSD_ERR_INVALID_ARG;   // (also rejects NaN)
+  if (fe->dt_bias && !aligned16(fe->dt_bias)) return SSD_ERR_MISALIGNED;
+  pb.dt_bias = fe->dt_bias;
+  pb.dt_softplus = fe->dt_softplus != 0;
+  pb.dt_min = fe->dt_min;
+  pb.dt_max = fe->dt_max;
+  pb.fe = pb.dt_bias || pb.dt_softplus || pb.dt_min > -__builtin_inff() || pb.dt_max < __builtin_inff();
+  return SSD_OK;
+}
+
+int run_bwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
+            const void* B, const void* C, const float* D, const void* dy, const float* initial_states,
             const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
-            float* d_initial_states, void* workspace, size_t workspace_bytes, void* stream,
+            float* d_initial_states, float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream,
             void* const* events) {
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (ddt_bias && !(fe && fe->dt_bias)) return SSD_ERR_INVALID_ARG;
+  if (ddt_bias && !aligned16(ddt_bias)) return SSD_ERR_MISALIGNED;
   if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !workspace)
     return SSD_ERR_INVALID_ARG;
   if (dD && !D) return SSD_ERR_INVALID_ARG;
@@ -179,10 +202,12 @@ int run_bwd(const ssd_shape* shape, const void* x, const float* dt, const float*
 
   ssd::Problem pb;
   fill_problem(shape, L, workspace, pb);
+  if ((rc = fill_frontend(fe, pb))) return rc;
   pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D; pb.dy = dy;
   pb.h0 = initial_states; pb.seq_idx = seq_idx;
   pb.dx = dx; pb.ddt = ddt; pb.dA = dA; pb.dB = dB; pb.dC = dC; pb.dD = dD;
   pb.dinit = d_initial_states;
+  pb.ddt_bias = ddt_bias;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = is_bf16(shape);
@@ -207,8 +232,17 @@ extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, c
                        const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
                        float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(shape, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
-                 d_initial_states, workspace, workspace_bytes, stream, nullptr);
+  return run_bwd(shape, nullptr, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, nullptr, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int ssd_bwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D, const void* dy,
+                          const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
+                          float* dA, void* dB, void* dC, float* dD, float* d_initial_states, float* ddt_bias,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(shape, fe, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, ddt_bias, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, const float* A,
@@ -218,13 +252,15 @@ extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const flo
                                 float* d_initial_states, void* workspace, size_t workspace_bytes,
                                 void* stream, void* const* events) {
   if (!events) return SSD_ERR_INVALID_ARG;
-  return run_bwd(shape, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
-                 d_initial_states, workspace, workspace_bytes, stream, events);
+  return run_bwd(shape, nullptr, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, nullptr, workspace, workspace_bytes, stream, events);
 }
 
-extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
-                       const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
-                       void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int run_fwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
+            const void* B, const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
+            void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!x || !dt || !A || !B || !C || !y || !workspace) return SSD_ERR_INVALID_ARG;
@@ -237,6 +273,7 @@ extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, c
   if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
   ssd::Problem pb;
   fill_problem(shape, L, workspace, pb);
+  if ((rc = fill_frontend(fe, pb))) return rc;
   pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D;
   pb.h0 = initial_states; pb.seq_idx = seq_idx;
   pb.y = y; pb.final = final_states;
@@ -247,6 +284,23 @@ extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, c
   if (final_states && ssd::launch_seqstart(pb, s) != hipSuccess) return SSD_ERR_HIP;
   if (ssd::launch_fwd_out(pb, bf16, s) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
+                       void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(shape, nullptr, x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace,
+                 workspace_bytes, stream);
+}
+
+extern "C" int ssd_fwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          const float* initial_states, const int32_t* seq_idx, void* y, float* final_states,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(shape, fe, x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace,
+                 workspace_bytes, stream);
 }
 
 extern "C" int ssd_bwd_stage_count(void) { return kStages; }

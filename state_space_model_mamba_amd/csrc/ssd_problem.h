@@ -42,6 +42,12 @@ struct Problem {
   void* dC;
   float* dD;
   float* dinit;
+  // dt front-end (fe = 0: dt is used as given)
+  int fe;                // nonzero when any of the three below applies
+  const float* dt_bias;  // (H) or nullptr
+  int dt_softplus;
+  float dt_min, dt_max;
+  float* ddt_bias;       // (H) output, nullable
   // forward outputs
   void* y;           // (B, L, H, P), I/O dtype
   float* final;      // (nseqs, H, P, N) fp32, nullable
@@ -60,8 +66,24 @@ struct Problem {
   float* endd;       // (B, H, nc, ntg)
   float* slot_dA;    // (B, nc, H)
   float* slot_dD;    // (B, nc, H)
+  float* slot_ddtb;  // (B, nc, H): dt_bias gradient partials
   int32_t* seqstart; // (nseqs): b * L + t of each sequence's first position (forward)
 };
+
+// The dt front-end of one raw value of head h: the activated, clamped dt and
+// (if dfdu) its derivative with respect to the raw value.  softplus(u) =
+// ln(1 + e^u), taken as u above 20, where the two agree to float precision.
+__device__ inline float dt_frontend(const Problem& pb, float raw, int h, float* dfdu) {
+  const float u = raw + (pb.dt_bias ? pb.dt_bias[h] : 0.f);
+  float v = u, d = 1.f;
+  if (pb.dt_softplus && u <= 20.f) {
+    v = log1pf(expf(u));
+    d = 1.f / (1.f + expf(-u));
+  }
+  const bool in = v >= pb.dt_min && v <= pb.dt_max;
+  if (dfdu) *dfdu = in ? d : 0.f;
+  return fminf(fmaxf(v, pb.dt_min), pb.dt_max);
+}
 
 // Launchers (defined next to their kernels).  Return hipSuccess or the
 // launch error.  io_bf16 selects the bf16 (true) or fp32 instantiation.

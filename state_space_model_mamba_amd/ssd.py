@@ -8,6 +8,7 @@ library's kernels.  Raises if the library is missing or returns an error.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -21,7 +22,8 @@ SSD_IO_F32 = 1
 SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
-            "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd")
+            "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd",
+            "ssd_fwd_fe", "ssd_bwd_fe")
 
 
 class SsdShape(ctypes.Structure):
@@ -29,6 +31,11 @@ class SsdShape(ctypes.Structure):
                 ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
                 ("chunk_size", ctypes.c_int64), ("nseqs", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SsdDtFrontend(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
 
 
 class SsdError(RuntimeError):
@@ -65,6 +72,11 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_profiled.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp, ctypes.POINTER(vp)]
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+    fp = ctypes.POINTER(SsdDtFrontend)
+    lib.ssd_fwd_fe.restype = ctypes.c_int
+    lib.ssd_fwd_fe.argtypes = [sp, fp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
+    lib.ssd_bwd_fe.restype = ctypes.c_int
+    lib.ssd_bwd_fe.argtypes = [sp, fp] + [vp] * 18 + [ctypes.c_size_t, vp]
     lib.ssd_bwd_stage_count.restype = ctypes.c_int
     lib.ssd_bwd_stage_count.argtypes = []
     lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
@@ -116,6 +128,15 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _frontend(dt_bias, dt_softplus, dt_limit, H, dev):
+    """The C front-end struct, or None when it would change nothing."""
+    lo, hi = float(dt_limit[0]), float(dt_limit[1])
+    if dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf:
+        return None
+    _check(dt_bias, "dt_bias", torch.float32, (H,), dev)
+    return SsdDtFrontend(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi)
+
+
 def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -125,7 +146,8 @@ def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
 
 def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_d_initial_states: bool = True,
-            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None):
+            workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None,
+            dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf)):
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
@@ -135,6 +157,9 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states.
     ``events``: optional list of stage_count() + 1 recorded torch.cuda.Event
     (timing enabled) handed to the profiling entry point.
+    ``dt_bias`` (H,) fp32, ``dt_softplus`` and ``dt_limit`` = (min, max): the dt
+    front-end of include/ssd_bwd.h (dt is then the raw input); with dt_bias the
+    dict also holds ddt_bias.
     """
     lib = load_library()
     dev = x.device
@@ -162,6 +187,9 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     _check(D, "D", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
+    fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
+    if fe is not None and events is not None:
+        raise ValueError("stage events are not available with the dt front-end")
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)
     if workspace is None or workspace.numel() < nbytes:
@@ -181,7 +209,11 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
             _ptr(out["d_initial_states"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
             ctypes.c_void_p(stream)]
-    if events is None:
+    if fe is not None:
+        if dt_bias is not None and out.get("ddt_bias") is None:
+            out["ddt_bias"] = torch.empty((H,), dtype=torch.float32, device=dev)
+        rc = lib.ssd_bwd_fe(args[0], ctypes.byref(fe), *args[1:17], _ptr(out.get("ddt_bias")), *args[17:])
+    elif events is None:
         rc = lib.ssd_bwd(*args)
     else:
         handles = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
@@ -196,12 +228,14 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
 
 def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_final_states: bool = False,
-            workspace: Optional[torch.Tensor] = None):
+            workspace: Optional[torch.Tensor] = None, dt_bias=None, dt_softplus: bool = False,
+            dt_limit=(-math.inf, math.inf)):
     """The SSD layer's forward, computed by libssd_bwd: y, and optionally the
     state after each sequence's last position.
 
-    Same argument conventions as ssd_bwd.  Returns a dict with y (the I/O
-    dtype, shaped like x) and final_states ((S, H, P, N) fp32, or None).
+    Same argument conventions as ssd_bwd (including the dt front-end).
+    Returns a dict with y (the I/O dtype, shaped like x) and final_states
+    ((S, H, P, N) fp32, or None).
     """
     lib = load_library()
     dev = x.device
@@ -228,6 +262,7 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     _check(D, "D", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
+    fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)
     if workspace is None or workspace.numel() < nbytes:
@@ -235,9 +270,12 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     y = torch.empty_like(x)
     fin = (torch.empty((S, H, P, N), dtype=torch.float32, device=dev) if want_final_states and S > 0 else None)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssd_fwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                     _ptr(initial_states), _ptr(seq_idx), _ptr(y), _ptr(fin), _ptr(workspace),
-                     ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states), _ptr(seq_idx),
+            _ptr(y), _ptr(fin), _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)]
+    if fe is None:
+        rc = lib.ssd_fwd(ctypes.byref(shape), *args)
+    else:
+        rc = lib.ssd_fwd_fe(ctypes.byref(shape), ctypes.byref(fe), *args)
     if rc:
         raise SsdError(rc, "ssd_fwd")
     return {"y": y, "final_states": fin, "workspace": workspace, "shape": shape}
@@ -249,27 +287,32 @@ class SsdChunkScan(torch.autograd.Function):
     saved inputs, so nothing but the inputs is kept between the two."""
 
     @staticmethod
-    def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, chunk_size, nseqs):
-        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs)["y"]
-        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx)
-        ctx.chunk_size, ctx.nseqs = chunk_size, nseqs
+    def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, chunk_size, nseqs, dt_softplus,
+                dt_limit):
+        fe = dict(dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit)
+        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs, **fe)["y"]
+        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias)
+        ctx.chunk_size, ctx.nseqs, ctx.dt_softplus, ctx.dt_limit = chunk_size, nseqs, dt_softplus, dt_limit
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, dt, A, B, C, D, h0, seq_idx = ctx.saved_tensors
+        x, dt, A, B, C, D, h0, seq_idx, dt_bias = ctx.saved_tensors
         want_h0 = h0 is not None and ctx.needs_input_grad[6]
         g = ssd_bwd(x, dt, A, B, C, D, dy.contiguous(), h0, seq_idx, chunk_size=ctx.chunk_size, nseqs=ctx.nseqs,
-                    want_d_initial_states=want_h0)
+                    want_d_initial_states=want_h0, dt_bias=dt_bias, dt_softplus=ctx.dt_softplus,
+                    dt_limit=ctx.dt_limit)
         return (g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"], g["dD"], g["d_initial_states"] if want_h0 else None,
-                None, None, None)
+                None, g.get("ddt_bias"), None, None, None, None)
 
 
 def ssd_chunk_scan(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
-                   nseqs: Optional[int] = None) -> torch.Tensor:
+                   nseqs: Optional[int] = None, dt_bias=None, dt_softplus: bool = False,
+                   dt_limit=(-math.inf, math.inf)) -> torch.Tensor:
     """y of the SSD layer with autograd support (see SsdChunkScan); the
-    gradients reach x, dt, A, B, C, D and initial_states."""
-    return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size, nseqs)
+    gradients reach x, dt, A, B, C, D, initial_states and dt_bias."""
+    return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, chunk_size, nseqs, dt_softplus,
+                              tuple(dt_limit))
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:

@@ -121,3 +121,22 @@ def test_version_and_status_strings():
     assert v >> 16 >= 1
     assert ssd.status_string(0) == "ok"
     assert ssd.status_string(-99) == "unknown status"
+
+
+def test_frontend_argument_errors_are_reported_before_launch():
+    lib = ssd.load_library()
+    s = shape()
+    names = ["x", "dt", "A", "B", "C", "D", "dy", "h0", "seq_idx", "dx", "ddt", "dA", "dB", "dC", "dD", "dinit"]
+
+    def call(fe, ddt_bias=None):
+        args = [ctypes.c_void_p(FAKE.get(n)) if FAKE.get(n) else None for n in names]
+        return lib.ssd_bwd_fe(ctypes.byref(s), ctypes.byref(fe) if fe is not None else None, *args,
+                              ctypes.c_void_p(ddt_bias) if ddt_bias else None, ctypes.c_void_p(FAKE["ws"]),
+                              ctypes.c_size_t(1 << 40), None)
+
+    inf = float("inf")
+    assert call(ssd.SsdDtFrontend(None, 1, 0.5, 0.1)) == -1            # dt_min > dt_max
+    assert call(ssd.SsdDtFrontend(None, 1, float("nan"), inf)) == -1   # NaN bound
+    assert call(ssd.SsdDtFrontend(None, 1, -inf, inf), ddt_bias=0x990000) == -1   # ddt_bias without dt_bias
+    assert call(None, ddt_bias=0x990000) == -1
+    assert call(ssd.SsdDtFrontend(0x990008, 1, -inf, inf)) == -4       # misaligned dt_bias
