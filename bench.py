@@ -241,6 +241,33 @@ def measure_forward(torch, ssd, w, d, S, ws, z, steps, warmup):
             "bitwise_repeat": bitwise}
 
 
+def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup):
+    """ssd_bwd with the dt front-end (the raw draws, dt_bias, softplus) on the same workload:
+    the same step as the headline plus the activation and the dt_bias gradient."""
+    out = {}
+
+    def call():
+        return ssd.ssd_bwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["dy"],
+                           initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
+                           nseqs=S, workspace=ws, dt_bias=d["dt_bias"], dt_softplus=True)
+    for _ in range(warmup):
+        ref = call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        last = call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    same = all(torch.equal(ref[k].view(torch.int16) if ref[k].dtype == torch.bfloat16 else ref[k].view(torch.int32),
+                           last[k].view(torch.int16) if last[k].dtype == torch.bfloat16 else last[k].view(torch.int32))
+               for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias"))
+    return {"ms_per_step": ms, "tokens_per_s": w.tokens / (ms * 1e-3), "steps": steps, "warmup": warmup,
+            "bitwise_repeat": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,7 +275,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-forward", action="store_true", help="skip the forward (ssd_fwd) measurement")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip the forward (ssd_fwd) and the dt front-end measurements")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -364,6 +392,8 @@ def main():
     if not args.no_forward:
         res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=min(args.steps, 100),
                                          warmup=min(args.warmup, 10))
+        res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=min(args.steps, 100),
+                                                            warmup=min(args.warmup, 10))
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:

@@ -57,8 +57,8 @@ struct HeadCfg {
   static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(P) * LDSN) * sizeof(T);  // x, dy, dS rows
   // da shares: [column tile J][position]
   static constexpr size_t RS_FLOATS = size_t(T16) * Q;
-  // vectors: acs dt w ee ddacs ddtp sj dd daint er (10 Q floats) + seg (Q ints) + red (W + 8)
-  static constexpr size_t RV_FLOATS = size_t(11) * Q + W + 8;
+  // vectors: acs dt w ee ddacs ddtp sj dd daint er dfe (11 Q floats) + seg (Q ints) + red (W + 8)
+  static constexpr size_t RV_FLOATS = size_t(12) * Q + W + 8;
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
@@ -391,7 +391,8 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   float* s_dd = s_sj + Q;
   float* s_daint = s_dd + Q;
   float* s_er = s_daint + Q;
-  int* s_seg = reinterpret_cast<int*>(s_er + Q);
+  float* s_dfe = s_er + Q;
+  int* s_seg = reinterpret_cast<int*>(s_dfe + Q);
   float* s_red = reinterpret_cast<float*>(s_seg + Q);
 
   const int hh = static_cast<int>(lb % pb.hpg);
@@ -409,11 +410,12 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
 
   // per-position metadata (thread tid owns position tid), loaded first so
   // that the bulk loads below do not delay it
-  float acs_i = 0.f, dt_i = 0.f, offd_i = 0.f;
+  float acs_i = 0.f, dt_i = 0.f, offd_i = 0.f, dfe_i = 1.f;
   int seg_i = 0;
   if (tid < Q) {
     acs_i = pb.acs[bhc * Q + tid];
     dt_i = pb.dtc[bhc * Q + tid];
+    if (pb.fe) dfe_i = pb.dfe[bhc * Q + tid];
     seg_i = pb.segpos[bc * Q + tid];
     for (int nt = 0; nt < pb.ntg; ++nt) offd_i += pb.offd[(bhc * pb.ntg + nt) * Q + tid];
   }
@@ -450,6 +452,7 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     s_ee[tid] = e;
     s_w[tid] = e * dt_i;
     s_er[tid] = uniform ? Elem<T>::exp(acs_i - acs_tile0) : 0.f;
+    s_dfe[tid] = dfe_i;
   }
 
   // ---- phase B: x, dy rows; decays; M; ddt_intra; da shares; dx_intra
@@ -644,18 +647,10 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
         if (t < pb.L) pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = s_ddtp[k] + Ah * da_k[e];
       }
     } else {        // ... and on to the raw dt, through the front-end's derivative
-      float raw[R];
-#pragma unroll
-      for (int e = 0; e < R; ++e) {
-        const int t = min(c * Q + l * R + e, pb.L - 1);
-        raw[e] = pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h];
-      }
 #pragma unroll
       for (int e = R - 1; e >= 0; --e) {
         const int k = l * R + e, t = c * Q + k;
-        float dfdu;
-        dt_frontend(pb, raw[e], h, &dfdu);
-        const float ddt = (s_ddtp[k] + Ah * da_k[e]) * dfdu;
+        const float ddt = (s_ddtp[k] + Ah * da_k[e]) * s_dfe[k];
         if (t < pb.L) {
           pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = ddt;
           dbp += ddt;

@@ -31,17 +31,19 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
   const int tid = threadIdx.x;
   __shared__ int s_flag[Q], s_lo[Q], s_rank[Q];
   __shared__ float s_dt[Q * LDD];
+  __shared__ float s_dfe[Q * LDD];   // (with a dt front-end) its derivative
 
   // this block's heads of the chunk's dt rows, coalesced (zeros past L and past H)
   // (through the dt front-end when one is given; zeros stay zeros)
   for (int v = tid; v < Q * PREP_HEADS; v += 256) {
     const int i = v / PREP_HEADS, hh = v % PREP_HEADS, t = c * Q + i;
-    float d = 0.f;
+    float d = 0.f, dfdu = 0.f;
     if (t < pb.L && h0 + hh < pb.H) {
       d = pb.dt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h0 + hh];
-      if (pb.fe) d = dt_frontend(pb, d, h0 + hh, nullptr);
+      if (pb.fe) d = dt_frontend(pb, d, h0 + hh, &dfdu);
     }
     s_dt[i * LDD + hh] = d;
+    if (pb.fe) s_dfe[i * LDD + hh] = dfdu;
   }
   if (tid < Q) {
     const int t = c * Q + tid;
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
       const double acs = fl ? v : carry + v;
       pb.acs[out + i] = static_cast<float>(acs);
       pb.dtc[out + i] = d;
+      if (pb.fe) pb.dfe[out + i] = s_dfe[i * LDD + hh];
       carry = __shfl(acs, WAVE - 1, WAVE);
     }
   }

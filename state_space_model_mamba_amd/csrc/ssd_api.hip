@@ -12,7 +12,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_ddtb, seqstart,
+  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_ddtb, seqstart,
       total;
   int nc, ntg;
 };
@@ -61,6 +61,7 @@ Layout make_layout(const ssd_shape* s) {
   L.cinfo = take(B * nc * ssd::CINFO * 4);
   L.acs = take(B * H * nc * Q * 4);
   L.dtc = take(B * H * nc * Q * 4);
+  L.dfe = take(B * H * nc * Q * 4);
   const size_t es = is_bf16(s) ? 2 : 4;
   L.hin = take(B * H * nc * P * N * es);
   L.dstate = take(B * H * nc * P * N * es);
@@ -144,6 +145,7 @@ void fill_problem(const ssd_shape* shape, const Layout& L, void* workspace, ssd:
   pb.cinfo = reinterpret_cast<int32_t*>(ws + L.cinfo);
   pb.acs = reinterpret_cast<float*>(ws + L.acs);
   pb.dtc = reinterpret_cast<float*>(ws + L.dtc);
+  pb.dfe = reinterpret_cast<float*>(ws + L.dfe);
   pb.hin = ws + L.hin;
   pb.dstate = ws + L.dstate;
   pb.dcb = ws + L.dcb;

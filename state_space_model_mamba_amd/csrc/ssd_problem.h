@@ -56,6 +56,7 @@ struct Problem {
   int32_t* cinfo;    // (B, nc, CINFO)
   float* acs;        // (B, H, nc, Q)
   float* dtc;        // (B, H, nc, Q)
+  float* dfe;        // (B, H, nc, Q): d dtc / d raw dt (written and read only with a dt front-end)
   void* hin;         // (B, H, nc, P, N), I/O dtype
   void* dstate;      // (B, H, nc, P, N), I/O dtype
   void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB

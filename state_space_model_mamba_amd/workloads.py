@@ -98,7 +98,8 @@ def seq_idx_from_lengths(lengths: list[int]) -> torch.Tensor:
 
 
 def make_inputs(w: Workload, lengths: Optional[list[int]] = None) -> dict:
-    """CPU tensors: x, dt, A, B, C, D, dy (+ initial_states, seq_idx when packed).
+    """CPU tensors: x, dt, A, B, C, D, dy (+ initial_states, seq_idx when packed), and
+    dt_raw, dt_bias: the draws dt is formed from (dt = softplus(dt_raw + dt_bias)).
 
     x/B/C/dy are in the workload's I/O dtype, dt/A/D/initial_states are fp32,
     seq_idx int32.  ``lengths`` overrides the drawn packed lengths.
@@ -121,7 +122,9 @@ def make_inputs(w: Workload, lengths: Optional[list[int]] = None) -> dict:
     A = (-torch.exp(u_A)).to(torch.float32).contiguous()
     out = {"x": _round(x, io), "dt": dt, "A": A, "B": _round(Bm, io), "C": _round(Cm, io),
            "D": D.to(torch.float32).contiguous(), "dy": _round(dy, io),
-           "initial_states": None, "seq_idx": None}
+           "initial_states": None, "seq_idx": None,
+           # the same step before its front-end: dt = softplus(dt_raw + dt_bias)
+           "dt_raw": z.to(torch.float32).contiguous(), "dt_bias": dt_bias.contiguous()}
     if w.nseqs_packed:
         if b != 1:
             raise ValueError("packed workloads use batch 1")
