@@ -159,22 +159,34 @@ typedef struct {
 } ssd_dt_frontend;
 
 /*
- * ssd_fwd and ssd_bwd with the dt front-end above (`fe` NULL: none, the same
- * as ssd_fwd / ssd_bwd).  `dt` is then the raw input and `ddt` the gradient
- * with respect to it; `ddt_bias` (nheads, fp32, nullable; requires
- * fe->dt_bias) receives the gradient with respect to dt_bias, summed over
- * batch and positions in a fixed order.  Everything else is as for
- * ssd_fwd / ssd_bwd, including the workspace size.
+ * ssd_fwd and ssd_bwd extended with the dt front-end above (`fe` NULL: none)
+ * and an output gate (`z` NULL: none).  With a front-end, `dt` is the raw
+ * input and `ddt` the gradient with respect to it; `ddt_bias` (nheads, fp32,
+ * nullable; requires fe->dt_bias) receives the gradient with respect to
+ * dt_bias, summed over batch and positions in a fixed order.
+ *
+ * The gate z (batch, seqlen, nheads, headdim) in the I/O dtype multiplies
+ * the layer's output by silu(z) = z sigmoid(z):  out = y * silu(z), y as
+ * above (D term included).  ssd_bwd_ex then takes `dy` as the gradient of
+ * `out` and writes `dz` (same shape and dtype as z; required with z):
+ *   dz = dy * y * sigmoid(z) (1 + z (1 - sigmoid(z))),
+ * and the gradients of everything else through dy * silu(z).  y is
+ * recomputed from the inputs.  The gated dy is held, rounded to the I/O
+ * dtype, in the dx buffer until dx overwrites it.
+ *
+ * The gate is not on the pages either: it is the output gate of the usual
+ * Mamba-2 layer, the second half of the same "next" step as the front-end.
+ * Everything else is as for ssd_fwd / ssd_bwd, including the workspace size.
  */
-int ssd_fwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
-               const float* A, const void* B, const void* C, const float* D, const float* initial_states,
-               const int32_t* seq_idx, void* y, float* final_states,
+int ssd_fwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+               const float* A, const void* B, const void* C, const float* D, const void* z,
+               const float* initial_states, const int32_t* seq_idx, void* y, float* final_states,
                void* workspace, size_t workspace_bytes, void* stream);
-int ssd_bwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
-               const float* A, const void* B, const void* C, const float* D, const void* dy,
+int ssd_bwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+               const float* A, const void* B, const void* C, const float* D, const void* z, const void* dy,
                const float* initial_states, const int32_t* seq_idx,
                void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
-               float* d_initial_states, float* ddt_bias, void* workspace, size_t workspace_bytes,
+               float* d_initial_states, float* ddt_bias, void* dz, void* workspace, size_t workspace_bytes,
                void* stream);
 
 /* Static description of a status code (never NULL). */

@@ -220,3 +220,39 @@ def backward(*args, **kw):
 
 def count_sequences(*args, **kw):
     return _DEFAULT.count_sequences(*args, **kw)
+
+
+# --------------------------------------------------------------------------
+# output gate (an elementwise map after the layer; numpy fp64)
+# --------------------------------------------------------------------------
+def silu(z):
+    """silu(z) = z sigmoid(z) and its derivative sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    z = _f64(z)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return z * s, s * (1.0 + z * (1.0 - s))
+
+
+def forward_ex(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, z=None, return_final_states=False,
+               **kw):
+    """forward_fe() (dt front-end keywords included) times silu(z) when z is given."""
+    res = forward_fe(x, dt, A, B, C, D, initial_states, seq_idx, return_final_states=return_final_states, **kw)
+    if z is None:
+        return res
+    y, fs = res if return_final_states else (res, None)
+    g, _ = silu(z)
+    return (y * g, fs) if return_final_states else y * g
+
+
+def backward_ex(x, dt, A, B, C, D, dout, initial_states=None, seq_idx=None, z=None, **kw):
+    """backward_fe() for the output out = y silu(z): dout is the gradient of
+    out, so the layer sees dy = dout silu(z), and dz = dout y silu'(z) with y
+    the ungated output."""
+    if z is None:
+        return backward_fe(x, dt, A, B, C, D, dout, initial_states, seq_idx, **kw)
+    fe = {k: kw[k] for k in ("dt_bias", "dt_softplus", "dt_limit") if k in kw}
+    y = forward_fe(x, dt, A, B, C, D, initial_states, seq_idx, **fe)
+    g, dg = silu(z)
+    dout = _f64(dout)
+    res = backward_fe(x, dt, A, B, C, D, dout * g, initial_states, seq_idx, **kw)
+    res["dz"] = dout * y * dg
+    return res

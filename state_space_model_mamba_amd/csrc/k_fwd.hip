@@ -10,6 +10,8 @@
 //               tiles in the output kernel's (wave, tile) order
 //   k_y         y_i = sum_{j <= i, same segment} CB[i,j] exp(Acs_i - Acs_j) dt_j x_j
 //                     + exp(Acs_i) C_i . E_seg(i)  +  D x_i
+//               (times silu(z_i) with an output gate; in the backward's gate
+//               pass it writes dout silu(z) and dz instead of y)
 //               per (batch, head, chunk); E is the state entering row i's
 //               segment: Hin_c when the segment continues the chunk's
 //               sequence, h0[s] when it starts sequence s
@@ -481,7 +483,9 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
     else
       y_tiles<T, Q, P, NS, false>(cb, ya, yb, s_x, s_acs, s_dt, s_ejdt, s_seg, w, l);
 
-    // ---- epilogue: y = intra + state + D x
+    // ---- epilogue: y = intra + state + D x, then the output gate if any:
+    // forward, y silu(z); gate pass (dz given), the gated dy = dout silu(z)
+    // into y's place and dz = dout y silu'(z)
     const float Dv = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -493,10 +497,33 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
       for (int pt = 0; pt < PT; ++pt) {
         const f32x4_t yv = a ? yb[pt] : ya[pt];
         const f32x4_t xv = load4f<T>(s_x + i * LDX + 16 * pt + 4 * kg);
+        const int64_t off = row + 16 * pt + 4 * kg;
         f32x4_t o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = yv[r] + Dv * xv[r];
-        store4f<T>(static_cast<T*>(pb.y) + row + 16 * pt + 4 * kg, o);
+        if (!pb.z) {   // (uniform)
+          store4f<T>(static_cast<T*>(pb.y) + off, o);
+          continue;
+        }
+        const f32x4_t zv = load4f<T>(static_cast<const T*>(pb.z) + off);
+        f32x4_t sg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sg[r] = 1.f / (1.f + expf(-zv[r]));
+        if (!pb.dz) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] *= zv[r] * sg[r];
+          store4f<T>(static_cast<T*>(pb.y) + off, o);
+        } else {
+          const f32x4_t dv = load4f<T>(static_cast<const T*>(pb.dout) + off);
+          f32x4_t dyv, dzv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dyv[r] = dv[r] * zv[r] * sg[r];
+            dzv[r] = dv[r] * o[r] * sg[r] * (1.f + zv[r] * (1.f - sg[r]));
+          }
+          store4f<T>(static_cast<T*>(pb.y) + off, dyv);
+          store4f<T>(static_cast<T*>(pb.dz) + off, dzv);
+        }
       }
     }
   }

@@ -178,14 +178,17 @@ int fill_frontend(const ssd_dt_frontend* fe, ssd::Problem& pb) {
 }
 
 int run_bwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
-            const void* B, const void* C, const float* D, const void* dy, const float* initial_states,
-            const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
-            float* d_initial_states, float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream,
-            void* const* events) {
+            const void* B, const void* C, const float* D, const void* z, const void* dy,
+            const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB,
+            void* dC, float* dD, float* d_initial_states, float* ddt_bias, void* dz, void* workspace,
+            size_t workspace_bytes, void* stream, void* const* events) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (ddt_bias && !(fe && fe->dt_bias)) return SSD_ERR_INVALID_ARG;
-  if (ddt_bias && !aligned16(ddt_bias)) return SSD_ERR_MISALIGNED;
+  if ((z != nullptr) != (dz != nullptr)) return SSD_ERR_INVALID_ARG;
+  if (z && (z == dx || dz == dx || dz == dy)) return SSD_ERR_INVALID_ARG;   // dx holds the gated dy
+  for (const void* p : {static_cast<const void*>(ddt_bias), z, static_cast<const void*>(dz)})
+    if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
   if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !workspace)
     return SSD_ERR_INVALID_ARG;
   if (dD && !D) return SSD_ERR_INVALID_ARG;
@@ -219,6 +222,14 @@ int run_bwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, co
   if (!mark(0)) return SSD_ERR_HIP;
   if (ssd::launch_prep(pb, s) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
   if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
+  if (z) {
+    // gate pass: recompute y, write the gated dy into dx's place and dz; the
+    // stages below read dy from there
+    ssd::Problem pg = pb;
+    pg.z = z; pg.dout = dy; pg.dz = dz; pg.y = dx;
+    if (ssd::launch_fwd_out(pg, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+    pb.dy = dx;
+  }
   if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess || !mark(3)) return SSD_ERR_HIP;
   if (ssd::launch_dcb(pb, bf16, s) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
   if (ssd::launch_dbdc(pb, bf16, s) != hipSuccess || !mark(5)) return SSD_ERR_HIP;
@@ -234,17 +245,17 @@ extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, c
                        const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
                        float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(shape, nullptr, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
-                 d_initial_states, nullptr, workspace, workspace_bytes, stream, nullptr);
+  return run_bwd(shape, nullptr, x, dt, A, B, C, D, nullptr, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC,
+                 dD, d_initial_states, nullptr, nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
-extern "C" int ssd_bwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
-                          const float* A, const void* B, const void* C, const float* D, const void* dy,
-                          const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
-                          float* dA, void* dB, void* dC, float* dD, float* d_initial_states, float* ddt_bias,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(shape, fe, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
-                 d_initial_states, ddt_bias, workspace, workspace_bytes, stream, nullptr);
+extern "C" int ssd_bwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D, const void* z,
+                          const void* dy, const float* initial_states, const int32_t* seq_idx, void* dx,
+                          float* ddt, float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
+                          float* ddt_bias, void* dz, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(shape, fe, x, dt, A, B, C, D, z, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, ddt_bias, dz, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, const float* A,
@@ -254,17 +265,19 @@ extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const flo
                                 float* d_initial_states, void* workspace, size_t workspace_bytes,
                                 void* stream, void* const* events) {
   if (!events) return SSD_ERR_INVALID_ARG;
-  return run_bwd(shape, nullptr, x, dt, A, B, C, D, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
-                 d_initial_states, nullptr, workspace, workspace_bytes, stream, events);
+  return run_bwd(shape, nullptr, x, dt, A, B, C, D, nullptr, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC,
+                 dD, d_initial_states, nullptr, nullptr, workspace, workspace_bytes, stream, events);
 }
 
 namespace {
 
 int run_fwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
-            const void* B, const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
-            void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+            const void* B, const void* C, const float* D, const void* z, const float* initial_states,
+            const int32_t* seq_idx, void* y, float* final_states, void* workspace, size_t workspace_bytes,
+            void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (z && !aligned16(z)) return SSD_ERR_MISALIGNED;
   if (!x || !dt || !A || !B || !C || !y || !workspace) return SSD_ERR_INVALID_ARG;
   if (!seq_idx && (initial_states || final_states) && shape->nseqs != shape->batch) return SSD_ERR_INVALID_ARG;
   if ((initial_states || final_states) && shape->nseqs < 1) return SSD_ERR_INVALID_ARG;
@@ -278,7 +291,7 @@ int run_fwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, co
   if ((rc = fill_frontend(fe, pb))) return rc;
   pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D;
   pb.h0 = initial_states; pb.seq_idx = seq_idx;
-  pb.y = y; pb.final = final_states;
+  pb.y = y; pb.final = final_states; pb.z = z;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = is_bf16(shape);
   if (ssd::launch_prep(pb, s) != hipSuccess) return SSD_ERR_HIP;
@@ -293,15 +306,15 @@ int run_fwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, co
 extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, const float* initial_states, const int32_t* seq_idx,
                        void* y, float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_fwd(shape, nullptr, x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace,
+  return run_fwd(shape, nullptr, x, dt, A, B, C, D, nullptr, initial_states, seq_idx, y, final_states, workspace,
                  workspace_bytes, stream);
 }
 
-extern "C" int ssd_fwd_fe(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
-                          const float* A, const void* B, const void* C, const float* D,
+extern "C" int ssd_fwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D, const void* z,
                           const float* initial_states, const int32_t* seq_idx, void* y, float* final_states,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return run_fwd(shape, fe, x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace,
+  return run_fwd(shape, fe, x, dt, A, B, C, D, z, initial_states, seq_idx, y, final_states, workspace,
                  workspace_bytes, stream);
 }
 

@@ -48,6 +48,11 @@ struct Problem {
   int dt_softplus;
   float dt_min, dt_max;
   float* ddt_bias;       // (H) output, nullable
+  // output gate (nullable): out = y silu(z); the backward's gate pass reads
+  // dout and writes the gated dy into y's place (the dx buffer) and dz
+  const void* z;     // (B, L, H, P), I/O dtype
+  const void* dout;  // gate pass only: the gradient of the gated output
+  void* dz;          // gate pass only
   // forward outputs
   void* y;           // (B, L, H, P), I/O dtype
   float* final;      // (nseqs, H, P, N) fp32, nullable

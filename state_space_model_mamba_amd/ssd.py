@@ -23,7 +23,7 @@ SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
             "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd",
-            "ssd_fwd_fe", "ssd_bwd_fe")
+            "ssd_fwd_ex", "ssd_bwd_ex")
 
 
 class SsdShape(ctypes.Structure):
@@ -73,10 +73,10 @@ def load_library(path: str = LIBRARY):
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
     fp = ctypes.POINTER(SsdDtFrontend)
-    lib.ssd_fwd_fe.restype = ctypes.c_int
-    lib.ssd_fwd_fe.argtypes = [sp, fp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
-    lib.ssd_bwd_fe.restype = ctypes.c_int
-    lib.ssd_bwd_fe.argtypes = [sp, fp] + [vp] * 18 + [ctypes.c_size_t, vp]
+    lib.ssd_fwd_ex.restype = ctypes.c_int
+    lib.ssd_fwd_ex.argtypes = [sp, fp] + [vp] * 11 + [vp, ctypes.c_size_t, vp]
+    lib.ssd_bwd_ex.restype = ctypes.c_int
+    lib.ssd_bwd_ex.argtypes = [sp, fp] + [vp] * 20 + [ctypes.c_size_t, vp]
     lib.ssd_bwd_stage_count.restype = ctypes.c_int
     lib.ssd_bwd_stage_count.argtypes = []
     lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
@@ -147,7 +147,7 @@ def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
 def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_d_initial_states: bool = True,
             workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None,
-            dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf)):
+            dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf), z=None):
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
@@ -159,7 +159,8 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     (timing enabled) handed to the profiling entry point.
     ``dt_bias`` (H,) fp32, ``dt_softplus`` and ``dt_limit`` = (min, max): the dt
     front-end of include/ssd_bwd.h (dt is then the raw input); with dt_bias the
-    dict also holds ddt_bias.
+    dict also holds ddt_bias.  ``z`` (like x): the output gate; dy is then the
+    gradient of y * silu(z) and the dict also holds dz.
     """
     lib = load_library()
     dev = x.device
@@ -188,8 +189,9 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
     fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
-    if fe is not None and events is not None:
-        raise ValueError("stage events are not available with the dt front-end")
+    _check(z, "z", io, (b, L, H, P), dev)
+    if (fe is not None or z is not None) and events is not None:
+        raise ValueError("stage events are not available with the dt front-end or the gate")
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)
     if workspace is None or workspace.numel() < nbytes:
@@ -209,10 +211,13 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
             _ptr(out["d_initial_states"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
             ctypes.c_void_p(stream)]
-    if fe is not None:
+    if fe is not None or z is not None:
         if dt_bias is not None and out.get("ddt_bias") is None:
             out["ddt_bias"] = torch.empty((H,), dtype=torch.float32, device=dev)
-        rc = lib.ssd_bwd_fe(args[0], ctypes.byref(fe), *args[1:17], _ptr(out.get("ddt_bias")), *args[17:])
+        if z is not None and out.get("dz") is None:
+            out["dz"] = torch.empty_like(z)
+        rc = lib.ssd_bwd_ex(args[0], ctypes.byref(fe) if fe is not None else None, *args[1:7], _ptr(z),
+                            *args[7:17], _ptr(out.get("ddt_bias")), _ptr(out.get("dz")), *args[17:])
     elif events is None:
         rc = lib.ssd_bwd(*args)
     else:
@@ -229,11 +234,12 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
 def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_final_states: bool = False,
             workspace: Optional[torch.Tensor] = None, dt_bias=None, dt_softplus: bool = False,
-            dt_limit=(-math.inf, math.inf)):
+            dt_limit=(-math.inf, math.inf), z=None):
     """The SSD layer's forward, computed by libssd_bwd: y, and optionally the
     state after each sequence's last position.
 
-    Same argument conventions as ssd_bwd (including the dt front-end).
+    Same argument conventions as ssd_bwd (including the dt front-end and the
+    output gate z: y is then multiplied by silu(z)).
     Returns a dict with y (the I/O dtype, shaped like x) and final_states
     ((S, H, P, N) fp32, or None).
     """
@@ -263,6 +269,7 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
     fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
+    _check(z, "z", io, (b, L, H, P), dev)
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)
     if workspace is None or workspace.numel() < nbytes:
@@ -272,10 +279,11 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states), _ptr(seq_idx),
             _ptr(y), _ptr(fin), _ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)]
-    if fe is None:
+    if fe is None and z is None:
         rc = lib.ssd_fwd(ctypes.byref(shape), *args)
     else:
-        rc = lib.ssd_fwd_fe(ctypes.byref(shape), ctypes.byref(fe), *args)
+        rc = lib.ssd_fwd_ex(ctypes.byref(shape), ctypes.byref(fe) if fe is not None else None, *args[:6], _ptr(z),
+                            *args[6:])
     if rc:
         raise SsdError(rc, "ssd_fwd")
     return {"y": y, "final_states": fin, "workspace": workspace, "shape": shape}
@@ -287,32 +295,33 @@ class SsdChunkScan(torch.autograd.Function):
     saved inputs, so nothing but the inputs is kept between the two."""
 
     @staticmethod
-    def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, chunk_size, nseqs, dt_softplus,
+    def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z, chunk_size, nseqs, dt_softplus,
                 dt_limit):
         fe = dict(dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit)
-        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs, **fe)["y"]
-        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias)
+        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs, z=z, **fe)["y"]
+        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z)
         ctx.chunk_size, ctx.nseqs, ctx.dt_softplus, ctx.dt_limit = chunk_size, nseqs, dt_softplus, dt_limit
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, dt, A, B, C, D, h0, seq_idx, dt_bias = ctx.saved_tensors
+        x, dt, A, B, C, D, h0, seq_idx, dt_bias, z = ctx.saved_tensors
         want_h0 = h0 is not None and ctx.needs_input_grad[6]
         g = ssd_bwd(x, dt, A, B, C, D, dy.contiguous(), h0, seq_idx, chunk_size=ctx.chunk_size, nseqs=ctx.nseqs,
                     want_d_initial_states=want_h0, dt_bias=dt_bias, dt_softplus=ctx.dt_softplus,
-                    dt_limit=ctx.dt_limit)
+                    dt_limit=ctx.dt_limit, z=z)
         return (g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"], g["dD"], g["d_initial_states"] if want_h0 else None,
-                None, g.get("ddt_bias"), None, None, None, None)
+                None, g.get("ddt_bias"), g.get("dz"), None, None, None, None)
 
 
 def ssd_chunk_scan(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
                    nseqs: Optional[int] = None, dt_bias=None, dt_softplus: bool = False,
-                   dt_limit=(-math.inf, math.inf)) -> torch.Tensor:
-    """y of the SSD layer with autograd support (see SsdChunkScan); the
-    gradients reach x, dt, A, B, C, D, initial_states and dt_bias."""
-    return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, chunk_size, nseqs, dt_softplus,
-                              tuple(dt_limit))
+                   dt_limit=(-math.inf, math.inf), z=None) -> torch.Tensor:
+    """y of the SSD layer (times silu(z) when z is given) with autograd
+    support (see SsdChunkScan); the gradients reach x, dt, A, B, C, D,
+    initial_states, dt_bias and z."""
+    return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z, chunk_size, nseqs,
+                              dt_softplus, tuple(dt_limit))
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:

@@ -128,10 +128,11 @@ def test_frontend_argument_errors_are_reported_before_launch():
     s = shape()
     names = ["x", "dt", "A", "B", "C", "D", "dy", "h0", "seq_idx", "dx", "ddt", "dA", "dB", "dC", "dD", "dinit"]
 
-    def call(fe, ddt_bias=None):
+    def call(fe, ddt_bias=None, z=None, dz=None):
         args = [ctypes.c_void_p(FAKE.get(n)) if FAKE.get(n) else None for n in names]
-        return lib.ssd_bwd_fe(ctypes.byref(s), ctypes.byref(fe) if fe is not None else None, *args,
-                              ctypes.c_void_p(ddt_bias) if ddt_bias else None, ctypes.c_void_p(FAKE["ws"]),
+        vp = lambda v: ctypes.c_void_p(v) if v else None
+        return lib.ssd_bwd_ex(ctypes.byref(s), ctypes.byref(fe) if fe is not None else None, *args[:6], vp(z),
+                              *args[6:], vp(ddt_bias), vp(dz), ctypes.c_void_p(FAKE["ws"]),
                               ctypes.c_size_t(1 << 40), None)
 
     inf = float("inf")
@@ -140,3 +141,7 @@ def test_frontend_argument_errors_are_reported_before_launch():
     assert call(ssd.SsdDtFrontend(None, 1, -inf, inf), ddt_bias=0x990000) == -1   # ddt_bias without dt_bias
     assert call(None, ddt_bias=0x990000) == -1
     assert call(ssd.SsdDtFrontend(0x990008, 1, -inf, inf)) == -4       # misaligned dt_bias
+    assert call(None, z=0x990000) == -1                                 # z without dz
+    assert call(None, dz=0x990000) == -1                                # dz without z
+    assert call(None, z=0x990000, dz=FAKE["dx"]) == -1                  # dz aliasing dx (dx holds the gated dy)
+    assert call(None, z=0x990000, dz=0x9a0008) == -4                    # misaligned dz

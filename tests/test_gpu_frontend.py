@@ -1,5 +1,5 @@
-"""GPU parity of the dt front-end (dt_bias, softplus, clamp; ssd_fwd_fe /
-ssd_bwd_fe) with the oracle's forward_fe / backward_fe: y and the final
+"""GPU parity of the dt front-end (dt_bias, softplus, clamp; ssd_fwd_ex /
+ssd_bwd_ex) with the oracle's forward_fe / backward_fe: y and the final
 states, every gradient with respect to the raw dt and dt_bias, and bitwise
 repeats.  The raw dt and dt_bias are drawn as the workloads' dt is
 (softplus of N(0, 0.5) plus a bias that puts the step in [1e-3, 1e-1])."""

@@ -1,0 +1,114 @@
+"""GPU parity of the output gate (out = y silu(z); ssd_fwd_ex / ssd_bwd_ex)
+with the oracle's forward_ex / backward_ex: the gated y, every gradient and
+dz, with and without the dt front-end; bitwise repeats; the autograd
+function with z as a leaf; the caller's dy left untouched."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from state_space_model_mamba_amd import ssd
+from state_space_model_mamba_amd.workloads import Workload, make_inputs, to_f64_numpy
+from tests.gpu_helpers import GRADS, TOL, bytes_equal, compare, normwise_err, to_device, to_numpy64
+from tests.test_gpu_parity import packed, small
+
+pytestmark = pytest.mark.gpu
+
+
+def with_gate(inputs, seed):
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn(inputs["x"].shape, generator=g)
+    inputs["z"] = z.to(inputs["x"].dtype).contiguous()
+    return inputs
+
+
+def run(inputs, chunk, frontend=False):
+    d = to_device(inputs)
+    nseqs = inputs["initial_states"].shape[0] if inputs.get("initial_states") is not None else None
+    kw = dict(z=d["z"])
+    dt = d["dt"]
+    if frontend:
+        kw.update(dt_bias=d["dt_bias"], dt_softplus=True)
+        dt = d["dt_raw"]
+    dy_before = d["dy"].clone()
+    f = ssd.ssd_fwd(d["x"], dt, d["A"], d["B"], d["C"], d["D"], d.get("initial_states"), d.get("seq_idx"),
+                    chunk_size=chunk, nseqs=nseqs, **kw)
+    g = ssd.ssd_bwd(d["x"], dt, d["A"], d["B"], d["C"], d["D"], d["dy"], d.get("initial_states"), d.get("seq_idx"),
+                    chunk_size=chunk, nseqs=nseqs, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dy_before, d["dy"]), "the caller's dy was modified"
+    return f, g
+
+
+def reference(inputs, frontend=False):
+    f = to_f64_numpy(inputs)
+    kw = dict(z=f["z"])
+    dt = f["dt"]
+    if frontend:
+        kw.update(dt_bias=f["dt_bias"], dt_softplus=True)
+        dt = f["dt_raw"]
+    y = oracle.forward_ex(f["x"], dt, f["A"], f["B"], f["C"], f["D"], f["initial_states"], f["seq_idx"], **kw)
+    g = oracle.backward_ex(f["x"], dt, f["A"], f["B"], f["C"], f["D"], f["dy"], f["initial_states"], f["seq_idx"],
+                           **kw)
+    return y, g
+
+
+def check(inputs, chunk, tol, label, frontend=False):
+    print(f"[case] gate {label}", flush=True)
+    f, g = run(inputs, chunk, frontend)
+    y_ref, g_ref = reference(inputs, frontend)
+    e_y = normwise_err(f["y"].double().cpu().numpy(), y_ref)
+    got = to_numpy64(g)
+    got["dz"] = g["dz"].double().cpu().numpy()
+    keys = GRADS + ("dz",)
+    if frontend:
+        got["ddt_bias"] = g["ddt_bias"].double().cpu().numpy()
+        keys += ("ddt_bias",)
+    compare(got, g_ref, tol, keys=keys, label=f"gate {label}")
+    print(f"gate {label}: gated y err {e_y:.2e}", flush=True)
+    assert e_y <= tol
+    return f, g
+
+
+def test_gate_fp32():
+    w = small("gate_f32", batch=2, seqlen=200, nheads=4, ngroups=2, headdim=16, dstate=32, chunk=64)
+    check(with_gate(packed(make_inputs(w), [[64, 40, 1, 95], [200]]), 3), 64, TOL["f32"], "f32 packed")
+
+
+def test_gate_fp32_with_frontend():
+    w = small("gate_f32_fe", batch=1, seqlen=300, nheads=4, ngroups=1, headdim=16, dstate=32, chunk=128)
+    check(with_gate(packed(make_inputs(w), [[100, 200]]), 4), 128, TOL["f32"], "f32 with dt front-end",
+          frontend=True)
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_gate_bf16(chunk):
+    w = Workload("gate_bf16", batch=2, seqlen=600, nheads=8, headdim=64, ngroups=2, dstate=64, chunk=chunk,
+                 dtype="bf16", seed=71)
+    check(with_gate(packed(make_inputs(w), [[200, 150, 250], [600]]), 5), chunk, TOL["bf16"], f"bf16 Q{chunk}",
+          frontend=True)
+
+
+def test_gate_bitwise_repeat_and_autograd():
+    w = Workload("gate_det", batch=1, seqlen=700, nheads=8, headdim=64, ngroups=2, dstate=64, chunk=128,
+                 dtype="bf16", seed=72)
+    inputs = with_gate(packed(make_inputs(w), [[250, 450]]), 6)
+    print("[case] gate determinism and autograd", flush=True)
+    f1, g1 = run(inputs, 128, frontend=True)
+    f2, g2 = run(inputs, 128, frontend=True)
+    assert torch.equal(f1["y"].view(torch.int16), f2["y"].view(torch.int16))
+    assert not bytes_equal(g1, g2, GRADS + ("ddt_bias", "dz"))
+    d = to_device(inputs)
+    leaves = {k: d[k].clone().requires_grad_(True) for k in ("x", "dt_raw", "A", "B", "C", "D", "dt_bias", "z")}
+    y = ssd.ssd_chunk_scan(leaves["x"], leaves["dt_raw"], leaves["A"], leaves["B"], leaves["C"], leaves["D"],
+                           d["initial_states"], d["seq_idx"], chunk_size=128, nseqs=2, dt_bias=leaves["dt_bias"],
+                           dt_softplus=True, z=leaves["z"])
+    y.backward(d["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach().view(torch.int16), f1["y"].view(torch.int16))
+    assert torch.equal(leaves["z"].grad.view(torch.int16), g1["dz"].view(torch.int16))
+    assert torch.equal(leaves["x"].grad.view(torch.int16), g1["dx"].view(torch.int16))
+    assert torch.equal(leaves["dt_raw"].grad.view(torch.int32), g1["ddt"].view(torch.int32))
+    assert torch.equal(leaves["dt_bias"].grad.view(torch.int32), g1["ddt_bias"].view(torch.int32))
