@@ -241,15 +241,14 @@ def measure_forward(torch, ssd, w, d, S, ws, z, steps, warmup):
             "bitwise_repeat": bitwise}
 
 
-def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup):
+def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup, z=None):
     """ssd_bwd with the dt front-end (the raw draws, dt_bias, softplus) on the same workload:
-    the same step as the headline plus the activation and the dt_bias gradient."""
-    out = {}
-
+    the same step as the headline plus the activation and the dt_bias gradient (and, with z,
+    the output gate: a recomputation of y and the gated dy and dz first)."""
     def call():
         return ssd.ssd_bwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["dy"],
                            initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
-                           nseqs=S, workspace=ws, dt_bias=d["dt_bias"], dt_softplus=True)
+                           nseqs=S, workspace=ws, dt_bias=d["dt_bias"], dt_softplus=True, z=z)
     for _ in range(warmup):
         ref = call()
     torch.cuda.synchronize()
@@ -263,7 +262,7 @@ def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup):
     ms = t0.elapsed_time(t1) / steps
     same = all(torch.equal(ref[k].view(torch.int16) if ref[k].dtype == torch.bfloat16 else ref[k].view(torch.int32),
                            last[k].view(torch.int16) if last[k].dtype == torch.bfloat16 else last[k].view(torch.int32))
-               for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias"))
+               for k in ref if k in ("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dz"))
     return {"ms_per_step": ms, "tokens_per_s": w.tokens / (ms * 1e-3), "steps": steps, "warmup": warmup,
             "bitwise_repeat": same}
 
@@ -394,6 +393,12 @@ def main():
                                          warmup=min(args.warmup, 10))
         res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=min(args.steps, 100),
                                                             warmup=min(args.warmup, 10))
+        # output gate: z ~ N(0, 1) (seeded), in the I/O dtype
+        gz = torch.Generator().manual_seed(w.seed + 1)
+        z = torch.randn(tuple(d["x"].shape), generator=gz).to(d["x"].dtype).to(dev)
+        res["backward_with_dt_frontend_and_gate"] = measure_frontend(
+            torch, ssd, w, d, S, ws, steps=min(args.steps, 100), warmup=min(args.warmup, 10), z=z)
+        del z
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
