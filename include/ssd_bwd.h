@@ -153,17 +153,20 @@ int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, const float*
  * sigmoid(u), or 1 for u > 20 : 1).
  */
 typedef struct {
-  const float* dt_bias; /* (nheads) fp32 device pointer, or NULL */
-  int32_t dt_softplus;  /* nonzero: softplus after the bias */
-  float dt_min, dt_max; /* clamp of the activated value */
-} ssd_dt_frontend;
+  const float* dt_bias;  /* (nheads) fp32 device pointer, or NULL */
+  int32_t dt_softplus;   /* nonzero: softplus after the bias */
+  float dt_min, dt_max;  /* clamp of the activated value */
+  int32_t d_per_channel; /* nonzero: D and dD are (nheads, headdim): y += D[h, p] x[.., h, p] */
+} ssd_options;
 
 /*
- * ssd_fwd and ssd_bwd extended with the dt front-end above (`fe` NULL: none)
- * and an output gate (`z` NULL: none).  With a front-end, `dt` is the raw
- * input and `ddt` the gradient with respect to it; `ddt_bias` (nheads, fp32,
- * nullable; requires fe->dt_bias) receives the gradient with respect to
- * dt_bias, summed over batch and positions in a fixed order.
+ * ssd_fwd and ssd_bwd extended with the options above (`opt` NULL: none of
+ * them) and an output gate (`z` NULL: none).  With a dt front-end, `dt` is
+ * the raw input and `ddt` the gradient with respect to it; `ddt_bias`
+ * (nheads, fp32, nullable; requires opt->dt_bias) receives the gradient with
+ * respect to dt_bias, summed over batch and positions in a fixed order.
+ * With d_per_channel, D (nullable) and dD are (nheads, headdim) fp32, dD
+ * summed over batch and positions in a fixed order.
  *
  * The gate z (batch, seqlen, nheads, headdim) in the I/O dtype multiplies
  * the layer's output by silu(z) = z sigmoid(z):  out = y * silu(z), y as
@@ -178,11 +181,11 @@ typedef struct {
  * Mamba-2 layer, the second half of the same "next" step as the front-end.
  * Everything else is as for ssd_fwd / ssd_bwd, including the workspace size.
  */
-int ssd_fwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+int ssd_fwd_ex(const ssd_shape* shape, const ssd_options* opt, const void* x, const float* dt,
                const float* A, const void* B, const void* C, const float* D, const void* z,
                const float* initial_states, const int32_t* seq_idx, void* y, float* final_states,
                void* workspace, size_t workspace_bytes, void* stream);
-int ssd_bwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+int ssd_bwd_ex(const ssd_shape* shape, const ssd_options* opt, const void* x, const float* dt,
                const float* A, const void* B, const void* C, const float* D, const void* z, const void* dy,
                const float* initial_states, const int32_t* seq_idx,
                void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,

@@ -232,10 +232,21 @@ def silu(z):
     return z * s, s * (1.0 + z * (1.0 - s))
 
 
+def _per_channel(D):
+    return D is not None and np.ndim(D) == 2
+
+
 def forward_ex(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, z=None, return_final_states=False,
                **kw):
-    """forward_fe() (dt front-end keywords included) times silu(z) when z is given."""
-    res = forward_fe(x, dt, A, B, C, D, initial_states, seq_idx, return_final_states=return_final_states, **kw)
+    """forward_fe() (dt front-end keywords included), with D either (H,) or
+    per channel (H, P): y += D[h, p] x[..., h, p]; times silu(z) when z is given."""
+    if _per_channel(D):
+        res = forward_fe(x, dt, A, B, C, None, initial_states, seq_idx, return_final_states=return_final_states,
+                         **kw)
+        dterm = _f64(x) * _f64(D)[None, None, :, :]
+        res = (res[0] + dterm, res[1]) if return_final_states else res + dterm
+    else:
+        res = forward_fe(x, dt, A, B, C, D, initial_states, seq_idx, return_final_states=return_final_states, **kw)
     if z is None:
         return res
     y, fs = res if return_final_states else (res, None)
@@ -244,15 +255,24 @@ def forward_ex(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, z=None
 
 
 def backward_ex(x, dt, A, B, C, D, dout, initial_states=None, seq_idx=None, z=None, **kw):
-    """backward_fe() for the output out = y silu(z): dout is the gradient of
-    out, so the layer sees dy = dout silu(z), and dz = dout y silu'(z) with y
-    the ungated output."""
-    if z is None:
-        return backward_fe(x, dt, A, B, C, D, dout, initial_states, seq_idx, **kw)
+    """backward_fe() with a per-channel D allowed (dx += D dy, dD[h, p] the sum
+    of dy x over batch and positions) and, with z, for the output
+    out = y silu(z): dout is the gradient of out, so the layer sees
+    dy = dout silu(z), and dz = dout y silu'(z) with y the ungated output."""
     fe = {k: kw[k] for k in ("dt_bias", "dt_softplus", "dt_limit") if k in kw}
-    y = forward_fe(x, dt, A, B, C, D, initial_states, seq_idx, **fe)
-    g, dg = silu(z)
-    dout = _f64(dout)
-    res = backward_fe(x, dt, A, B, C, D, dout * g, initial_states, seq_idx, **kw)
-    res["dz"] = dout * y * dg
+    dy = _f64(dout)
+    res_dz = None
+    if z is not None:
+        y = forward_ex(x, dt, A, B, C, D, initial_states, seq_idx, **fe)
+        g, dg = silu(z)
+        res_dz = dy * y * dg
+        dy = dy * g
+    if _per_channel(D):
+        res = backward_fe(x, dt, A, B, C, None, dy, initial_states, seq_idx, **kw)
+        res["dx"] = res["dx"] + _f64(D)[None, None, :, :] * dy
+        res["dD"] = (dy * _f64(x)).sum(axis=(0, 1))
+    else:
+        res = backward_fe(x, dt, A, B, C, D, dy, initial_states, seq_idx, **kw)
+    if z is not None:
+        res["dz"] = res_dz
     return res

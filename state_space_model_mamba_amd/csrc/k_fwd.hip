@@ -179,9 +179,10 @@ struct YCfg {
   static constexpr int LDE = NS + VEC;   // E rows [p][n] of one dstate slab
   static constexpr int NOWN = T16 + 1;
   using Split = RowSplit<T16>;
-  // x, C, E; acs, dt, exp-table, segpos (Q each) and segment starts (Q + 1)
+  // x, C, E; acs, dt, exp-table, segpos (Q each), segment starts (Q + 1) and
+  // the head's per-channel D (P)
   static constexpr size_t LDS =
-      (size_t(Q) * LDX + size_t(Q) * LDC + size_t(P) * LDE) * sizeof(T) + size_t(5 * Q + 1) * 4;
+      (size_t(Q) * LDX + size_t(Q) * LDC + size_t(P) * LDE) * sizeof(T) + size_t(5 * Q + 4 + P) * 4;
 };
 
 // The intra-chunk term over the wave's tiles (row split order), added to the
@@ -293,6 +294,7 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
   float* const s_ejdt0 = s_dt0 + Q;
   int* const s_seg0 = reinterpret_cast<int*>(s_ejdt0 + Q);
   int* const s_segstart0 = s_seg0 + Q;   // Q + 1 entries (only the chunk's segments are used)
+  float* const s_D = reinterpret_cast<float*>(s_segstart0 + Q + 4);   // per-channel D of the head (16-byte aligned)
 
   // block -> (batch, group, chunk, head slice); the slices of one (b, g, c)
   // are consecutive logical blocks and so share an XCD's L2
@@ -417,6 +419,7 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
     }
     st_x.store(s_x, LDX);
     if (e0_hin) st_e.store(s_e, LDE);
+    if (tid < P) s_D[tid] = pb.D ? pb.D[pb.d_hp ? h * P + tid : h] : 0.f;   // D per channel (or repeated)
     __syncthreads();
     if (h + 1 < h_end) prefetch(h + 1);
 
@@ -486,7 +489,6 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
     // ---- epilogue: y = intra + state + D x, then the output gate if any:
     // forward, y silu(z); gate pass (dz given), the gated dy = dout silu(z)
     // into y's place and dz = dout y silu'(z)
-    const float Dv = pb.D ? pb.D[h] : 0.f;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int I = Cf::Split::row(w, a);
@@ -498,9 +500,10 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
         const f32x4_t yv = a ? yb[pt] : ya[pt];
         const f32x4_t xv = load4f<T>(s_x + i * LDX + 16 * pt + 4 * kg);
         const int64_t off = row + 16 * pt + 4 * kg;
+        const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(s_D + 16 * pt + 4 * kg);
         f32x4_t o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = yv[r] + Dv * xv[r];
+        for (int r = 0; r < 4; ++r) o[r] = yv[r] + D4[r] * xv[r];
         if (!pb.z) {   // (uniform)
           store4f<T>(static_cast<T*>(pb.y) + off, o);
           continue;

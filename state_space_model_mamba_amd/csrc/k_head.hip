@@ -58,7 +58,8 @@ struct HeadCfg {
   // da shares: [column tile J][position]
   static constexpr size_t RS_FLOATS = size_t(T16) * Q;
   // vectors: acs dt w ee ddacs ddtp sj dd daint er dfe (11 Q floats) + seg (Q ints) + red (W + 8)
-  static constexpr size_t RV_FLOATS = size_t(12) * Q + W + 8;
+  // + per-channel dD partials (W x P) + the head's D per channel (P)
+  static constexpr size_t RV_FLOATS = size_t(12) * Q + ((W + 8 + 3) & ~3) + size_t(W + 1) * P;
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
@@ -394,6 +395,8 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   float* s_dfe = s_er + Q;
   int* s_seg = reinterpret_cast<int*>(s_dfe + Q);
   float* s_red = reinterpret_cast<float*>(s_seg + Q);
+  float* s_redp = s_red + ((W + 8 + 3) & ~3);   // (16-byte aligned)
+  float* s_Dp = s_redp + W * P;   // D of this head, per channel (the scalar D repeated)
 
   const int hh = static_cast<int>(lb % pb.hpg);
   int64_t rest = lb / pb.hpg;
@@ -421,7 +424,9 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   }
   const float acs_end = pb.acs[bhc * Q + Q - 1];
   const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
-  const float Dh = pb.D ? pb.D[h] : 0.f;
+  const float Dh = pb.D && !pb.d_hp ? pb.D[h] : 0.f;
+  float Dp = Dh;
+  if (pb.d_hp && pb.D && tid < P) Dp = pb.D[h * P + tid];
   const float Ah = pb.A[h];
   float endd = 0.f;   // the chunk-end term's dstate-tile partials, in tile order (used by wave 0)
   if (tid < WAVE)
@@ -454,12 +459,15 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     s_er[tid] = uniform ? Elem<T>::exp(acs_i - acs_tile0) : 0.f;
     s_dfe[tid] = dfe_i;
   }
+  if (tid < P) {
+    s_Dp[tid] = Dp;
+  }
 
   // ---- phase B: x, dy rows; decays; M; ddt_intra; da shares; dx_intra
   st_x.store(s_xk, LDP);
   st_dy.store(s_dyk, LDP);
   __syncthreads();
-  {
+  if (!pb.d_hp) {   // (uniform) dD of the head: sum of dy . x over the chunk
     float dd = 0.f;
     for (int v = tid; v < Q * P / VEC; v += NTHR) {
       const int i = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
@@ -470,6 +478,25 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     }
     dd = wave_sum(dd);
     if (l == 0) s_red[w] = dd;
+  } else {          // per channel: a thread's vectors all start at p0 = VEC (tid mod P / VEC)
+    static_assert(NTHR % (P / VEC) == 0 && WAVE % (P / VEC) == 0, "fixed channel group per thread");
+    float dd[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dd[e] = 0.f;
+    for (int v = tid; v < Q * P / VEC; v += NTHR) {
+      const int i = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
+      const uint4 dv = *reinterpret_cast<const uint4*>(s_dyk + i * LDP + p0);
+      const uint4 xv = *reinterpret_cast<const uint4*>(s_xk + i * LDP + p0);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dd[e] += vget<T>(dv, e) * vget<T>(xv, e);
+    }
+    // over the lanes of one channel group (fixed xor order), then per wave to LDS
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      for (int m = P / VEC; m < WAVE; m <<= 1) dd[e] += __shfl_xor(dd[e], m, WAVE);
+    if (l < P / VEC)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s_redp[w * P + l * VEC + e] = dd[e];
   }
 
   f32x4_t dxt[Cf::NCOL][PT];
@@ -550,10 +577,11 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     for (int pt = 0; pt < PT; ++pt) {
       const f32x4_t dyv = load4f<T>(s_dyk + j * LDP + 16 * pt + 4 * kg);
       const f32x4_t xv = load4f<T>(s_xk + j * LDP + 16 * pt + 4 * kg);
+      const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(s_Dp + 16 * pt + 4 * kg);
       f32x4_t outv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        outv[r] = dtj * dxt[a][pt][r] + wj * zt[a][pt][r] + Dh * dyv[r];
+        outv[r] = dtj * dxt[a][pt][r] + wj * zt[a][pt][r] + D4[r] * dyv[r];
         xz += xv[r] * zt[a][pt][r];
       }
       if (t < pb.L)
@@ -572,6 +600,11 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   load_item_rows<T, Q, P>(pb, lb_next, st_x, st_dy);
 
   // ---- phase D: da and its consumers
+  if (pb.d_hp && tid < P) {   // per-channel dD slot of this (b, c, h), waves in order
+    float dd = 0.f;
+    for (int k = 0; k < W; ++k) dd += s_redp[k * P + tid];
+    pb.slot_dDp[(bc * pb.H + h) * P + tid] = dd;
+  }
   if (tid < Q) {
     const int k = tid, K = k / 16;
     float da = 0.f;
@@ -662,9 +695,11 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     if (l == 0) {
       if (pb.ddt_bias) pb.slot_ddtb[bc * pb.H + h] = dbp;
       pb.slot_dA[bc * pb.H + h] = dap;
-      float dd = 0.f;
-      for (int k = 0; k < W; ++k) dd += s_red[k];
-      pb.slot_dD[bc * pb.H + h] = dd;
+      if (!pb.d_hp) {
+        float dd = 0.f;
+        for (int k = 0; k < W; ++k) dd += s_red[k];
+        pb.slot_dD[bc * pb.H + h] = dd;
+      }
     }
   }
 }

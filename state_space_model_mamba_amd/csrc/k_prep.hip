@@ -176,9 +176,19 @@ __global__ __launch_bounds__(256) void k_reduce(Problem pb) {
   e = wave_sum_f64(e);
   if (l == 0) {
     pb.dA[h] = static_cast<float>(a);
-    if (pb.dD) pb.dD[h] = static_cast<float>(d);
+    if (pb.dD && !pb.d_hp) pb.dD[h] = static_cast<float>(d);
     if (pb.ddt_bias) pb.ddt_bias[h] = static_cast<float>(e);
   }
+}
+
+// Per-channel dD: one thread per (h, p), the (b, c) slots in order, in double.
+__global__ __launch_bounds__(256) void k_reduce_dp(Problem pb) {
+  const int hp = blockIdx.x * 256 + threadIdx.x;
+  if (hp >= pb.H * pb.P) return;
+  const int n = pb.B * pb.nc;
+  double d = 0.0;
+  for (int k = 0; k < n; ++k) d += static_cast<double>(pb.slot_dDp[static_cast<int64_t>(k) * pb.H * pb.P + hp]);
+  pb.dD[hp] = static_cast<float>(d);
 }
 
 hipError_t launch_prep(const Problem& pb, hipStream_t s) {
@@ -197,6 +207,11 @@ hipError_t launch_prep(const Problem& pb, hipStream_t s) {
 
 hipError_t launch_reduce(const Problem& pb, hipStream_t s) {
   hipLaunchKernelGGL(k_reduce, dim3((pb.H + 3) / 4), dim3(256), 0, s, pb);
+  if (pb.d_hp && pb.dD) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_reduce_dp, dim3((pb.H * pb.P + 255) / 256), dim3(256), 0, s, pb);
+  }
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_ddtb, seqstart,
+  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_dDp, slot_ddtb, seqstart,
       total;
   int nc, ntg;
 };
@@ -73,6 +73,7 @@ Layout make_layout(const ssd_shape* s) {
   L.slot_dA = take(B * nc * H * 4);
   L.slot_dD = take(B * nc * H * 4);
   L.slot_ddtb = take(B * nc * H * 4);
+  L.slot_dDp = take(B * nc * H * P * 4);
   L.seqstart = take((s->nseqs > 0 ? s->nseqs : 1) * 4);
   L.total = off;
   L.nc = static_cast<int>(nc);
@@ -156,12 +157,14 @@ void fill_problem(const ssd_shape* shape, const Layout& L, void* workspace, ssd:
   pb.slot_dA = reinterpret_cast<float*>(ws + L.slot_dA);
   pb.slot_dD = reinterpret_cast<float*>(ws + L.slot_dD);
   pb.slot_ddtb = reinterpret_cast<float*>(ws + L.slot_ddtb);
+  pb.slot_dDp = reinterpret_cast<float*>(ws + L.slot_dDp);
   pb.seqstart = reinterpret_cast<int32_t*>(ws + L.seqstart);
 }
 
-// The dt front-end's fields of the problem (fe NULL: none).
-int fill_frontend(const ssd_dt_frontend* fe, ssd::Problem& pb) {
+// The options' fields of the problem (fe NULL: none).
+int fill_frontend(const ssd_options* fe, ssd::Problem& pb) {
   pb.fe = 0;
+  pb.d_hp = 0;
   pb.dt_bias = nullptr;
   pb.dt_softplus = 0;
   pb.dt_min = -__builtin_inff();
@@ -174,10 +177,11 @@ int fill_frontend(const ssd_dt_frontend* fe, ssd::Problem& pb) {
   pb.dt_min = fe->dt_min;
   pb.dt_max = fe->dt_max;
   pb.fe = pb.dt_bias || pb.dt_softplus || pb.dt_min > -__builtin_inff() || pb.dt_max < __builtin_inff();
+  pb.d_hp = fe->d_per_channel != 0;
   return SSD_OK;
 }
 
-int run_bwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
+int run_bwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const float* dt, const float* A,
             const void* B, const void* C, const float* D, const void* z, const void* dy,
             const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt, float* dA, void* dB,
             void* dC, float* dD, float* d_initial_states, float* ddt_bias, void* dz, void* workspace,
@@ -249,7 +253,7 @@ extern "C" int ssd_bwd(const ssd_shape* shape, const void* x, const float* dt, c
                  dD, d_initial_states, nullptr, nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
-extern "C" int ssd_bwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+extern "C" int ssd_bwd_ex(const ssd_shape* shape, const ssd_options* fe, const void* x, const float* dt,
                           const float* A, const void* B, const void* C, const float* D, const void* z,
                           const void* dy, const float* initial_states, const int32_t* seq_idx, void* dx,
                           float* ddt, float* dA, void* dB, void* dC, float* dD, float* d_initial_states,
@@ -271,7 +275,7 @@ extern "C" int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const flo
 
 namespace {
 
-int run_fwd(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt, const float* A,
+int run_fwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const float* dt, const float* A,
             const void* B, const void* C, const float* D, const void* z, const float* initial_states,
             const int32_t* seq_idx, void* y, float* final_states, void* workspace, size_t workspace_bytes,
             void* stream) {
@@ -310,7 +314,7 @@ extern "C" int ssd_fwd(const ssd_shape* shape, const void* x, const float* dt, c
                  workspace_bytes, stream);
 }
 
-extern "C" int ssd_fwd_ex(const ssd_shape* shape, const ssd_dt_frontend* fe, const void* x, const float* dt,
+extern "C" int ssd_fwd_ex(const ssd_shape* shape, const ssd_options* fe, const void* x, const float* dt,
                           const float* A, const void* B, const void* C, const float* D, const void* z,
                           const float* initial_states, const int32_t* seq_idx, void* y, float* final_states,
                           void* workspace, size_t workspace_bytes, void* stream) {

@@ -48,6 +48,7 @@ struct Problem {
   int dt_softplus;
   float dt_min, dt_max;
   float* ddt_bias;       // (H) output, nullable
+  int d_hp;              // nonzero: D and dD are (H, P)
   // output gate (nullable): out = y silu(z); the backward's gate pass reads
   // dout and writes the gated dy into y's place (the dx buffer) and dz
   const void* z;     // (B, L, H, P), I/O dtype
@@ -73,6 +74,7 @@ struct Problem {
   float* slot_dA;    // (B, nc, H)
   float* slot_dD;    // (B, nc, H)
   float* slot_ddtb;  // (B, nc, H): dt_bias gradient partials
+  float* slot_dDp;   // (B, nc, H, P): per-channel dD partials
   int32_t* seqstart; // (nseqs): b * L + t of each sequence's first position (forward)
 };
 

@@ -33,9 +33,9 @@ class SsdShape(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
-class SsdDtFrontend(ctypes.Structure):
+class SsdOptions(ctypes.Structure):
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
-                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float), ("d_per_channel", ctypes.c_int32)]
 
 
 class SsdError(RuntimeError):
@@ -72,7 +72,7 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_profiled.argtypes = [sp] + [vp] * 17 + [ctypes.c_size_t, vp, ctypes.POINTER(vp)]
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_fwd.argtypes = [sp] + [vp] * 10 + [vp, ctypes.c_size_t, vp]
-    fp = ctypes.POINTER(SsdDtFrontend)
+    fp = ctypes.POINTER(SsdOptions)
     lib.ssd_fwd_ex.restype = ctypes.c_int
     lib.ssd_fwd_ex.argtypes = [sp, fp] + [vp] * 11 + [vp, ctypes.c_size_t, vp]
     lib.ssd_bwd_ex.restype = ctypes.c_int
@@ -128,13 +128,15 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _frontend(dt_bias, dt_softplus, dt_limit, H, dev):
-    """The C front-end struct, or None when it would change nothing."""
+def _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev):
+    """The C options struct (dt front-end, per-channel D), or None when it would change nothing."""
     lo, hi = float(dt_limit[0]), float(dt_limit[1])
-    if dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf:
+    per_channel = D is not None and D.dim() == 2
+    _check(D, "D", torch.float32, (H, P) if per_channel else (H,), dev)
+    if dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf and not per_channel:
         return None
     _check(dt_bias, "dt_bias", torch.float32, (H,), dev)
-    return SsdDtFrontend(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi)
+    return SsdOptions(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, 1 if per_channel else 0)
 
 
 def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
@@ -151,7 +153,7 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
-    dt: (b, L, H), A, D: (H,), initial_states: (S, H, P, N) fp32 or None,
+    dt: (b, L, H), A: (H,), D: (H,) or (H, P) (per channel), initial_states: (S, H, P, N) fp32 or None,
     seq_idx: (b, L) int32 or None.  ``nseqs`` (the number of sequence starts)
     is needed only when seq_idx is given without initial_states.
     Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states.
@@ -185,10 +187,9 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     _check(C, "C", io, (b, L, G, N), dev)
     _check(dt, "dt", torch.float32, (b, L, H), dev)
     _check(A, "A", torch.float32, (H,), dev)
-    _check(D, "D", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
-    fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
+    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev)
     _check(z, "z", io, (b, L, H, P), dev)
     if (fe is not None or z is not None) and events is not None:
         raise ValueError("stage events are not available with the dt front-end or the gate")
@@ -201,7 +202,7 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
             "dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
             "dA": torch.empty((H,), dtype=torch.float32, device=dev),
             "dB": torch.empty_like(B), "dC": torch.empty_like(C),
-            "dD": torch.empty((H,), dtype=torch.float32, device=dev) if D is not None else None,
+            "dD": torch.empty(tuple(D.shape), dtype=torch.float32, device=dev) if D is not None else None,
             "d_initial_states": (torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
                                  if want_d_initial_states and S > 0 else None),
         }
@@ -265,10 +266,9 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     _check(C, "C", io, (b, L, G, N), dev)
     _check(dt, "dt", torch.float32, (b, L, H), dev)
     _check(A, "A", torch.float32, (H,), dev)
-    _check(D, "D", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
-    fe = _frontend(dt_bias, dt_softplus, dt_limit, H, dev)
+    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev)
     _check(z, "z", io, (b, L, H, P), dev)
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)

@@ -136,11 +136,11 @@ def test_frontend_argument_errors_are_reported_before_launch():
                               ctypes.c_size_t(1 << 40), None)
 
     inf = float("inf")
-    assert call(ssd.SsdDtFrontend(None, 1, 0.5, 0.1)) == -1            # dt_min > dt_max
-    assert call(ssd.SsdDtFrontend(None, 1, float("nan"), inf)) == -1   # NaN bound
-    assert call(ssd.SsdDtFrontend(None, 1, -inf, inf), ddt_bias=0x990000) == -1   # ddt_bias without dt_bias
+    assert call(ssd.SsdOptions(None, 1, 0.5, 0.1, 0)) == -1            # dt_min > dt_max
+    assert call(ssd.SsdOptions(None, 1, float("nan"), inf, 0)) == -1   # NaN bound
+    assert call(ssd.SsdOptions(None, 1, -inf, inf, 0), ddt_bias=0x990000) == -1   # ddt_bias without dt_bias
     assert call(None, ddt_bias=0x990000) == -1
-    assert call(ssd.SsdDtFrontend(0x990008, 1, -inf, inf)) == -4       # misaligned dt_bias
+    assert call(ssd.SsdOptions(0x990008, 1, -inf, inf, 0)) == -4       # misaligned dt_bias
     assert call(None, z=0x990000) == -1                                 # z without dz
     assert call(None, dz=0x990000) == -1                                # dz without z
     assert call(None, z=0x990000, dz=FAKE["dx"]) == -1                  # dz aliasing dx (dx holds the gated dy)
