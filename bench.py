@@ -275,7 +275,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
-                    help="skip the forward (ssd_fwd) and the dt front-end measurements")
+                    help="skip the forward (ssd_fwd) and the dt front-end / gate measurements")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the dt front-end / gate measurements (the backward and forward only)")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -391,6 +393,7 @@ def main():
     if not args.no_forward:
         res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=min(args.steps, 100),
                                          warmup=min(args.warmup, 10))
+    if not args.no_forward and not args.no_options:
         res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=min(args.steps, 100),
                                                             warmup=min(args.warmup, 10))
         # output gate: z ~ N(0, 1) (seeded), in the I/O dtype
