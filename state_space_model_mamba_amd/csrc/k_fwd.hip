@@ -488,44 +488,60 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
 
     // ---- epilogue: y = intra + state + D x, then the output gate if any:
     // forward, y silu(z); gate pass (dz given), the gated dy = dout silu(z)
-    // into y's place and dz = dout y silu'(z)
+    // into y's place and dz = dout y silu'(z).  y goes through the wave's own
+    // x rows in LDS (every wave has finished reading x) so that the rows
+    // leave, and dout / z arrive, as whole 16-byte pieces per lane.
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const int I = Cf::Split::row(w, a);
-      const int i = 16 * I + r16, t = c * Q + i;
-      if (t >= pb.L) continue;
-      const int64_t row = ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P;
+      const int i = 16 * Cf::Split::row(w, a) + r16;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const f32x4_t yv = a ? yb[pt] : ya[pt];
-        const f32x4_t xv = load4f<T>(s_x + i * LDX + 16 * pt + 4 * kg);
-        const int64_t off = row + 16 * pt + 4 * kg;
+        T* px = s_x + i * LDX + 16 * pt + 4 * kg;
+        const f32x4_t xv = load4f<T>(px);
         const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(s_D + 16 * pt + 4 * kg);
         f32x4_t o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = yv[r] + D4[r] * xv[r];
+        store4f<T>(px, o);   // (each element is read and rewritten by the same lane)
+      }
+    }
+    constexpr int VEC = Cf::VEC, CV = P / VEC, RV = 16 * CV / WAVE;   // 16-byte pieces per lane and row tile
+    static_assert((16 * CV) % WAVE == 0, "whole pieces per lane");
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int I = Cf::Split::row(w, a);
+#pragma unroll
+      for (int q = 0; q < RV; ++q) {
+        const int v = l + WAVE * q, i = 16 * I + v / CV, cv = v % CV, t = c * Q + i;
+        if (t >= pb.L) continue;
+        const uint4 yu = *reinterpret_cast<const uint4*>(s_x + i * LDX + cv * VEC);
+        const int64_t off = ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + cv * VEC;
         if (!pb.z) {   // (uniform)
-          store4f<T>(static_cast<T*>(pb.y) + off, o);
+          *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = yu;
           continue;
         }
-        const f32x4_t zv = load4f<T>(static_cast<const T*>(pb.z) + off);
-        f32x4_t sg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sg[r] = 1.f / (1.f + expf(-zv[r]));
+        const uint4 zu = ld_global16(static_cast<const T*>(pb.z) + off);
         if (!pb.dz) {
+          T o[VEC];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] *= zv[r] * sg[r];
-          store4f<T>(static_cast<T*>(pb.y) + off, o);
-        } else {
-          const f32x4_t dv = load4f<T>(static_cast<const T*>(pb.dout) + off);
-          f32x4_t dyv, dzv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            dyv[r] = dv[r] * zv[r] * sg[r];
-            dzv[r] = dv[r] * o[r] * sg[r] * (1.f + zv[r] * (1.f - sg[r]));
+          for (int e = 0; e < VEC; ++e) {
+            const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz));
+            o[e] = Elem<T>::from_f(vget<T>(yu, e) * zz * sg);
           }
-          store4f<T>(static_cast<T*>(pb.y) + off, dyv);
-          store4f<T>(static_cast<T*>(pb.dz) + off, dzv);
+          *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = *reinterpret_cast<const uint4*>(o);
+        } else {
+          const uint4 du = ld_global16(static_cast<const T*>(pb.dout) + off);
+          T dyo[VEC], dzo[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz)), dv = vget<T>(du, e);
+            dyo[e] = Elem<T>::from_f(dv * zz * sg);
+            dzo[e] = Elem<T>::from_f(dv * vget<T>(yu, e) * sg * (1.f + zz * (1.f - sg)));
+          }
+          *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = *reinterpret_cast<const uint4*>(dyo);
+          *reinterpret_cast<uint4*>(static_cast<T*>(pb.dz) + off) = *reinterpret_cast<const uint4*>(dzo);
         }
       }
     }
