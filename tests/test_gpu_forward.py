@@ -139,3 +139,36 @@ def test_autograd_function_matches_entry_points():
     for k, gk in (("dt", "ddt"), ("A", "dA"), ("D", "dD")):
         assert torch.equal(leaves[k].grad.view(torch.int32), ref[gk].view(torch.int32)), k
     assert torch.equal(h0_leaf.grad.view(torch.int32), ref["d_initial_states"].view(torch.int32))
+
+
+def heads_slice(inputs, g, h0, h1):
+    """The sub-problem of heads [h0, h1) of group g: their x, dt, A, D, dy and
+    initial states, and the group's B, C."""
+    sub = dict(inputs)
+    for k in ("x", "dy", "dt"):
+        sub[k] = inputs[k][:, :, h0:h1].contiguous()
+    for k in ("A", "D"):
+        sub[k] = inputs[k][h0:h1].contiguous() if inputs.get(k) is not None else None
+    for k in ("B", "C"):
+        sub[k] = inputs[k][:, :, g:g + 1].contiguous()
+    if inputs.get("initial_states") is not None:
+        sub["initial_states"] = inputs["initial_states"][:, h0:h1].contiguous()
+    return sub
+
+
+@pytest.mark.parametrize("name,group,nh", [("bf16_L16384_H128", 5, 16), ("bf16_varlen7_L16384_N256", 0, 8)])
+def test_forward_full_size_sampled_group(name, group, nh):
+    """The full-size workloads in the launch configuration bench.py times; the oracle
+    evaluates the first nh heads of one group (y and final states of those heads are compared)."""
+    w = WORKLOADS[name]
+    inputs = make_inputs(w)
+    print(f"[case] forward {name} group {group}", flush=True)
+    res = run_fwd(inputs, w.chunk, want_final=True)
+    h0 = group * (w.nheads // w.ngroups)
+    h1 = h0 + nh
+    y_ref, f_ref = oracle_fwd(heads_slice(inputs, group, h0, h1), want_final=True)
+    y = res["y"][:, :, h0:h1].double().cpu().numpy()
+    fs = res["final_states"][:, h0:h1].double().cpu().numpy()
+    e_y, e_f = normwise_err(y, y_ref), normwise_err(fs, f_ref)
+    print(f"forward {name} heads {h0}..{h1 - 1}: y err {e_y:.2e}, final states err {e_f:.2e}", flush=True)
+    assert e_y <= TOL["bf16"] and e_f <= TOL["bf16"]
