@@ -148,3 +148,72 @@ def to_f64_numpy(inputs: dict) -> dict:
         else:
             out[k] = v.to(torch.float64).numpy()
     return out
+
+
+# Depthwise causal convolution over the Mamba-2 block's xBC channels
+# (channels = nheads * headdim + 2 * ngroups * dstate of the SSD workload it
+# feeds).  Draws: x, dout ~ N(0, 1) in the I/O dtype; the filter w and bias
+# ~ U(-1/sqrt(width), 1/sqrt(width)) in fp32 (the usual fan-in bound of a
+# depthwise filter of that width); packed rows reuse seq_lengths.
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    channels: int
+    width: int
+    dtype: str
+    seed: int
+    activation: str = "silu"
+    nseqs_packed: int = 0
+    min_len: int = 512
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+    def scaled(self, **kw) -> "ConvWorkload":
+        return replace(self, **kw)
+
+
+CONV_WORKLOADS = {
+    "conv_tiny_f32": ConvWorkload("conv_tiny_f32", batch=2, seqlen=200, channels=96, width=4, dtype="f32",
+                                  seed=2000),
+    # the xBC convolution of bf16_L16384_H128: 128*64 + 2*8*128 channels
+    "conv_bf16_L16384_C10240": ConvWorkload("conv_bf16_L16384_C10240", batch=1, seqlen=16384, channels=10240,
+                                            width=4, dtype="bf16", seed=2001),
+    # the xBC convolution of bf16_varlen7_L16384_N256: 64*64 + 2*1*256 channels, 7 packed sequences
+    "conv_bf16_varlen7_L16384_C4608": ConvWorkload("conv_bf16_varlen7_L16384_C4608", batch=1, seqlen=16384,
+                                                   channels=4608, width=4, dtype="bf16", seed=2002,
+                                                   nseqs_packed=7),
+}
+
+CONV_HEADLINE = "conv_bf16_L16384_C10240"
+
+
+def make_conv_inputs(w: ConvWorkload, lengths: Optional[list[int]] = None) -> dict:
+    """CPU tensors: x, dout (I/O dtype, (batch, seqlen, channels)), weight (channels, width) and
+    bias (channels) in fp32, seq_idx (int32) and lengths when packed."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    b, L, C, W = w.batch, w.seqlen, w.channels, w.width
+    io = w.torch_dtype
+    x = torch.randn((b, L, C), generator=g)
+    dout = torch.randn((b, L, C), generator=g)
+    bound = 1.0 / math.sqrt(W)
+    weight = (torch.rand((C, W), generator=g) * 2 - 1) * bound
+    bias = (torch.rand((C,), generator=g) * 2 - 1) * bound
+    out = {"x": _round(x, io), "dout": _round(dout, io), "weight": weight.contiguous(), "bias": bias.contiguous(),
+           "seq_idx": None}
+    if w.nseqs_packed:
+        if b != 1:
+            raise ValueError("packed workloads use batch 1")
+        if lengths is None:
+            lengths = seq_lengths(L, w.nseqs_packed, w.min_len, g)
+        out["seq_idx"] = seq_idx_from_lengths(lengths)
+        out["lengths"] = lengths
+    return out
