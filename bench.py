@@ -267,6 +267,61 @@ def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup, z=None):
             "bitwise_repeat": same}
 
 
+def measure_conv1d(torch, steps, warmup, dev):
+    """The xBC causal convolution of the headline layer (conv1d_fwd, conv1d_bwd), each timed
+    over `steps` calls with HIP events on the current stream.
+
+    Algorithmic bytes per call: forward reads x and writes out; backward reads
+    x and dout and writes dx (the filter, bias and their gradients are
+    channels * (width + 1) floats each way)."""
+    from state_space_model_mamba_amd import conv1d
+    from state_space_model_mamba_amd.workloads import CONV_HEADLINE, CONV_WORKLOADS, make_conv_inputs
+    cw = CONV_WORKLOADS[CONV_HEADLINE]
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_conv_inputs(cw).items()}
+    shape = conv1d.make_shape(cw.batch, cw.seqlen, cw.channels, cw.width, cw.activation,
+                              0 if cw.dtype == "bf16" else 1)
+    ws = torch.empty(conv1d.workspace_size(shape), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(d["x"])
+    g = {"dx": torch.empty_like(d["x"]), "dweight": torch.empty_like(d["weight"]),
+         "dbias": torch.empty_like(d["bias"])}
+    fwd = lambda: conv1d.conv1d_fwd(d["x"], d["weight"], d["bias"], d["seq_idx"], cw.activation, out=y)
+    bwd = lambda: conv1d.conv1d_bwd(d["x"], d["weight"], d["bias"], d["seq_idx"], d["dout"], cw.activation,
+                                    workspace=ws, out=g)
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            call()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    el = d["x"].element_size() * d["x"].numel()
+    par = cw.channels * (cw.width + 1) * 4
+    res = {"workload": cw.name, "batch": cw.batch, "seqlen": cw.seqlen, "channels": cw.channels,
+           "width": cw.width, "activation": cw.activation, "dtype": cw.dtype}
+    for name, call, alg in (("forward", fwd, 2 * el + par), ("backward", bwd, 3 * el + 2 * par)):
+        ms = timed(call)
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[name] = {"ms_per_call": ms, "tokens_per_s": cw.tokens / (ms * 1e-3), "calls": steps, "warmup": warmup,
+                     "roofline": {"bound": "hbm", "alg_bytes": alg, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+    y0, g0 = y.clone(), {k: v.clone() for k, v in g.items()}
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    res["bitwise_repeat"] = (torch.equal(y0.view(torch.int16), y.view(torch.int16))
+                             and torch.equal(g0["dx"].view(torch.int16), g["dx"].view(torch.int16))
+                             and torch.equal(g0["dweight"].view(torch.int32), g["dweight"].view(torch.int32))
+                             and torch.equal(g0["dbias"].view(torch.int32), g["dbias"].view(torch.int32)))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +333,8 @@ def main():
                     help="skip the forward (ssd_fwd) and the dt front-end / gate measurements")
     ap.add_argument("--no-options", action="store_true",
                     help="skip the dt front-end / gate measurements (the backward and forward only)")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip the causal-conv1d forward / backward measurement")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -402,6 +459,9 @@ def main():
         res["backward_with_dt_frontend_and_gate"] = measure_frontend(
             torch, ssd, w, d, S, ws, steps=min(args.steps, 100), warmup=min(args.warmup, 10), z=z)
         del z
+    if not args.no_conv and not args.no_options:
+        res["causal_conv1d"] = measure_conv1d(torch, steps=min(args.steps, 100), warmup=min(args.warmup, 10),
+                                              dev=dev)
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:

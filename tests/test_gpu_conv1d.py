@@ -1,0 +1,147 @@
+"""GPU parity of the causal-conv1d forward and deterministic backward with the fp64 oracle.
+
+Small cases (several 256-row blocks, ragged tails, idle lanes in the last
+channel block, packed sequences starting on and next to block and wave
+boundaries) compare every element; the full-size xBC workloads, in the launch
+configuration the benchmark times, compare a spread of channels over the
+whole sequence (channels are independent, so the oracle evaluates only
+those).  Repeated calls with garbage workspaces must agree bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import conv1d as oc
+from state_space_model_mamba_amd import conv1d
+from state_space_model_mamba_amd.workloads import (CONV_WORKLOADS, ConvWorkload, make_conv_inputs,
+                                                   seq_idx_from_lengths)
+from tests.gpu_helpers import TOL, normwise_err
+
+pytestmark = pytest.mark.gpu
+
+
+def f64(t):
+    return None if t is None else t.double().cpu().numpy()
+
+
+def run(inputs, act, ws_fill=None):
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inputs.items()}
+    ws = None
+    if ws_fill is not None:
+        x = d["x"]
+        s = conv1d.make_shape(*x.shape, d["weight"].shape[1], act,
+                              0 if x.dtype == torch.bfloat16 else 1)
+        ws = torch.randint(0, 256, (conv1d.workspace_size(s),), dtype=torch.uint8, device="cuda")
+    y = conv1d.conv1d_fwd(d["x"], d["weight"], d["bias"], d["seq_idx"], act)
+    g = conv1d.conv1d_bwd(d["x"], d["weight"], d["bias"], d["seq_idx"], d["dout"], act, workspace=ws)
+    torch.cuda.synchronize()
+    return y, g
+
+
+def oracle_of(inputs, act, channels=None):
+    x, w, bias, dout = (f64(inputs[k]) for k in ("x", "weight", "bias", "dout"))
+    if channels is not None:
+        x, w, dout = x[:, :, channels], w[channels], dout[:, :, channels]
+        bias = None if bias is None else bias[channels]
+    sidx = None if inputs["seq_idx"] is None else inputs["seq_idx"].numpy()
+    return oc.forward(x, w, bias, sidx, act), oc.backward(x, w, bias, sidx, dout, act)
+
+
+def check(inputs, act, tol, label, channels=None):
+    print(f"[case] conv1d {label}", flush=True)
+    y, g = run(inputs, act)
+    y_ref, g_ref = oracle_of(inputs, act, channels)
+    sel = (lambda a: a) if channels is None else (lambda a: a[..., channels])
+    errs = {"y": normwise_err(sel(f64(y)), y_ref), "dx": normwise_err(sel(f64(g["dx"])), g_ref["dx"]),
+            "dweight": normwise_err(f64(g["dweight"])[channels if channels is not None else slice(None)],
+                                    g_ref["dw"])}
+    if inputs["bias"] is not None:
+        errs["dbias"] = normwise_err(f64(g["dbias"])[channels if channels is not None else slice(None)],
+                                     g_ref["dbias"])
+    msg = f"conv1d {label}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items())
+    print(msg, flush=True)
+    for k in ("y", "dx"):
+        assert not torch.isnan(y if k == "y" else g["dx"]).any(), k
+    assert max(errs.values()) <= tol, msg
+
+
+@pytest.mark.parametrize("act", ["silu", "none"])
+def test_tiny_fp32(act):
+    w = CONV_WORKLOADS["conv_tiny_f32"]
+    check(make_conv_inputs(w), act, TOL["f32"], f"{w.name} {act}")
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_fp32_widths_ragged_idle_lanes(W):
+    # 700 rows: three 256-row blocks, the last ragged; 260 fp32 channels: a second channel block of one lane
+    w = ConvWorkload("conv_f32_w", batch=2, seqlen=700, channels=260, width=W, dtype="f32", seed=2100 + W)
+    check(make_conv_inputs(w), "silu", TOL["f32"], f"fp32 W={W} L=700 C=260")
+
+
+def test_fp32_packed_sequences_on_block_and_wave_boundaries():
+    # starts at 63/64/65 (wave boundary), 255/256/257 (block boundary), and sequences of one and two rows
+    lengths = [63, 1, 1, 190, 1, 1, 2, 3, 250, 88]
+    L = sum(lengths)
+    w = ConvWorkload("conv_f32_packed", batch=1, seqlen=L, channels=64, width=4, dtype="f32", seed=2110)
+    inputs = make_conv_inputs(w)
+    inputs["seq_idx"] = seq_idx_from_lengths(lengths)
+    check(inputs, "silu", TOL["f32"], "fp32 packed boundaries")
+
+
+def test_bf16_packed_no_bias_short_rows():
+    w = ConvWorkload("conv_bf16_packed", batch=1, seqlen=1500, channels=1032, width=4, dtype="bf16", seed=2120,
+                     nseqs_packed=5, min_len=3)
+    inputs = make_conv_inputs(w)
+    inputs["bias"] = None
+    check(inputs, "silu", TOL["bf16"], "bf16 packed, no bias, C=1032")
+
+
+@pytest.mark.parametrize("L", [1, 3, 65])
+def test_short_inputs(L):
+    w = ConvWorkload("conv_short", batch=3, seqlen=L, channels=16, width=4, dtype="bf16", seed=2130 + L)
+    check(make_conv_inputs(w), "silu", TOL["bf16"], f"bf16 L={L}, batch 3")
+
+
+def spread_channels(C, n=192, seed=0):
+    """n channels: the first and last 16, the rest drawn over the whole range."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(16, C - 16), n - 32, replace=False)
+    return np.unique(np.concatenate([np.arange(16), np.arange(C - 16, C), mid]))
+
+
+@pytest.mark.parametrize("name", ["conv_bf16_L16384_C10240", "conv_bf16_varlen7_L16384_C4608"])
+def test_full_size_sampled_channels(name):
+    w = CONV_WORKLOADS[name]
+    check(make_conv_inputs(w), w.activation, TOL["bf16"], f"{name} (sampled channels)",
+          channels=spread_channels(w.channels))
+
+
+def test_bitwise_repeatable_with_garbage_workspace():
+    w = ConvWorkload("conv_det", batch=2, seqlen=3000, channels=2048, width=4, dtype="bf16", seed=2140,
+                     nseqs_packed=0)
+    inputs = make_conv_inputs(w)
+    print("[case] conv1d determinism", flush=True)
+    y0, g0 = run(inputs, "silu", ws_fill=True)
+    for _ in range(4):
+        y1, g1 = run(inputs, "silu", ws_fill=True)
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+        assert torch.equal(g0["dx"].view(torch.int16), g1["dx"].view(torch.int16))
+        assert torch.equal(g0["dweight"].view(torch.int32), g1["dweight"].view(torch.int32))
+        assert torch.equal(g0["dbias"].view(torch.int32), g1["dbias"].view(torch.int32))
+
+
+def test_autograd_function_matches_entry_points():
+    w = ConvWorkload("conv_autograd", batch=1, seqlen=900, channels=512, width=4, dtype="bf16", seed=2150,
+                     nseqs_packed=3, min_len=100)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in make_conv_inputs(w).items()}
+    print("[case] conv1d autograd", flush=True)
+    leaves = {k: d[k].clone().requires_grad_(True) for k in ("x", "weight", "bias")}
+    y = conv1d.causal_conv1d(leaves["x"], leaves["weight"], leaves["bias"], d["seq_idx"], "silu")
+    y.backward(d["dout"])
+    ref_y = conv1d.conv1d_fwd(d["x"], d["weight"], d["bias"], d["seq_idx"], "silu")
+    ref = conv1d.conv1d_bwd(d["x"], d["weight"], d["bias"], d["seq_idx"], d["dout"], "silu")
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach().view(torch.int16), ref_y.view(torch.int16))
+    assert torch.equal(leaves["x"].grad.view(torch.int16), ref["dx"].view(torch.int16))
+    assert torch.equal(leaves["weight"].grad.view(torch.int32), ref["dweight"].view(torch.int32))
+    assert torch.equal(leaves["bias"].grad.view(torch.int32), ref["dbias"].view(torch.int32))
