@@ -8,9 +8,9 @@
 // filter has W <= 4 taps), so the kernels are streaming walks, not
 // contractions:
 //
-// * A lane owns 16 bytes of channels (8 bf16 or 4 fp32), a wave 64 lanes
-//   side by side, so every row load or store of a wave is one contiguous
-//   1 KiB piece of a channels-last row.
+// * A lane owns 16 bytes (forward) or 8 bytes (backward) of channels, a
+//   wave 64 lanes side by side, so every row load or store of a wave is one
+//   contiguous 1 KiB or 512-byte piece of a channels-last row.
 // * Each wave walks TT consecutive rows, keeping the last W input rows (and,
 //   in the backward, the last W values of g = dout * act'(pre)) in registers,
 //   with DEPTH rows of loads in flight ahead of the row it computes.  The
@@ -19,7 +19,7 @@
 //   window of W rows that lies in one sequence (nearly all of them) takes
 //   the unmasked path; a window across a sequence start, the first row or
 //   the end of the input takes the masked one.  Both tests are wave-uniform.
-// * Backward: the filter and bias gradients of the block's 4 * TT rows are
+// * Backward: the filter and bias gradients of the block's NWAVE * TT rows are
 //   summed in registers (row order), then over the block's 4 waves in wave
 //   order through LDS, and parked in the block's own slot of the workspace;
 //   k_conv_reduce adds the slots in slot order in double.  No atomics.
@@ -35,40 +35,51 @@ using ssd::bf16_t;
 using ssd::pack_bf16x2;
 
 constexpr int WAVE = 64;
-constexpr int NWAVE = 4;          // waves per block, one run of TT rows each
-constexpr int TT = 64;            // rows per wave
-constexpr int RB = NWAVE * TT;    // rows per block
+constexpr int NWAVE = 4;          // waves per block, one run of rows each
 constexpr int NTHR = NWAVE * WAVE;
-constexpr int DEPTH = 4;          // rows requested ahead of the one computed
 // sequence ids of the rows before the first and past the last (never in the same sequence as a real row)
 constexpr int BEFORE_START = INT32_MIN, PAST_END = INT32_MIN + 1;
 
-template <typename T> struct Io;
-template <> struct Io<bf16_t> {
-  static constexpr int VEC = 8;
-  static __device__ __forceinline__ void unpack(const uint4& u, float (&f)[8]) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Rows per wave, bytes per lane and rows requested ahead (DEPTH) of each walk,
+// from a sweep at L = 16384 and 10240 bf16 channels.  The backward carries
+// more state per lane (the g ring and the gradient sums): with 8 bytes per
+// lane it keeps 3 waves per SIMD, and its longer runs amortise the halo rows
+// and the per-block slot.
+template <bool BWD> struct Walk {
+  static constexpr int TT = BWD ? 128 : 32;
+  static constexpr int NB = BWD ? 8 : 16;
+  static constexpr int DEPTH = BWD ? 4 : 8;
+  static constexpr int RB = NWAVE * TT;   // rows per block
+};
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <int NWD> struct RawT;
+template <> struct RawT<2> { using type = u32x2_t; };
+template <> struct RawT<4> { using type = u32x4_t; };
+
+// A lane's NB bytes of one row: load, store, and conversion to and from fp32
+template <typename T, int NB> struct Io {
+  static constexpr int VEC = NB / static_cast<int>(sizeof(T)), NWD = NB / 4;
+  using raw = typename RawT<NWD>::type;
+  static __device__ __forceinline__ raw load(const T* p) { return *reinterpret_cast<const raw*>(p); }
+  static __device__ __forceinline__ void store(T* p, raw r) { *reinterpret_cast<raw*>(p) = r; }
+  static __device__ __forceinline__ void unpack(raw u, float (&f)[VEC]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int i = 0; i < NWD; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      } else {
+        f[i] = __uint_as_float(u[i]);
+      }
     }
   }
-  static __device__ __forceinline__ uint4 pack(const float (&f)[8]) {
-    return uint4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                 pack_bf16x2(f[6], f[7])};
-  }
-};
-template <> struct Io<float> {
-  static constexpr int VEC = 4;
-  static __device__ __forceinline__ void unpack(const uint4& u, float (&f)[4]) {
-    f[0] = __uint_as_float(u.x);
-    f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z);
-    f[3] = __uint_as_float(u.w);
-  }
-  static __device__ __forceinline__ uint4 pack(const float (&f)[4]) {
-    return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+  static __device__ __forceinline__ raw pack(const float (&f)[VEC]) {
+    raw r;
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) r[i] = sizeof(T) == 2 ? pack_bf16x2(f[2 * i], f[2 * i + 1]) : __float_as_uint(f[i]);
+    return r;
   }
 };
 
@@ -84,12 +95,15 @@ struct Args {
   int ntb;        // row blocks per batch row
 };
 
-// SiLU and its derivative from one exponential
-__device__ __forceinline__ float sigmoid(float p) { return __frcp_rn(1.f + __expf(-p)); }
+// SiLU and its derivative from one exponential and one hardware reciprocal
+// (v_rcp_f32, 1 ulp; an IEEE division would cost about ten instructions per element)
+__device__ __forceinline__ float sigmoid(float p) { return __builtin_amdgcn_rcpf(1.f + __expf(-p)); }
 
 template <typename T, int W, bool SILU, bool BWD>
 __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
-  constexpr int VEC = Io<T>::VEC, CB = WAVE * VEC;
+  using IO = Io<T, Walk<BWD>::NB>;
+  constexpr int TT = Walk<BWD>::TT, RB = Walk<BWD>::RB, DEPTH = Walk<BWD>::DEPTH;
+  constexpr int VEC = IO::VEC, CB = WAVE * VEC;
   constexpr int NSTEP = BWD ? (TT + W - 1 + DEPTH - 1) / DEPTH * DEPTH : TT;
   // rows tb0-(W-1) .. up to the last wave's last step
   constexpr int SEQN = (NWAVE - 1) * TT + NSTEP + W - 1;
@@ -130,7 +144,7 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
 #pragma unroll
   for (int k = 1; k < W; ++k) {
     const int64_t t = t0 - W + k;
-    Io<T>::unpack(*reinterpret_cast<const uint4*>(xb + row(t)), xr[k]);
+    IO::unpack(IO::load(xb + row(t)), xr[k]);
     sr[k] = seq_of(t);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) gr[k][e] = 0.f;
@@ -143,13 +157,18 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
     for (int k = 0; k < W; ++k) dwa[k][e] = 0.f;
   }
 
-  uint4 rx[DEPTH], rd[DEPTH];
+  typename IO::raw rx[DEPTH], rd[DEPTH];
 #pragma unroll
   for (int u = 0; u < DEPTH; ++u) {
-    rx[u] = *reinterpret_cast<const uint4*>(xb + row(t0 + u));
-    if constexpr (BWD) rd[u] = *reinterpret_cast<const uint4*>(db + row(t0 + u));
+    rx[u] = IO::load(xb + row(t0 + u));
+    if constexpr (BWD) rd[u] = IO::load(db + row(t0 + u));
   }
 
+  // next rows to request, and the last row (requests past the end reload it)
+  const T* nx = xb + (t0 + DEPTH) * C;
+  const T* nd = BWD ? db + (t0 + DEPTH) * C : nullptr;
+  const T* xlast = xb + (L - 1) * C;
+  const T* dlast = BWD ? db + (L - 1) * C : nullptr;
   for (int s0 = 0; s0 < NSTEP; s0 += DEPTH) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
@@ -164,13 +183,24 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
           gr[k][e] = gr[k + 1][e];
         }
       }
-      Io<T>::unpack(rx[u], xr[W - 1]);
+      IO::unpack(rx[u], xr[W - 1]);
       float dv[VEC];
-      if constexpr (BWD) Io<T>::unpack(rd[u], dv);
+      if constexpr (BWD) IO::unpack(rd[u], dv);
       sr[W - 1] = seq_of(t);
       // next request into the slot just consumed (past the end: a clamped, unused row)
-      rx[u] = *reinterpret_cast<const uint4*>(xb + row(t + DEPTH));
-      if constexpr (BWD) rd[u] = *reinterpret_cast<const uint4*>(db + row(t + DEPTH));
+      // (kept after the unpacks above, so that the request can reuse their registers:
+      // a request issued before them would leave a copy, and a wait, at the loop's end)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        asm volatile("" : "+v"(xr[W - 1][e]));
+        if constexpr (BWD) asm volatile("" : "+v"(dv[e]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const bool in = t + DEPTH < L;
+      rx[u] = IO::load(in ? nx : xlast);
+      if constexpr (BWD) rd[u] = IO::load(in ? nd : dlast);
+      nx += C;
+      if constexpr (BWD) nd += C;
 
       bool uni = true;
 #pragma unroll
@@ -197,7 +227,7 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
           float o[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) o[e] = SILU ? pre[e] * sigmoid(pre[e]) : pre[e];
-          *reinterpret_cast<uint4*>(yb + t * C) = Io<T>::pack(o);
+          IO::store(yb + t * C, IO::pack(o));
         }
       } else {
         const bool live = t < L;                         // g past the end is zero
@@ -215,8 +245,13 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             dba[e] += g[e];
+            if (uni) {
 #pragma unroll
-            for (int k = 0; k < W; ++k) dwa[k][e] = fmaf(g[e] * keep[k], xr[k][e], dwa[k][e]);
+              for (int k = 0; k < W; ++k) dwa[k][e] = fmaf(g[e], xr[k][e], dwa[k][e]);
+            } else {
+#pragma unroll
+              for (int k = 0; k < W; ++k) dwa[k][e] = fmaf(g[e] * keep[k], xr[k][e], dwa[k][e]);
+            }
           }
         }
 #pragma unroll
@@ -228,14 +263,19 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             float acc = 0.f;
+            if (uni) {
 #pragma unroll
-            for (int k = 0; k < W; ++k) {
-              const float m = (uni || sr[W - 1 - k] == sr[0]) ? 1.f : 0.f;
-              acc = fmaf(wt[k][e] * m, gr[W - 1 - k][e], acc);
+              for (int k = 0; k < W; ++k) acc = fmaf(wt[k][e], gr[W - 1 - k][e], acc);
+            } else {
+#pragma unroll
+              for (int k = 0; k < W; ++k) {
+                const float m = sr[W - 1 - k] == sr[0] ? 1.f : 0.f;
+                acc = fmaf(wt[k][e] * m, gr[W - 1 - k][e], acc);
+              }
             }
             o[e] = acc;
           }
-          *reinterpret_cast<uint4*>(yb + tx * C) = Io<T>::pack(o);
+          IO::store(yb + tx * C, IO::pack(o));
         }
       }
     }
@@ -277,7 +317,8 @@ __global__ __launch_bounds__(256) void k_conv_reduce(const float* part, int64_t 
   }
 }
 
-int64_t row_blocks(const conv1d_shape& s) { return (s.seqlen + RB - 1) / RB; }
+template <bool BWD>
+int64_t row_blocks(const conv1d_shape& s) { return (s.seqlen + Walk<BWD>::RB - 1) / Walk<BWD>::RB; }
 
 int check(const conv1d_shape* s) {
   if (!s || s->reserved != 0) return SSD_ERR_INVALID_ARG;
@@ -287,7 +328,7 @@ int check(const conv1d_shape* s) {
   if (s->io_dtype != SSD_IO_BF16 && s->io_dtype != SSD_IO_F32) return SSD_ERR_UNSUPPORTED_SHAPE;
   const int vec = s->io_dtype == SSD_IO_BF16 ? 8 : 4;
   if (s->channels % vec != 0) return SSD_ERR_UNSUPPORTED_SHAPE;
-  if (s->batch > 65535 || row_blocks(*s) > 65535) return SSD_ERR_UNSUPPORTED_SHAPE;
+  if (s->batch > 65535 || row_blocks<false>(*s) > 65535) return SSD_ERR_UNSUPPORTED_SHAPE;
   return SSD_OK;
 }
 
@@ -295,8 +336,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <typename T, int W, bool SILU, bool BWD>
 void launch(const conv1d_shape& s, const Args& a, hipStream_t st) {
-  constexpr int CB = WAVE * Io<T>::VEC;
-  const dim3 grid(static_cast<unsigned>((s.channels + CB - 1) / CB), static_cast<unsigned>(row_blocks(s)),
+  constexpr int CB = WAVE * Io<T, Walk<BWD>::NB>::VEC;
+  const dim3 grid(static_cast<unsigned>((s.channels + CB - 1) / CB), static_cast<unsigned>(row_blocks<BWD>(s)),
                   static_cast<unsigned>(s.batch));
   hipLaunchKernelGGL((k_conv<T, W, SILU, BWD>), grid, dim3(NTHR), 0, st, a);
 }
@@ -319,7 +360,7 @@ int conv1d_bwd_workspace_size(const conv1d_shape* shape, size_t* bytes) {
   const int rc = conv::check(shape);
   if (rc != SSD_OK) return rc;
   if (!bytes) return SSD_ERR_INVALID_ARG;
-  *bytes = static_cast<size_t>(shape->batch * conv::row_blocks(*shape)) * (shape->width + 1) *
+  *bytes = static_cast<size_t>(shape->batch * conv::row_blocks<true>(*shape)) * (shape->width + 1) *
            static_cast<size_t>(shape->channels) * sizeof(float);
   return SSD_OK;
 }
@@ -332,7 +373,7 @@ int conv1d_fwd(const conv1d_shape* shape, const void* x, const float* weight, co
   if (!conv::aligned16(x) || !conv::aligned16(out)) return SSD_ERR_MISALIGNED;
   if (out == x) return SSD_ERR_INVALID_ARG;
   conv::Args a{x, weight, bias, seq_idx, nullptr, out, nullptr, shape->seqlen, shape->channels,
-               static_cast<int>(conv::row_blocks(*shape))};
+               static_cast<int>(conv::row_blocks<false>(*shape))};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (shape->io_dtype == SSD_IO_BF16) {
     conv::dispatch<ssd::bf16_t, false>(*shape, a, st);
@@ -353,7 +394,7 @@ int conv1d_bwd(const conv1d_shape* shape, const void* x, const float* weight, co
   if (!conv::aligned16(x) || !conv::aligned16(dout) || !conv::aligned16(dx) || !conv::aligned16(workspace))
     return SSD_ERR_MISALIGNED;
   if (dx == x || dx == dout) return SSD_ERR_INVALID_ARG;
-  const int64_t ntb = conv::row_blocks(*shape);
+  const int64_t ntb = conv::row_blocks<true>(*shape);
   conv::Args a{x, weight, bias, seq_idx, dout, dx, static_cast<float*>(workspace), shape->seqlen,
                shape->channels, static_cast<int>(ntb)};
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -29,8 +29,8 @@ def test_library_exports_every_declared_function():
 
 def test_workspace_size():
     s = conv1d.make_shape(2, 1000, 96, 4, "silu", ssd.SSD_IO_F32)
-    # one slot of (width + 1) * channels floats per 256-row block of each batch row
-    assert conv1d.workspace_size(s) == 2 * 4 * 5 * 96 * 4
+    # one slot of (width + 1) * channels floats per 512-row block of each batch row
+    assert conv1d.workspace_size(s) == 2 * 2 * 5 * 96 * 4
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,8 +1,8 @@
 """GPU parity of the causal-conv1d forward and deterministic backward with the fp64 oracle.
 
-Small cases (several 256-row blocks, ragged tails, idle lanes in the last
-channel block, packed sequences starting on and next to block and wave
-boundaries) compare every element; the full-size xBC workloads, in the launch
+Small cases (several row blocks of each walk, ragged tails, idle lanes in
+the last channel block, packed sequences starting on and next to block and
+wave boundaries) compare every element; the full-size xBC workloads, in the launch
 configuration the benchmark times, compare a spread of channels over the
 whole sequence (channels are independent, so the oracle evaluates only
 those).  Repeated calls with garbage workspaces must agree bit for bit.
@@ -73,14 +73,16 @@ def test_tiny_fp32(act):
 
 @pytest.mark.parametrize("W", [2, 3, 4])
 def test_fp32_widths_ragged_idle_lanes(W):
-    # 700 rows: three 256-row blocks, the last ragged; 260 fp32 channels: a second channel block of one lane
-    w = ConvWorkload("conv_f32_w", batch=2, seqlen=700, channels=260, width=W, dtype="f32", seed=2100 + W)
-    check(make_conv_inputs(w), "silu", TOL["f32"], f"fp32 W={W} L=700 C=260")
+    # 1300 rows: three 512-row blocks of the backward walk (eleven 128-row blocks of the forward), the last
+    # ragged; 260 fp32 channels: a last channel block with one (forward) or two (backward) busy lanes
+    w = ConvWorkload("conv_f32_w", batch=2, seqlen=1300, channels=260, width=W, dtype="f32", seed=2100 + W)
+    check(make_conv_inputs(w), "silu", TOL["f32"], f"fp32 W={W} L=1300 C=260")
 
 
 def test_fp32_packed_sequences_on_block_and_wave_boundaries():
-    # starts at 63/64/65 (wave boundary), 255/256/257 (block boundary), and sequences of one and two rows
-    lengths = [63, 1, 1, 190, 1, 1, 2, 3, 250, 88]
+    # starts at 31/32/33 (a forward wave boundary), 127/128/129 (forward block, backward wave),
+    # 511/512/513 (backward block), and sequences of one, two and three rows
+    lengths = [31, 1, 1, 94, 1, 1, 382, 1, 1, 2, 3, 200]
     L = sum(lengths)
     w = ConvWorkload("conv_f32_packed", batch=1, seqlen=L, channels=64, width=4, dtype="f32", seed=2110)
     inputs = make_conv_inputs(w)
