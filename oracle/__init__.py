@@ -86,7 +86,7 @@ class Oracle:
             lib.ssdo_backward.restype = ctypes.c_int
             lib.ssdo_backward.argtypes = ([ctypes.POINTER(_Shape)] + [dp] * 7 + [ip, dp] +
                                           [ctypes.c_int64, ctypes.c_int64] + [dp] * 7 +
-                                          [ctypes.c_int64, dp, dp, ctypes.c_int])
+                                          [ctypes.c_int64, dp, dp, dp, ctypes.c_int])
             self.__dict__["_lib"] = lib
         return self.__dict__["_lib"]
 
@@ -118,8 +118,11 @@ class Oracle:
         return (y, fs) if return_final_states else y
 
     def backward(self, x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, head_lo=0,
-                 head_hi=None, chunk=0, nthreads=None, want_d_initial=True, partial_groups=False):
-        """All gradients of l = sum(dy * y) in fp64.
+                 head_hi=None, chunk=0, nthreads=None, want_d_initial=True, partial_groups=False,
+                 d_last=None):
+        """All gradients of l = sum(dy * y) in fp64 (plus <d_last[b], h_{L-1}> per batch row when
+        ``d_last`` (B, H, P, N) is given: the gradient handed back for the state after each row's
+        last position).
 
         Returns a dict with dx, ddt, dA, dB, dC, dD, d_initial_states (None when
         not requested) and, when ``chunk`` > 0, ``chunk_states`` / ``chunk_dout``
@@ -128,7 +131,7 @@ class Oracle:
         every head of a group; with ``partial_groups`` a range may split
         groups and dB/dC of those groups stay NaN.
         """
-        x, dt, A, B, C, D, dy, h0 = map(_f64, (x, dt, A, B, C, D, dy, initial_states))
+        x, dt, A, B, C, D, dy, h0, d_last = map(_f64, (x, dt, A, B, C, D, dy, initial_states, d_last))
         si = _i32(seq_idx)
         s = self._shape(x, B, h0, si)
         if head_hi is None:
@@ -154,7 +157,7 @@ class Oracle:
             _dptr(h0), _iptr(si), _dptr(dy), head_lo, head_hi, _dptr(out["dx"]),
             _dptr(out["ddt"]), _dptr(out["dA"]), _dptr(out["dB"]), _dptr(out["dC"]),
             _dptr(out["dD"]), _dptr(out["d_initial_states"]), chunk, _dptr(cs), _dptr(cd),
-            nthreads or default_threads())
+            _dptr(d_last), nthreads or default_threads())
         if rc:
             raise RuntimeError(f"ssdo_backward failed: {rc}")
         if chunk:

@@ -21,10 +21,14 @@
  *       a_t  = dt_t * A_h
  *       h_t  = exp(a_t) * h_{t-1} + dt_t * x_t (outer) B_t     (P x N)
  *       y_t  = h_t C_t + D_h * x_t                              (P)
- *   The loss whose gradients are returned is  l = sum_t dy_t . y_t.
+ *   The loss whose gradients are returned is  l = sum_t dy_t . y_t, plus
+ *   <d_last[b], h_{L-1}>_F for every batch row b when d_last is given (the
+ *   gradient that arrives for the state after a row's last position, which is
+ *   what a later stretch of the same sequence hands back).
  *
  * Reverse adjoint, lambda_t = dl/dh_t, running t downwards:
  *       lambda_t = dy_t (outer) C_t + [t+1 in same sequence] exp(a_{t+1}) lambda_{t+1}
+ *                  (+ d_last[b] at t = L-1)
  *       dC_t  += h_t^T dy_t                    (summed over the heads of a group)
  *       dx_t   = dt_t lambda_t B_t + D_h dy_t
  *       dB_t  += dt_t lambda_t^T x_t           (summed over the heads of a group)
@@ -86,7 +90,7 @@ static int64_t find_sequences(const ssdo_shape* s, const int32_t* seq_idx,
 
 typedef struct {
   const ssdo_shape* s;
-  const double *x, *dt, *A, *B, *C, *D, *h0, *dy;
+  const double *x, *dt, *A, *B, *C, *D, *h0, *dy, *d_last;
   const uint8_t* start;
   const int64_t* seq;
   int64_t head_lo, head_hi;
@@ -194,8 +198,11 @@ static void backward_item(ctx_t* c, int64_t item, int64_t b, int64_t h,
   }
 
   /* Reverse sweep.  lam holds the carry [t+1 same seq] exp(a_{t+1}) lambda_{t+1}
-   * on entry to position t. */
-  memset(lam, 0, sizeof(double) * PN);
+   * on entry to position t; on entry to L-1 it is d_last[b] (zero without it). */
+  if (c->d_last)
+    memcpy(lam, c->d_last + ((b * s->nheads + h) * PN), sizeof(double) * PN);
+  else
+    memset(lam, 0, sizeof(double) * PN);
   double dA_acc = 0.0, dD_acc = 0.0;
   for (int64_t k = nblk - 1; k >= 0; --k) {
     const int64_t t0 = k * CKPT, t1 = (t0 + CKPT < L) ? t0 + CKPT : L;
@@ -372,6 +379,8 @@ int ssdo_forward(const ssdo_shape* s, const double* x, const double* dt, const d
  * Outputs (all fp64, caller-owned, written only for the covered heads/groups):
  *   dx (B,L,H,P), ddt (B,L,H), dA (H), dB (B,L,G,N), dC (B,L,G,N), dD (H),
  *   d_h0 (S,H,P,N, nullable).
+ *   d_last (B,H,P,N, nullable): gradient input for the state after position
+ *   L-1 of each batch row (the final state of the row's last sequence).
  * Optional exports for chunk-level checks (chunk > 0):
  *   chunk_states (B,nc,H,P,N): state after position c*chunk - 1 (zeros for c=0),
  *   chunk_dout  (B,nc,H,P,N): gradient w.r.t. the state at the end of chunk c
@@ -382,7 +391,7 @@ int ssdo_backward(const ssdo_shape* s, const double* x, const double* dt, const 
                   const int32_t* seq_idx, const double* dy, int64_t head_lo, int64_t head_hi,
                   double* dx, double* ddt, double* dA, double* dB, double* dC, double* dD,
                   double* d_h0, int64_t chunk, double* chunk_states, double* chunk_dout,
-                  int nthreads) {
+                  const double* d_last, int nthreads) {
   if (check_shape(s) || !x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB ||
       !dC || !dD)
     return SSDO_EINVAL;
@@ -404,6 +413,7 @@ int ssdo_backward(const ssdo_shape* s, const double* x, const double* dt, const 
   if (find_sequences(s, seq_idx, st, sq) != s->nseqs) goto done;
   c.s = s; c.x = x; c.dt = dt; c.A = A; c.B = B; c.C = C; c.D = D; c.h0 = h0; c.dy = dy;
   c.start = st; c.seq = sq; c.head_lo = head_lo; c.head_hi = head_hi;
+  c.d_last = d_last;
   c.dx = dx; c.ddt = ddt; c.dA_part = dAp; c.dD_part = dDp; c.d_h0 = d_h0;
   c.dB_item = dBi; c.dC_item = dCi;
   c.chunk = chunk; c.chunk_states = chunk_states; c.chunk_dout = chunk_dout;
