@@ -157,6 +157,10 @@ typedef struct {
   int32_t dt_softplus;   /* nonzero: softplus after the bias */
   float dt_min, dt_max;  /* clamp of the activated value */
   int32_t d_per_channel; /* nonzero: D and dD are (nheads, headdim): y += D[h, p] x[.., h, p] */
+  /* (batch, nheads, headdim, dstate) fp32 device pointer, or NULL; read by ssd_bwd_ex only:
+   * the gradient arriving for the state after position seqlen-1 of each batch row (the final
+   * state of the row's last sequence).  The loss becomes l + sum_b <d_last_states[b], h_{L-1}>. */
+  const float* d_last_states;
 } ssd_options;
 
 /*
@@ -179,6 +183,14 @@ typedef struct {
  *
  * The gate is not on the pages either: it is the output gate of the usual
  * Mamba-2 layer, the second half of the same "next" step as the front-end.
+ *
+ * d_last_states is what a split of the sequence axis needs (a stretch of a
+ * sequence on one device, the rest on the next): the later stretch starts
+ * from this stretch's last states (initial_states) and hands back their
+ * gradient (its d_initial_states), which enters here; chained that way the
+ * stretches' gradients are those of the whole sequence.  No page describes
+ * the hand-off; it follows from the recurrence above (the adjoint of the
+ * state after the stretch's last position).
  * Everything else is as for ssd_fwd / ssd_bwd, including the workspace size.
  */
 int ssd_fwd_ex(const ssd_shape* shape, const ssd_options* opt, const void* x, const float* dt,

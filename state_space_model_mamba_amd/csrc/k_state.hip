@@ -324,9 +324,21 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     return u;
   };
 
+  // the gradient at the end of the last chunk: zero, or the one handed in for the
+  // state after the row's last position (padded positions leave the state unchanged)
   f32x4_t dout[Cf::TPW];
 #pragma unroll
-  for (int k = 0; k < Cf::TPW; ++k) dout[k] = zero4();
+  for (int k = 0; k < Cf::TPW; ++k) {
+    dout[k] = zero4();
+    const int tile = w + Cf::NW * k;
+    if (pb.dlast && tile < Cf::NTILE) {
+      const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        dout[k][r] = pb.dlast[((static_cast<int64_t>(b) * pb.H + h) * P + pt * 16 + 4 * kg + r) * pb.N + n0 +
+                              nt * 16 + r16];
+    }
+  }
   request(pb.nc - 1);
   Upd cur = stage(pb.nc - 1, 0);
   request(pb.nc - 2);

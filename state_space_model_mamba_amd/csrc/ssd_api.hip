@@ -169,6 +169,7 @@ int fill_frontend(const ssd_options* fe, ssd::Problem& pb) {
   pb.dt_softplus = 0;
   pb.dt_min = -__builtin_inff();
   pb.dt_max = __builtin_inff();
+  pb.dlast = nullptr;
   if (!fe) return SSD_OK;
   if (!(fe->dt_min <= fe->dt_max)) return SSD_ERR_INVALID_ARG;   // (also rejects NaN)
   if (fe->dt_bias && !aligned16(fe->dt_bias)) return SSD_ERR_MISALIGNED;
@@ -178,6 +179,7 @@ int fill_frontend(const ssd_options* fe, ssd::Problem& pb) {
   pb.dt_max = fe->dt_max;
   pb.fe = pb.dt_bias || pb.dt_softplus || pb.dt_min > -__builtin_inff() || pb.dt_max < __builtin_inff();
   pb.d_hp = fe->d_per_channel != 0;
+  pb.dlast = fe->d_last_states;
   return SSD_OK;
 }
 

@@ -45,6 +45,7 @@ struct Problem {
   // dt front-end (fe = 0: dt is used as given)
   int fe;                // nonzero when any of the three below applies
   const float* dt_bias;  // (H) or nullptr
+  const float* dlast;    // (B, H, P, N) gradient of each row's state after position L-1, or nullptr
   int dt_softplus;
   float dt_min, dt_max;
   float* ddt_bias;       // (H) output, nullable

@@ -35,7 +35,8 @@ class SsdShape(ctypes.Structure):
 
 class SsdOptions(ctypes.Structure):
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
-                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float), ("d_per_channel", ctypes.c_int32)]
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float), ("d_per_channel", ctypes.c_int32),
+                ("d_last_states", ctypes.c_void_p)]
 
 
 class SsdError(RuntimeError):
@@ -128,15 +129,17 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev):
-    """The C options struct (dt front-end, per-channel D), or None when it would change nothing."""
+def _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last=None):
+    """The C options struct (dt front-end, per-channel D, last-state gradient), or None when it
+    would change nothing."""
     lo, hi = float(dt_limit[0]), float(dt_limit[1])
     per_channel = D is not None and D.dim() == 2
     _check(D, "D", torch.float32, (H, P) if per_channel else (H,), dev)
-    if dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf and not per_channel:
+    if (dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf and not per_channel
+            and d_last is None):
         return None
     _check(dt_bias, "dt_bias", torch.float32, (H,), dev)
-    return SsdOptions(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, 1 if per_channel else 0)
+    return SsdOptions(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, 1 if per_channel else 0, _ptr(d_last))
 
 
 def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
@@ -149,7 +152,8 @@ def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
 def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_d_initial_states: bool = True,
             workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None,
-            dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf), z=None):
+            dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf), z=None,
+            d_last_states=None):
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
@@ -162,7 +166,9 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     ``dt_bias`` (H,) fp32, ``dt_softplus`` and ``dt_limit`` = (min, max): the dt
     front-end of include/ssd_bwd.h (dt is then the raw input); with dt_bias the
     dict also holds ddt_bias.  ``z`` (like x): the output gate; dy is then the
-    gradient of y * silu(z) and the dict also holds dz.
+    gradient of y * silu(z) and the dict also holds dz.  ``d_last_states``
+    (b, H, P, N) fp32: the gradient handed in for the state after each row's
+    last position (the hand-off of a sequence split across calls).
     """
     lib = load_library()
     dev = x.device
@@ -189,7 +195,8 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     _check(A, "A", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
-    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev)
+    _check(d_last_states, "d_last_states", torch.float32, (b, H, P, N), dev)
+    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last_states)
     _check(z, "z", io, (b, L, H, P), dev)
     if (fe is not None or z is not None) and events is not None:
         raise ValueError("stage events are not available with the dt front-end or the gate")
