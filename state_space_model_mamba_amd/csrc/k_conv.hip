@@ -302,14 +302,27 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
   }
 }
 
-// dweight[c][k] and dbias[c]: the slots added in slot order, in double
-__global__ __launch_bounds__(256) void k_conv_reduce(const float* part, int64_t nslot, int64_t C, int W,
-                                                     float* dw, float* dbias) {
+// dweight[c][k] and dbias[c]: the slots added in slot order, in double.  Small
+// blocks spread the (W + 1) * C sums over every CU; the slot loads are issued
+// eight at a time ahead of their (ordered) adds.
+constexpr int RED_THR = 64;
+__global__ __launch_bounds__(RED_THR) void k_conv_reduce(const float* part, int64_t nslot, int64_t C, int W,
+                                                         float* dw, float* dbias) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= (W + 1) * C) return;
   const int64_t k = i / C, c = i % C;
+  const int64_t stride = (W + 1) * C;
+  const float* p = part + k * C + c;
   double acc = 0.0;
-  for (int64_t s = 0; s < nslot; ++s) acc += static_cast<double>(part[(s * (W + 1) + k) * C + c]);
+  int64_t s = 0;
+  for (; s + 8 <= nslot; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += static_cast<double>(v[j]);
+  }
+  for (; s < nslot; ++s) acc += static_cast<double>(p[s * stride]);
   if (k < W) {
     dw[c * W + k] = static_cast<float>(acc);
   } else if (dbias) {
@@ -404,7 +417,8 @@ int conv1d_bwd(const conv1d_shape* shape, const void* x, const float* weight, co
     conv::dispatch<float, true>(*shape, a, st);
   }
   const int64_t n = (shape->width + 1) * shape->channels;
-  hipLaunchKernelGGL(conv::k_conv_reduce, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(conv::k_conv_reduce, dim3(static_cast<unsigned>((n + conv::RED_THR - 1) / conv::RED_THR)),
+                     dim3(conv::RED_THR), 0, st,
                      static_cast<const float*>(workspace), shape->batch * ntb, shape->channels, shape->width,
                      dweight, dbias);
   return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
