@@ -167,8 +167,12 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
   // next rows to request, and the last row (requests past the end reload it)
   const T* nx = xb + (t0 + DEPTH) * C;
   const T* nd = BWD ? db + (t0 + DEPTH) * C : nullptr;
-  const T* xlast = xb + (L - 1) * C;
-  const T* dlast = BWD ? db + (L - 1) * C : nullptr;
+  // the last row this wave reads (its run, plus W-1 rows of g for the backward); requests
+  // past it reload that row instead, which is already in the cache, rather than pull the
+  // next run's rows from HBM ahead of the wave that reads them
+  const int64_t tend = min(L, t0 + (BWD ? TT + W - 1 : TT)) - 1;
+  const T* xlast = xb + tend * C;
+  const T* dlast = BWD ? db + tend * C : nullptr;
   for (int s0 = 0; s0 < NSTEP; s0 += DEPTH) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
       float dv[VEC];
       if constexpr (BWD) IO::unpack(rd[u], dv);
       sr[W - 1] = seq_of(t);
-      // next request into the slot just consumed (past the end: a clamped, unused row)
+      // next request into the slot just consumed (past the run: a reload of its last row)
       // (kept after the unpacks above, so that the request can reuse their registers:
       // a request issued before them would leave a copy, and a wait, at the loop's end)
 #pragma unroll
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
         if constexpr (BWD) asm volatile("" : "+v"(dv[e]));
       }
       __builtin_amdgcn_sched_barrier(0);
-      const bool in = t + DEPTH < L;
+      const bool in = t + DEPTH <= tend;
       rx[u] = IO::load(in ? nx : xlast);
       if constexpr (BWD) rd[u] = IO::load(in ? nd : dlast);
       nx += C;
