@@ -267,7 +267,27 @@ def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup, z=None):
             "bitwise_repeat": same}
 
 
-def measure_conv1d(torch, steps, warmup, dev):
+def conv_cpu_baseline(cw, inputs, channels=10240):
+    """The fp64 conv oracle (forward and backward) on the host, over the first `channels` channels of
+    the same inputs (channels are independent); tokens/s scaled by that fraction of the channels."""
+    import numpy as np
+    from oracle import conv1d as oc
+    c1 = min(channels, cw.channels)
+    x = inputs["x"][:, :, :c1].double().numpy()
+    dout = inputs["dout"][:, :, :c1].double().numpy()
+    w, b = inputs["weight"][:c1].double().numpy(), inputs["bias"][:c1].double().numpy()
+    sidx = None if inputs["seq_idx"] is None else inputs["seq_idx"].numpy()
+    t0 = time.perf_counter()
+    oc.forward(x, w, b, sidx, cw.activation)
+    oc.backward(x, w, b, sidx, dout, cw.activation)
+    dt = time.perf_counter() - t0
+    return {"value": cw.tokens * (c1 / cw.channels) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"all {cw.tokens} tokens of channels 0..{c1 - 1} (forward and backward); tokens/s scaled "
+                      f"by {c1}/{cw.channels} of the channels"}
+
+
+def measure_conv1d(torch, steps, warmup, dev, cpu=False):
     """The xBC causal convolution of the headline layer (conv1d_fwd, conv1d_bwd), each timed
     over `steps` calls with HIP events on the current stream.
 
@@ -277,7 +297,8 @@ def measure_conv1d(torch, steps, warmup, dev):
     from state_space_model_mamba_amd import conv1d
     from state_space_model_mamba_amd.workloads import CONV_HEADLINE, CONV_WORKLOADS, make_conv_inputs
     cw = CONV_WORKLOADS[CONV_HEADLINE]
-    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_conv_inputs(cw).items()}
+    ci = make_conv_inputs(cw)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in ci.items()}
     shape = conv1d.make_shape(cw.batch, cw.seqlen, cw.channels, cw.width, cw.activation,
                               0 if cw.dtype == "bf16" else 1)
     ws = torch.empty(conv1d.workspace_size(shape), dtype=torch.uint8, device=dev)
@@ -315,6 +336,8 @@ def measure_conv1d(torch, steps, warmup, dev):
     fwd()
     bwd()
     torch.cuda.synchronize()
+    if cpu:
+        res["cpu_baseline"] = conv_cpu_baseline(cw, ci)
     res["bitwise_repeat"] = (torch.equal(y0.view(torch.int16), y.view(torch.int16))
                              and torch.equal(g0["dx"].view(torch.int16), g["dx"].view(torch.int16))
                              and torch.equal(g0["dweight"].view(torch.int32), g["dweight"].view(torch.int32))
@@ -461,7 +484,7 @@ def main():
         del z
     if not args.no_conv and not args.no_options:
         res["causal_conv1d"] = measure_conv1d(torch, steps=min(args.steps, 100), warmup=min(args.warmup, 10),
-                                              dev=dev)
+                                              dev=dev, cpu=not args.no_cpu_baseline)
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:
