@@ -42,6 +42,7 @@ def sizes(w, ntg):
         DINIT=S * w.nheads * w.headdim * w.dstate * 4,
         SEQ=w.batch * w.seqlen * 4 if w.nseqs_packed else 0,
         T=w.batch * w.nheads * nc * w.headdim * w.dstate * s,      # Hin or dS (I/O dtype)
+        T32=w.batch * w.nheads * nc * w.headdim * w.dstate * 4,    # Hin or dS at fp32
         CH=w.batch * w.nheads * nc * w.chunk * 4,                  # one per-chunk fp32 vector
         OFFD=w.batch * w.nheads * nc * ntg * w.chunk * 4,
         SEG=w.batch * nc * w.chunk * 4,
@@ -52,9 +53,17 @@ def sizes(w, ntg):
     return z
 
 
-def step_alg_bytes(z):
-    """Compulsory I/O plus one write and one read of the chunk states and state gradients."""
-    return 3 * z["X"] + 4 * z["BC"] + 2 * z["DT"] + z["INIT"] + z["DINIT"] + z["SEQ"] + 4 * z["T"]
+def step_alg_bytes(z, state_bytes="fp32"):
+    """Compulsory I/O plus one write and one read of the chunk states Hin and the state
+    gradients dS -- counted at fp32 (the algorithmic model: the chunked method's published
+    states) or as this library stores them (the I/O dtype)."""
+    T = z["T32"] if state_bytes == "fp32" else z["T"]
+    return step_compulsory_bytes(z) + 4 * T
+
+
+def step_compulsory_bytes(z):
+    """Read x, dy, B, C, dt (and h0, seq_idx); write dx, dB, dC, ddt (and d_init)."""
+    return 3 * z["X"] + 4 * z["BC"] + 2 * z["DT"] + z["INIT"] + z["DINIT"] + z["SEQ"]
 
 
 def stage_alg_bytes(z):
@@ -68,6 +77,12 @@ def stage_alg_bytes(z):
         "head_bwd": 3 * z["X"] + z["BC"] + z["T"] + z["CBT"] + 2 * z["CH"] + z["OFFD"] + z["DT"],
         "reduce": 0,
     }
+
+
+def head_alg_bytes(z):
+    """What the per-head kernel must touch by the method: read x, dy, B, C (for C B^T), dS (at
+    fp32), dt; write dx, ddt.  Design intermediates (stored C B^T tiles, ddA partials) excluded."""
+    return 3 * z["X"] + 2 * z["BC"] + z["T32"] + 2 * z["DT"]
 
 
 def forward_alg_bytes(z, fin):
@@ -178,6 +193,18 @@ def ingest_counters(fetch_csv, write_csv, workload, out_path=TRAFFIC_FILE):
     return rec
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inputs, groups=1):
     """The fp64 oracle on the heads of `groups` groups of the workload (all tokens)."""
     import numpy as np
@@ -204,7 +231,7 @@ def cpu_baseline(w, inputs, groups=1):
     dt = time.perf_counter() - t0
     frac = h1 / w.nheads
     return {"value": w.tokens * frac / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "seconds": round(dt, 3),
             "sample": (f"all {w.tokens} tokens, all {w.nheads} heads" if h1 == w.nheads else
                        f"all {w.tokens} tokens of heads 0..{h1 - 1} ({groups} of {w.ngroups} groups); "
                        f"tokens/s scaled by {h1}/{w.nheads} of the heads")}
@@ -345,6 +372,96 @@ def measure_conv1d(torch, steps, warmup, dev, cpu=False):
     return res
 
 
+def _bits(t):
+    return t.view(torch_int_view(t))
+
+
+def torch_int_view(t):
+    import torch
+    return {2: torch.int16, 4: torch.int32}[t.element_size()]
+
+
+def measure_backward(torch, ssd, w, steps, warmup, dev, stages=True):
+    """Time `steps` ssd_bwd calls on workload w (after `warmup` untimed calls) with HIP events
+    on the call's stream: the whole timed region (mean) and every call (median, min).  Then,
+    outside the timed region, per-stage times from the profiling entry point.  Returns the
+    measurement, the inputs and the per-stage algorithmic bytes."""
+    from state_space_model_mamba_amd.workloads import make_inputs
+    inputs = make_inputs(w)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.items()}
+    S = d["initial_states"].shape[0] if d.get("initial_states") is not None else (w.nseqs_packed or w.batch)
+    shape = ssd.shape_of(d["x"], d["B"], w.chunk, S)
+    ws = torch.empty(ssd.workspace_size(shape), dtype=torch.uint8, device=dev)
+    H, P, N = w.nheads, w.headdim, w.dstate
+    out = {"dx": torch.empty_like(d["x"]), "ddt": torch.empty_like(d["dt"]),
+           "dA": torch.empty(H, device=dev), "dB": torch.empty_like(d["B"]),
+           "dC": torch.empty_like(d["C"]), "dD": torch.empty(H, device=dev),
+           "d_initial_states": torch.empty((S, H, P, N), device=dev)}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dy"],
+                    initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
+                    nseqs=S, workspace=ws, out=out, events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(steps):
+        step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    mean_ms = ev[0].elapsed_time(ev[steps]) / steps
+    bitwise = all(torch.equal(_bits(out[k]), _bits(ref[k])) for k in out)
+    stage_ms = None
+    if stages:
+        # per-stage times from a second pass, with the library recording an
+        # event between stages (kept out of the timed region above)
+        names = ssd.stage_names()
+        nprof = max(1, min(steps, 50))
+        ev_steps = [ssd.make_stage_events(stream) for _ in range(nprof)]
+        torch.cuda.synchronize()
+        for k in range(nprof):
+            step(ev_steps[k])
+        torch.cuda.synchronize()
+        stage_ms = {n: 0.0 for n in names}
+        for evs in ev_steps:
+            for i, n in enumerate(names):
+                stage_ms[n] += evs[i].elapsed_time(evs[i + 1]) / nprof
+    ntg = N // next(t for t in (128, 64, 32, 16) if N % t == 0)
+    z = sizes(w, ntg)
+    alg = step_alg_bytes(z, "fp32")
+    alg_io = step_alg_bytes(z, "io")
+    comp = step_compulsory_bytes(z)
+    med = per_call[len(per_call) // 2]
+    rec = {
+        "workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": H, "headdim": P,
+        "ngroups": w.ngroups, "dstate": N, "chunk": w.chunk, "nseqs": S, "initial_states": w.h0_std > 0,
+        "dtype": w.dtype, "steps": steps, "warmup": warmup,
+        "ms_per_layer": {"mean": mean_ms, "median": med, "min": per_call[0], "max": per_call[-1]},
+        "tokens_per_s": {"mean": w.tokens / (mean_ms * 1e-3), "median": w.tokens / (med * 1e-3),
+                         "best": w.tokens / (per_call[0] * 1e-3)},
+        # the algorithmic model: compulsory I/O plus one write and one read of Hin and dS at fp32
+        "roofline_fp32_states": {"alg_bytes": alg, "roofline_ms": alg / (PEAK_HBM_GBS * 1e9) * 1e3,
+                                 "frac_mean": alg / (PEAK_HBM_GBS * 1e9) * 1e3 / mean_ms,
+                                 "frac_median": alg / (PEAK_HBM_GBS * 1e9) * 1e3 / med},
+        # the same with the states as this library stores them (I/O dtype)
+        "roofline_io_states": {"alg_bytes": alg_io, "frac_median": alg_io / (PEAK_HBM_GBS * 1e9) * 1e3 / med},
+        # compulsory I/O only (no chunk states at all): the stricter fraction
+        "roofline_compulsory": {"alg_bytes": comp, "frac_median": comp / (PEAK_HBM_GBS * 1e9) * 1e3 / med},
+        "alg_mfma_tflops_median": step_alg_flops(w) / (med * 1e-3) / 1e12,
+        "bitwise_repeat": bitwise,
+    }
+    if stage_ms is not None:
+        rec["stages_ms"] = stage_ms
+    return rec, inputs, d, S, ws, z
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +475,8 @@ def main():
                     help="skip the dt front-end / gate measurements (the backward and forward only)")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip the causal-conv1d forward / backward measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (not the other workloads of the family)")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -378,71 +497,23 @@ def main():
 
     import torch
     from state_space_model_mamba_amd import ssd
-    from state_space_model_mamba_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from state_space_model_mamba_amd.workloads import HEADLINE, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload or HEADLINE]
-    inputs = make_inputs(w)
     dev = torch.device("cuda:0")
-    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inputs.items()}
-    S = d["initial_states"].shape[0] if d.get("initial_states") is not None else (
-        w.nseqs_packed or w.batch)
-    shape = ssd.shape_of(d["x"], d["B"], w.chunk, S)
-    ws = torch.empty(ssd.workspace_size(shape), dtype=torch.uint8, device=dev)
-    H, P, N = w.nheads, w.headdim, w.dstate
-    out = {"dx": torch.empty_like(d["x"]), "ddt": torch.empty_like(d["dt"]),
-           "dA": torch.empty(H, device=dev), "dB": torch.empty_like(d["B"]),
-           "dC": torch.empty_like(d["C"]), "dD": torch.empty(H, device=dev),
-           "d_initial_states": torch.empty((S, H, P, N), device=dev)}
-    names = ssd.stage_names()
-    stream = torch.cuda.current_stream(dev)
-
-    def step(events=None):
-        ssd.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["dy"],
-                    initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
-                    nseqs=S, workspace=ws, out=out, events=events)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ref = {k: v.clone() for k, v in out.items()}
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for k in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    # per-stage times from a second pass of the same steps, with the library
-    # recording an event between stages (kept out of the timed region above)
-    nprof = min(args.steps, 50)
-    ev_steps = [ssd.make_stage_events(stream) for _ in range(nprof)]
-    torch.cuda.synchronize()
-    for k in range(nprof):
-        step(ev_steps[k])
-    torch.cuda.synchronize()
-    stage_ms = {n: 0.0 for n in names}
-    for evs in ev_steps:
-        for i, n in enumerate(names):
-            stage_ms[n] += evs[i].elapsed_time(evs[i + 1]) / nprof
-    bitwise = all(torch.equal(out[k].view(torch.uint8) if out[k].dtype != torch.bfloat16 else out[k].view(torch.int16),
-                              ref[k].view(torch.uint8) if ref[k].dtype != torch.bfloat16 else ref[k].view(torch.int16))
-                  for k in out)
-
-    ntg = N // next(t for t in (128, 64, 32, 16) if N % t == 0)
-    z = sizes(w, ntg)
+    print(f"[bench] {w.name}: {args.warmup} warm-up and {args.steps} timed calls", file=sys.stderr, flush=True)
+    rec, inputs, d, S, ws, z = measure_backward(torch, ssd, w, args.steps, args.warmup, dev)
+    stage_ms = rec["stages_ms"]
     sb = stage_alg_bytes(z)
+    sb["head_bwd"] = head_alg_bytes(z)
     dom = max(stage_ms, key=stage_ms.get)
     achieved = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(w.name, dom)
-    step_bytes = step_alg_bytes(z)
-    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    flops = step_alg_flops(w)
+    ms_per_step = rec["ms_per_layer"]["mean"]
+    H = w.nheads
     res = {
         "metric": METRIC,
         "value": w.tokens / (ms_per_step * 1e-3),
@@ -456,35 +527,51 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": H, "headdim": P,
-                   "ngroups": w.ngroups, "dstate": N, "chunk": w.chunk,
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": H, "headdim": w.headdim,
+                   "ngroups": w.ngroups, "dstate": w.dstate, "chunk": w.chunk,
                    "nseqs": S, "initial_states": w.h0_std > 0, "parallelism": "single GPU"},
+        "ms_per_layer": rec["ms_per_layer"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": sb[dom], "avg_ms": stage_ms[dom]},
-        "step_roofline": {"bound": "hbm", "alg_bytes": step_bytes, "achieved": step_gbs,
-                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": step_gbs / PEAK_HBM_GBS,
-                          "roofline_ms": step_bytes / (PEAK_HBM_GBS * 1e9) * 1e3,
-                          "alg_mfma_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "step_roofline": {"bound": "hbm", "alg_bytes": rec["roofline_fp32_states"]["alg_bytes"],
+                          "achieved": rec["roofline_fp32_states"]["alg_bytes"] / (ms_per_step * 1e-3) / 1e9,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": rec["roofline_fp32_states"]["frac_mean"],
+                          "frac_median": rec["roofline_fp32_states"]["frac_median"],
+                          "roofline_ms": rec["roofline_fp32_states"]["roofline_ms"],
+                          "frac_io_states_median": rec["roofline_io_states"]["frac_median"],
+                          "frac_compulsory_median": rec["roofline_compulsory"]["frac_median"],
+                          "alg_mfma_tflops": step_alg_flops(w) / (ms_per_step * 1e-3) / 1e12,
                           "mfma_peak_tflops": PEAK_BF16_TFLOPS},
         "stages_ms": stage_ms,
-        "bitwise_repeat": bitwise,
+        "bitwise_repeat": rec["bitwise_repeat"],
     }
     if not args.no_forward:
-        res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=min(args.steps, 100),
-                                         warmup=min(args.warmup, 10))
+        res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=args.steps, warmup=args.warmup)
     if not args.no_forward and not args.no_options:
-        res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=min(args.steps, 100),
-                                                            warmup=min(args.warmup, 10))
+        res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=args.steps,
+                                                            warmup=args.warmup)
         # output gate: z ~ N(0, 1) (seeded), in the I/O dtype
         gz = torch.Generator().manual_seed(w.seed + 1)
-        z = torch.randn(tuple(d["x"].shape), generator=gz).to(d["x"].dtype).to(dev)
+        zg = torch.randn(tuple(d["x"].shape), generator=gz).to(d["x"].dtype).to(dev)
         res["backward_with_dt_frontend_and_gate"] = measure_frontend(
-            torch, ssd, w, d, S, ws, steps=min(args.steps, 100), warmup=min(args.warmup, 10), z=z)
-        del z
+            torch, ssd, w, d, S, ws, steps=args.steps, warmup=args.warmup, z=zg)
+        del zg
     if not args.no_conv and not args.no_options:
-        res["causal_conv1d"] = measure_conv1d(torch, steps=min(args.steps, 100), warmup=min(args.warmup, 10),
+        res["causal_conv1d"] = measure_conv1d(torch, steps=args.steps, warmup=args.warmup,
                                               dev=dev, cpu=not args.no_cpu_baseline)
+    del d, ws
+    torch.cuda.empty_cache()
+    if not args.no_configs and args.workload is None:
+        # the other workloads of the family (the pages' seqlens 2048 / 4096 and the packed
+        # varlen case), each timed the same way
+        res["configs"] = {}
+        for name in ("bf16_L2048_H128", "bf16_B2_L4096_H128", "bf16_varlen7_L16384_N256"):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            crec = measure_backward(torch, ssd, WORKLOADS[name], args.steps, args.warmup, dev)[0]
+            res["configs"][name] = crec
+            torch.cuda.empty_cache()
     if args.calibration_copy:
         calibration_copy(torch, dev)
     if not args.no_cpu_baseline:

@@ -242,6 +242,24 @@ int ssd_bwd_profiled(const ssd_shape* shape, const void* x, const float* dt, con
 int ssd_bwd_stage_count(void);
 const char* ssd_bwd_stage_name(int stage);
 
+/*
+ * Launch geometry that the problem shape does not fix by itself, for tests of
+ * the determinism contract.  The page "Deterministic bwd kernel for mamba2"
+ * (its "Autotuner / kernel-shape non-determinism" section) reports results
+ * that changed with the kernels' block shape; here no result depends on the
+ * launch geometry, and this hook lets a test show it:
+ *   head_blocks          persistent blocks of the backward's per-head kernel
+ *                        (0: the default, 256, capped by the number of
+ *                        (batch, head, chunk) items)
+ *   fwd_heads_per_block  heads of one group handled by one block of the
+ *                        forward's output kernel (0: the default, chosen from
+ *                        the shape alone; capped by the heads per group)
+ * Process-wide; takes effect for calls made after it returns.  Outputs are
+ * byte-identical for every setting.  Returns SSD_OK, or SSD_ERR_INVALID_ARG
+ * for a negative value.
+ */
+int ssd_set_launch_geometry(int head_blocks, int fwd_heads_per_block);
+
 /* Library version, (major << 16) | minor. */
 int ssd_bwd_version(void);
 

@@ -450,19 +450,12 @@ int group_ntile(int N, bool io_bf16) {
 template <typename T, int Q, int P, int NTG>
 static hipError_t launch_dbdc_t(const Problem& pb, hipStream_t s) {
   using Cf = DbdcCfg<T, Q, P, NTG>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_db<T, Q, P, NTG>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS_DB));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG>), Cf::LDS);
+  if (e == hipSuccess) e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_db<T, Q, P, NTG>), Cf::LDS_DB);
+  if (e != hipSuccess) return e;
   const int64_t blocks = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg;
   hipLaunchKernelGGL((k_dc<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_db<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS_DB, s, pb);
   return hipGetLastError();

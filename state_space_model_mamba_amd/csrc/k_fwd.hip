@@ -669,27 +669,17 @@ __global__ __launch_bounds__((FinalCfg<T, Q, P, NT>::NTHR)) void k_final(Problem
 template <typename T, int Q, int P, int NS, bool MULTI>
 static hipError_t launch_y(const Problem& pb, hipStream_t s) {
   using Cf = YCfg<T, Q, P, NS>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_y<T, Q, P, NS, MULTI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  // heads per block: as many as keep about four blocks per CU in the grid
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_y<T, Q, P, NS, MULTI>), Cf::LDS);
+  if (e != hipSuccess) return e;
+  // heads per block: as many as keep about 1024 blocks (four per CU of an
+  // MI355X) in the grid -- a function of the shape only -- or the test
+  // override; every head's arithmetic is the same whatever the split
   const int64_t bgc = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
-  static int ncu = 0;
-  if (ncu == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      ncu = n;
-    else
-      ncu = 256;
-  }
-  const int64_t want = 4 * static_cast<int64_t>(ncu);
+  const int64_t want = 4 * static_cast<int64_t>(kHeadBlocks);
   int nsplit = static_cast<int>(std::min<int64_t>(pb.hpg, (want + bgc - 1) / bgc));
-  const int hper = (pb.hpg + nsplit - 1) / nsplit;
+  int hper = (pb.hpg + nsplit - 1) / nsplit;
+  const int ov = fwd_heads_per_block_override();
+  if (ov > 0) hper = std::min(ov, pb.hpg);
   nsplit = (pb.hpg + hper - 1) / hper;
   hipLaunchKernelGGL((k_y<T, Q, P, NS, MULTI>), dim3(static_cast<unsigned>(bgc * nsplit)), dim3(Cf::NTHR), Cf::LDS, s, pb);
   return hipGetLastError();

@@ -355,21 +355,11 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   }
 }
 
-template <typename K>
-static hipError_t allow_lds(K kernel, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(bytes));
-}
-
 template <typename T, int Q, int P>
 static hipError_t launch_dcb_t(const Problem& pb, hipStream_t s) {
   using C1 = DcbCfg<T, Q, P>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = allow_lds(&k_dcb<T, Q, P>, C1::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dcb<T, Q, P>), C1::LDS);
+  if (e != hipSuccess) return e;
   const int64_t b1 = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
   hipLaunchKernelGGL((k_dcb<T, Q, P>), dim3(static_cast<unsigned>(b1)), dim3(C1::NTHR), C1::LDS, s, pb);
   return hipGetLastError();

@@ -707,14 +707,15 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
 // Persistent blocks: the blocks on one XCD (block i runs on XCD i % 8) take
 // the logical items of that XCD's contiguous share in order, so the heads of
 // one (group, chunk), which read the same CB tiles, run on one XCD at about
-// the same time.  Every item is computed the same way whichever block takes
-// it.
+// the same time.  With fewer than 8 blocks the items are split into as many
+// shares as there are blocks, so every item has a block at any grid size.
+// Every item is computed the same way whichever block takes it.
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem pb) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int64_t NXCD = 8;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
   const int64_t nblk = gridDim.x;
+  const int64_t NXCD = nblk < 8 ? nblk : 8;
   const int64_t xcd = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
   const int64_t nb_x = nblk / NXCD + (xcd < nblk % NXCD ? 1 : 0);   // blocks on this XCD
   const int64_t q = total / NXCD, r = total % NXCD;
@@ -733,23 +734,15 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
 template <typename T, int Q, int P>
 static hipError_t launch_head_t(const Problem& pb, hipStream_t s) {
   using Cf = HeadCfg<T, Q, P>;
-  static bool attr_set = false;
-  static int resident = 0;   // blocks that fit on the device at once
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_head_bwd<T, Q, P>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(Cf::LDS));
-    if (e != hipSuccess) return e;
-    int dev = 0, ncu = 0, per_cu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_head_bwd<T, Q, P>),
-                                                          Cf::NTHR, Cf::LDS)) != hipSuccess)
-      return e;
-    resident = ncu * (per_cu > 0 ? per_cu : 1);
-    attr_set = true;
-  }
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_head_bwd<T, Q, P>), Cf::LDS);
+  if (e != hipSuccess) return e;
+  // a fixed number of persistent blocks (one per CU of an MI355X at one block
+  // per CU), or the test override; each block's items and every item's
+  // arithmetic are the same whatever the count
   const int64_t items = static_cast<int64_t>(pb.B) * pb.H * pb.nc;
-  const int64_t blocks = items < resident ? items : resident;
+  const int ov = head_blocks_override();
+  const int64_t want = ov > 0 ? ov : kHeadBlocks;
+  const int64_t blocks = items < want ? items : want;
   hipLaunchKernelGGL((k_head_bwd<T, Q, P>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
   return hipGetLastError();
 }

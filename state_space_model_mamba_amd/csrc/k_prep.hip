@@ -11,7 +11,7 @@
 // size alone: the chunk is scanned as Q/64 runs of 64 positions, each with a
 // 64-lane Hillis-Steele segmented scan (shuffle offsets 1, 2, ..., 32) that
 // starts from the previous run's last value.
-// A block handles 32 heads of one (batch, chunk).  That page
+// A block handles PREP_HEADS (4) heads of one (batch, chunk), one per wave.  That page
 // reports that a cumsum whose result changes with the block shape broke
 // run-to-run reproducibility; here the result does not depend on how many
 // heads a block handles or on the launch shape.

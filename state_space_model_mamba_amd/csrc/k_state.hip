@@ -411,23 +411,13 @@ static hipError_t launch_state_t(const Problem& pb, bool fwd, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(pb.B) * pb.H * (pb.N / NT);
   if (fwd) {
     constexpr size_t lds = StateFwdCfg<T, Q, P, NT>::LDS;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_state_fwd<T, Q, P, NT>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_state_fwd<T, Q, P, NT>), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_state_fwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), lds, s, pb);
   } else {
     constexpr size_t lds = StateBwdCfg<T, Q, P, NT>::LDS;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_state_bwd<T, Q, P, NT>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_state_bwd<T, Q, P, NT>), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_state_bwd<T, Q, P, NT>), dim3(static_cast<unsigned>(blocks)), dim3(StateCfg<T, Q, P, NT>::NTHR), lds, s, pb);
   }
   return hipGetLastError();

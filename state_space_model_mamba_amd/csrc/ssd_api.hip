@@ -2,8 +2,44 @@
 // the workspace layout and the launch sequence of the SSD backward.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "ssd_bwd.h"
 #include "ssd_problem.h"
+
+namespace ssd {
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;   // (device, kernel) already raised
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({dev, kernel})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e == hipSuccess) done.insert({dev, kernel});
+  return e;
+}
+
+namespace {
+std::atomic<int> g_head_blocks{0}, g_fwd_heads{0};
+}  // namespace
+
+int head_blocks_override() { return g_head_blocks.load(std::memory_order_relaxed); }
+int fwd_heads_per_block_override() { return g_fwd_heads.load(std::memory_order_relaxed); }
+
+}  // namespace ssd
+
+extern "C" int ssd_set_launch_geometry(int head_blocks, int fwd_heads_per_block) {
+  if (head_blocks < 0 || fwd_heads_per_block < 0) return SSD_ERR_INVALID_ARG;
+  ssd::g_head_blocks.store(head_blocks, std::memory_order_relaxed);
+  ssd::g_fwd_heads.store(fwd_heads_per_block, std::memory_order_relaxed);
+  return SSD_OK;
+}
 
 namespace {
 

@@ -94,6 +94,21 @@ __device__ inline float dt_frontend(const Problem& pb, float raw, int h, float* 
   return fminf(fmaxf(v, pb.dt_min), pb.dt_max);
 }
 
+// Raises `kernel`'s dynamic-LDS limit to `bytes` once per device (the
+// device current on the calling thread); thread-safe.  Every launcher calls
+// it before launching a kernel that needs more than the default.
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
+// Launch geometry that is not fixed by the problem shape alone, as
+// overridden through ssd_set_launch_geometry (0: the shape-derived default).
+// The results do not depend on either value.
+int head_blocks_override();
+int fwd_heads_per_block_override();
+
+// Persistent blocks of the head kernel: a constant (the CU count of one
+// MI355X), so the grid is a function of the problem shape only.
+constexpr int kHeadBlocks = 256;
+
 // Launchers (defined next to their kernels).  Return hipSuccess or the
 // launch error.  io_bf16 selects the bf16 (true) or fp32 instantiation.
 hipError_t launch_prep(const Problem& pb, hipStream_t s);

@@ -23,7 +23,7 @@ SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
             "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd",
-            "ssd_fwd_ex", "ssd_bwd_ex")
+            "ssd_fwd_ex", "ssd_bwd_ex", "ssd_set_launch_geometry")
 
 
 class SsdShape(ctypes.Structure):
@@ -82,6 +82,8 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_stage_count.argtypes = []
     lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
     lib.ssd_bwd_stage_name.argtypes = [ctypes.c_int]
+    lib.ssd_set_launch_geometry.restype = ctypes.c_int
+    lib.ssd_set_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -329,6 +331,13 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, ch
     initial_states, dt_bias and z."""
     return SsdChunkScan.apply(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z, chunk_size, nseqs,
                               dt_softplus, tuple(dt_limit))
+
+
+def set_launch_geometry(head_blocks: int = 0, fwd_heads_per_block: int = 0) -> None:
+    """Override the launch geometry the shape does not fix (0: default); see include/ssd_bwd.h."""
+    rc = load_library().ssd_set_launch_geometry(int(head_blocks), int(fwd_heads_per_block))
+    if rc:
+        raise SsdError(rc, "ssd_set_launch_geometry")
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:

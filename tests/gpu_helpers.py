@@ -82,8 +82,11 @@ def normwise_err(got, ref) -> float:
 def compare(got: dict, ref: dict, tol: float, keys=GRADS, label="") -> dict:
     errs = {}
     for k in keys:
-        if ref.get(k) is None or got.get(k) is None:
+        if ref.get(k) is None:
             continue
+        # every gradient the oracle defines must come back from the library
+        assert got.get(k) is not None, f"{label}{k}: missing from the library result"
+        assert not np.isnan(ref[k]).all(), f"{label}{k}: the oracle left it undefined"
         assert not np.isnan(got[k]).any(), f"{label}{k}: NaN in library output"
         errs[k] = normwise_err(got[k], ref[k])
     print(f"{label} normwise errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)

@@ -145,3 +145,10 @@ def test_frontend_argument_errors_are_reported_before_launch():
     assert call(None, dz=0x990000) == -1                                # dz without z
     assert call(None, z=0x990000, dz=FAKE["dx"]) == -1                  # dz aliasing dx (dx holds the gated dy)
     assert call(None, z=0x990000, dz=0x9a0008) == -4                    # misaligned dz
+
+
+def test_launch_geometry_hook_checks_its_arguments():
+    lib = ssd.load_library()
+    assert lib.ssd_set_launch_geometry(-1, 0) == -1
+    assert lib.ssd_set_launch_geometry(0, -3) == -1
+    assert lib.ssd_set_launch_geometry(0, 0) == 0

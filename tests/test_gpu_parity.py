@@ -123,24 +123,22 @@ def test_workload_L2048_full():
     check(make_inputs(w), w.chunk, TOL["bf16"], w.name)
 
 
-def test_workload_B2_L4096_sampled_group():
+# Full-size workloads, every output over every head and group, in the launch
+# configuration bench.py times (the library's default geometry).
+def test_workload_B2_L4096_full():
     w = WORKLOADS["bf16_B2_L4096_H128"]
-    inputs = make_inputs(w)
-    check(inputs, w.chunk, TOL["bf16"], w.name + " group 3", oracle_kw=dict(head_lo=48, head_hi=64))
+    check(make_inputs(w), w.chunk, TOL["bf16"], w.name)
 
 
-def test_headline_L16384_sampled_group():
+def test_headline_L16384_full():
     w = WORKLOADS["bf16_L16384_H128"]
-    inputs = make_inputs(w)
-    check(inputs, w.chunk, TOL["bf16"], w.name + " group 5", oracle_kw=dict(head_lo=80, head_hi=96))
+    check(make_inputs(w), w.chunk, TOL["bf16"], w.name)
 
 
-def test_varlen_N256_full_size_sampled_heads():
+def test_varlen_N256_full_size():
+    # 7 packed sequences with initial states; dB and dC sum all 64 heads of the one group over 64 chunks
     w = WORKLOADS["bf16_varlen7_L16384_N256"]
-    inputs = make_inputs(w)
-    # 8 of the 64 heads of the single group: per-head outputs; dB/dC need the whole group
-    check(inputs, w.chunk, TOL["bf16"], w.name + " heads 24..31",
-          oracle_kw=dict(head_lo=24, head_hi=32, partial_groups=True))
+    check(make_inputs(w), w.chunk, TOL["bf16"], w.name)
 
 
 def test_varlen_N256_shortened_all_outputs():
@@ -256,6 +254,31 @@ def test_batch_rows_independent_bitwise():
         for k in ("dx", "ddt", "dB", "dC"):
             assert torch.equal(single[k][0], both[k][r]), (r, k)
         assert torch.equal(single["d_initial_states"][0], both["d_initial_states"][r])
+
+
+def test_bitwise_independent_of_launch_geometry():
+    # The persistent head kernel's block count decides which block takes which
+    # (batch, head, chunk) item; the forward's heads per block decides which
+    # block computes which head.  Neither may change a byte of the results.
+    w = Workload("bf16_geom", batch=2, seqlen=1300, nheads=16, headdim=64, ngroups=2, dstate=128,
+                 chunk=256, dtype="bf16", seed=61)
+    inputs = packed(make_inputs(w), [[700, 600], [1300]])
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inputs.items()}
+    print("[case] launch geometry", flush=True)
+    runs, fwds = [], []
+    try:
+        for head_blocks, fwd_heads in ((0, 0), (37, 3), (5, 1), (1000, 8)):
+            ssd.set_launch_geometry(head_blocks, fwd_heads)
+            runs.append(run_library(inputs, 256, fill="garbage"))
+            fwds.append(ssd.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["initial_states"],
+                                    d["seq_idx"], chunk_size=256, want_final_states=True))
+            torch.cuda.synchronize()
+    finally:
+        ssd.set_launch_geometry(0, 0)
+    for r, f in zip(runs[1:], fwds[1:]):
+        assert bytes_equal(runs[0], r) == []
+        assert torch.equal(fwds[0]["y"].view(torch.int16), f["y"].view(torch.int16))
+        assert torch.equal(fwds[0]["final_states"].view(torch.int32), f["final_states"].view(torch.int32))
 
 
 def test_dA_cumsum_matches_oracle_and_ignores_launch_shape():
