@@ -204,6 +204,31 @@ int ssd_bwd_ex(const ssd_shape* shape, const ssd_options* opt, const void* x, co
                float* d_initial_states, float* ddt_bias, void* dz, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/*
+ * ssd_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and the same output bytes as ssd_bwd, with no workspace
+ * argument.  Its workspace is a fixed array of SSD_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) in the library's device memory: one copy per GPU, whose address is
+ * looked up on the first call on that device and which that GPU holds until
+ * the process ends.  The call makes no hipMalloc/hipFree and no other
+ * allocating call.
+ *   - Shapes whose ssd_bwd_workspace_size exceeds SSD_NOALLOC_SCRATCH_BYTES
+ *     are rejected with SSD_ERR_WORKSPACE_TOO_SMALL before anything is
+ *     enqueued (the 2048-token, 128-head, dstate-128 layer needs 61 MiB).
+ *   - Every call on one GPU shares that GPU's array and leaves its values in
+ *     it; the next call's results do not depend on them.  Calls that overlap
+ *     on one GPU (two streams, two host threads) race on the array: the
+ *     caller serialises them.
+ * Arguments, layouts and return codes are those of ssd_bwd.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssd_bwd_noalloc(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, const void* dy,
+                    const float* initial_states, const int32_t* seq_idx,
+                    void* dx, float* ddt, float* dA, void* dB, void* dC, float* dD,
+                    float* d_initial_states, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);
 

@@ -360,6 +360,52 @@ extern "C" int ssd_fwd_ex(const ssd_shape* shape, const ssd_options* fe, const v
                  workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// ssd_bwd_noalloc: ssd_bwd with its workspace in a fixed device array of
+// this library (one copy per GPU, held until the process ends), for callers
+// that cannot allocate.  The array's name is a host-side stand-in for a
+// device symbol: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// passed on.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (guarded by g_scratch_mu)
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" int ssd_bwd_noalloc(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D, const void* dy,
+                               const float* initial_states, const int32_t* seq_idx, void* dx, float* ddt,
+                               float* dA, void* dB, void* dC, float* dD, float* d_initial_states, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (make_layout(shape).total > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  // the workspace's contents on entry do not affect the results, so nothing
+  // is cleared here (the previous call's values are simply overwritten)
+  return run_bwd(shape, nullptr, x, dt, A, B, C, D, nullptr, dy, initial_states, seq_idx, dx, ddt, dA, dB, dC, dD,
+                 d_initial_states, nullptr, nullptr, ws, SSD_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
+
 extern "C" int ssd_bwd_stage_count(void) { return kStages; }
 
 extern "C" const char* ssd_bwd_stage_name(int stage) {

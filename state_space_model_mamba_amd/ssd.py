@@ -23,7 +23,9 @@ SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
             "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd",
-            "ssd_fwd_ex", "ssd_bwd_ex", "ssd_set_launch_geometry")
+            "ssd_fwd_ex", "ssd_bwd_ex", "ssd_set_launch_geometry", "ssd_bwd_noalloc")
+# bytes of the library's own device workspace used by ssd_bwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SsdShape(ctypes.Structure):
@@ -82,6 +84,8 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_stage_count.argtypes = []
     lib.ssd_bwd_stage_name.restype = ctypes.c_char_p
     lib.ssd_bwd_stage_name.argtypes = [ctypes.c_int]
+    lib.ssd_bwd_noalloc.restype = ctypes.c_int
+    lib.ssd_bwd_noalloc.argtypes = [sp] + [vp] * 17
     lib.ssd_set_launch_geometry.restype = ctypes.c_int
     lib.ssd_set_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int]
     _lib = lib
@@ -239,6 +243,41 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     res["workspace"] = workspace
     res["shape"] = shape
     return res
+
+
+def ssd_bwd_noalloc(x, dt, A, B, C, D, dy, out: dict, initial_states=None, seq_idx=None,
+                    chunk_size: int = 256, nseqs: Optional[int] = None):
+    """ssd_bwd through the entry point that allocates nothing (its workspace is the library's
+    fixed device array, see include/ssd_bwd.h): the caller passes the outputs in ``out``
+    (dx, ddt, dA, dB, dC, and dD / d_initial_states or None), shaped as ssd_bwd returns them.
+    Calls on one device share that array and must not overlap."""
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_bwd_noalloc runs on a HIP device; got tensors on " + str(dev))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = x.dtype
+    S = initial_states.shape[0] if initial_states is not None else (b if seq_idx is None else (nseqs or 0))
+    for t, name, dtype, shp in ((x, "x", io, (b, L, H, P)), (dy, "dy", io, (b, L, H, P)), (B, "B", io, (b, L, G, N)),
+                                (C, "C", io, (b, L, G, N)), (dt, "dt", torch.float32, (b, L, H)),
+                                (A, "A", torch.float32, (H,)), (D, "D", torch.float32, (H,)),
+                                (initial_states, "initial_states", torch.float32, (S, H, P, N)),
+                                (seq_idx, "seq_idx", torch.int32, (b, L)),
+                                (out["dx"], "dx", io, (b, L, H, P)), (out["ddt"], "ddt", torch.float32, (b, L, H)),
+                                (out["dA"], "dA", torch.float32, (H,)), (out["dB"], "dB", io, (b, L, G, N)),
+                                (out["dC"], "dC", io, (b, L, G, N)), (out.get("dD"), "dD", torch.float32, (H,)),
+                                (out.get("d_initial_states"), "d_initial_states", torch.float32, (S, H, P, N))):
+        _check(t, name, dtype, shp, dev)
+    shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_bwd_noalloc(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dy),
+                             _ptr(initial_states), _ptr(seq_idx), _ptr(out["dx"]), _ptr(out["ddt"]),
+                             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+                             _ptr(out.get("d_initial_states")), ctypes.c_void_p(stream))
+    if rc:
+        raise SsdError(rc, "ssd_bwd_noalloc")
+    return out
 
 
 def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
