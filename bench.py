@@ -25,7 +25,7 @@ METRIC = "SSD bwd ms/layer + tokens/s at L=16K (1 GPU); bitwise repeat + % roofl
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_head.hip", "k_fwd.hip",
+KERNEL_SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_grp.hip", "k_head.hip", "k_fwd.hip",
                   "ssd_device.h", "ssd_tiles.h", "ssd_problem.h"]
 
 
@@ -46,8 +46,8 @@ def sizes(w, ntg):
         CH=w.batch * w.nheads * nc * w.chunk * 4,                  # one per-chunk fp32 vector
         OFFD=w.batch * w.nheads * nc * ntg * w.chunk * 4,
         SEG=w.batch * nc * w.chunk * 4,
-        DCB=w.batch * w.ngroups * nc * w.chunk * w.chunk * s,      # dCB tile (or its transpose)
         CBT=w.batch * w.ngroups * nc * (w.chunk * (w.chunk + 16) // 2) * 4,   # causal C B^T tiles, fp32
+        DCB=w.batch * w.ngroups * nc * w.chunk * w.chunk * s,      # dCB tile (or its transpose), split path
         CBT_FWD=w.batch * w.ngroups * nc * (w.chunk * (w.chunk + 16) // 2) * s,   # the forward's, I/O dtype
     )
     return z
@@ -66,14 +66,27 @@ def step_compulsory_bytes(z):
     return 3 * z["X"] + 4 * z["BC"] + 2 * z["DT"] + z["INIT"] + z["DINIT"] + z["SEQ"]
 
 
-def stage_alg_bytes(z):
-    """Each operand a stage must read or write, counted once."""
+def group_fused(w):
+    """The library's choice of group kernels for this workload (split when their grid has >= 256 blocks)."""
+    nc = -(-w.seqlen // w.chunk)
+    ntg = w.dstate // next(t for t in (128, 64, 32, 16) if w.dstate % t == 0)
+    return w.batch * w.ngroups * nc * ntg < 256
+
+
+def stage_alg_bytes(z, fused=False):
+    """Each operand a stage must read or write, counted once (the group stages per path)."""
+    if fused:   # k_cb; k_grp
+        dcb = 2 * z["BC"] + z["CBT"]
+        dbdc = 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["SEG"] + z["INIT"] + z["OFFD"]
+    else:       # k_dcb; k_dc and k_db
+        dcb = 2 * z["X"] + 2 * z["BC"] + 2 * z["CH"] + z["SEG"] + 2 * z["DCB"] + z["CBT"]
+        dbdc = 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"] + 2 * z["DCB"]
     return {
         "prep": z["DT"] + z["SEQ"] + 2 * z["CH"] + z["SEG"],
         "state_fwd": z["X"] + z["BC"] + 2 * z["CH"] + z["INIT"] + z["T"],
         "state_bwd": z["X"] + z["BC"] + z["CH"] + z["T"] + z["DINIT"],
-        "dcb": 2 * z["X"] + 2 * z["BC"] + 2 * z["CH"] + z["SEG"] + 2 * z["DCB"] + z["CBT"],
-        "dbdc": 2 * z["X"] + 4 * z["BC"] + 2 * z["T"] + 2 * z["CH"] + z["INIT"] + z["OFFD"] + 2 * z["DCB"],
+        "dcb": dcb,
+        "dbdc": dbdc,
         "head_bwd": 3 * z["X"] + z["BC"] + z["T"] + z["CBT"] + 2 * z["CH"] + z["OFFD"] + z["DT"],
         "reduce": 0,
     }
@@ -128,7 +141,8 @@ def measured_traffic(workload, stage):
 
 # stage of each library kernel (kernel name prefix -> stage)
 STAGE_OF_KERNEL = [("k_head_bwd", "head_bwd"), ("k_state_fwd", "state_fwd"), ("k_state_bwd", "state_bwd"),
-                   ("k_dcb<", "dcb"), ("k_dc<", "dbdc"), ("k_db<", "dbdc"), ("k_prep", "prep"),
+                   ("k_dcb<", "dcb"), ("k_dc<", "dbdc"), ("k_db<", "dbdc"), ("k_cb<", "dcb"), ("k_grp<", "dbdc"),
+                   ("k_prep", "prep"),
                    ("k_seqbase", "prep"), ("k_reduce", "reduce"),
                    ("k_cbf<", "fwd_cbf"), ("k_y<", "fwd_y"), ("k_final<", "fwd_final"), ("k_seqstart", "fwd_final")]
 CALIB_BYTES = 1 << 28   # bytes read (and written) by one calibration copy
@@ -191,6 +205,54 @@ def ingest_counters(fetch_csv, write_csv, workload, out_path=TRAFFIC_FILE):
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
     return rec
+
+
+# rocprofv3 --pmc passes for the per-kernel counter summaries (each within one run's limits:
+# at most 8 SQ and 2 GRBM counters)
+PMC_PASSES = {
+    "A": ["GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES",
+          "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_ANY"],
+    "B": ["GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_INSTS_SALU",
+          "SQ_WAVE_CYCLES", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VMEM_RD"],
+}
+N_CU, N_SIMD, N_XCD = 256, 1024, 8   # MI355X
+
+
+def summarize_pmc(csv_paths):
+    """Per-kernel means (per dispatch) of the counters in rocprofv3 counter_collection CSVs.  The
+    SQ counters are totals over the GPU; GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's
+    busy cycles are GRBM_GUI_ACTIVE / 8.  Derived rates: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    (cycles * SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / (cycles * CUs) (rocprofv3's VALUBusy);
+    LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / (cycles * CUs); waits per wave-cycle =
+    SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.  Returns markdown."""
+    import csv
+    vals, durs = {}, {}
+    for path in csv_paths:
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                k = row["Kernel_Name"]
+                stage = next((st for pre, st in STAGE_OF_KERNEL if pre in k), None)
+                if stage is None:
+                    continue
+                key = (stage, k.split("(")[0].replace("void ", ""))
+                vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                if row["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    durs.setdefault(key, []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    lines = ["| kernel | dispatch us | MFMA busy | VALU busy | VALU insts/wave | MFMA insts/wave | "
+             "LDS insts/wave | LDS bank-conflict cycles / CU-cycles | wait-any / wave-cycles | trans f32 insts/wave |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for (stage, name), c in sorted(vals.items()):
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        g = m.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD
+        waves = m.get("SQ_WAVES", float("nan"))
+        f = lambda k, d: m[k] / d if k in m and d else float("nan")
+        us = sum(durs[(stage, name)]) / len(durs[(stage, name)]) / 1e3
+        lines.append(f"| {name} | {us:.1f} | {f('SQ_VALU_MFMA_BUSY_CYCLES', g * N_SIMD):.1%} | "
+                     f"{f('SQ_ACTIVE_INST_VALU', g * N_CU):.1%} | {f('SQ_INSTS_VALU', waves):.0f} | "
+                     f"{f('SQ_INSTS_MFMA', waves):.0f} | {f('SQ_INSTS_LDS', waves):.0f} | "
+                     f"{f('SQ_LDS_BANK_CONFLICT', g * N_CU):.1%} | {f('SQ_WAIT_INST_ANY', m.get('SQ_WAVE_CYCLES')):.2f} | "
+                     f"{f('SQ_INSTS_VALU_TRANS_F32', waves):.0f} |")
+    return "\n".join(lines)
 
 
 def cpu_model():
@@ -442,7 +504,7 @@ def measure_backward(torch, ssd, w, steps, warmup, dev, stages=True):
     rec = {
         "workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": H, "headdim": P,
         "ngroups": w.ngroups, "dstate": N, "chunk": w.chunk, "nseqs": S, "initial_states": w.h0_std > 0,
-        "dtype": w.dtype, "steps": steps, "warmup": warmup,
+        "dtype": w.dtype, "steps": steps, "warmup": warmup, "group_path": "fused" if group_fused(w) else "split",
         "ms_per_layer": {"mean": mean_ms, "median": med, "min": per_call[0], "max": per_call[-1]},
         "tokens_per_s": {"mean": w.tokens / (mean_ms * 1e-3), "median": w.tokens / (med * 1e-3),
                          "best": w.tokens / (per_call[0] * 1e-3)},
@@ -483,7 +545,17 @@ def main():
                     help="after timing, run a plain copy of known size (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter files into the traffic record and exit")
+    ap.add_argument("--pmc-pass", choices=sorted(PMC_PASSES),
+                    help="print the counters of one rocprofv3 --pmc pass (space separated) and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print a per-kernel markdown table of rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.pmc_pass:
+        print(" ".join(PMC_PASSES[args.pmc_pass]))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.ingest_counters:
         from state_space_model_mamba_amd.workloads import HEADLINE
         rec = ingest_counters(*args.ingest_counters, workload=args.workload or HEADLINE)
@@ -507,7 +579,7 @@ def main():
     print(f"[bench] {w.name}: {args.warmup} warm-up and {args.steps} timed calls", file=sys.stderr, flush=True)
     rec, inputs, d, S, ws, z = measure_backward(torch, ssd, w, args.steps, args.warmup, dev)
     stage_ms = rec["stages_ms"]
-    sb = stage_alg_bytes(z)
+    sb = stage_alg_bytes(z, group_fused(w))
     sb["head_bwd"] = head_alg_bytes(z)
     dom = max(stage_ms, key=stage_ms.get)
     achieved = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9

@@ -285,6 +285,23 @@ const char* ssd_bwd_stage_name(int stage);
  */
 int ssd_set_launch_geometry(int head_blocks, int fwd_heads_per_block);
 
+/*
+ * Which of the two implementations of the group stage (the head-summed dCB
+ * and dC, dB; stages "dcb" and "dbdc") the calls made after this one use,
+ * for tests that cover both:
+ *   0  by shape (the default): split kernels when their grid has at least
+ *      256 blocks, else the fused slab kernel, which has Q / 64 times more
+ *   1  fused: per (batch, group, chunk, 64-row slab, dstate tile), dCB, dC
+ *      and dB in one pass over the group's heads
+ *   2  split: dCB per (batch, group, chunk), then dC and dB per (batch,
+ *      group, chunk, dstate tile)
+ * Both sum the same terms in fixed orders, so each is deterministic; they
+ * add in different orders, so they agree to rounding, not bit for bit.
+ * The choice also changes the workspace size.  Process-wide.  Returns
+ * SSD_OK, or SSD_ERR_INVALID_ARG for another value.
+ */
+int ssd_set_group_path(int path);
+
 /* Library version, (major << 16) | minor. */
 int ssd_bwd_version(void);
 

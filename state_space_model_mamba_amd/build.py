@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libssd_bwd.so")
 ARCH = "gfx950"
-SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_head.hip", "k_fwd.hip", "ssd_api.hip",
-           "k_conv.hip"]
+SOURCES = ["k_prep.hip", "k_state.hip", "k_group.hip", "k_dbdc.hip", "k_grp.hip", "k_head.hip", "k_fwd.hip",
+           "ssd_api.hip", "k_conv.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -2,6 +2,7 @@
 // the workspace layout and the launch sequence of the SSD backward.
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <set>
@@ -26,13 +27,20 @@ hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
 }
 
 namespace {
-std::atomic<int> g_head_blocks{0}, g_fwd_heads{0};
+std::atomic<int> g_head_blocks{0}, g_fwd_heads{0}, g_group_path{0};
 }  // namespace
 
 int head_blocks_override() { return g_head_blocks.load(std::memory_order_relaxed); }
 int fwd_heads_per_block_override() { return g_fwd_heads.load(std::memory_order_relaxed); }
+int group_path_override() { return g_group_path.load(std::memory_order_relaxed); }
 
 }  // namespace ssd
+
+extern "C" int ssd_set_group_path(int path) {
+  if (path < 0 || path > 2) return SSD_ERR_INVALID_ARG;
+  ssd::g_group_path.store(path, std::memory_order_relaxed);
+  return SSD_OK;
+}
 
 extern "C" int ssd_set_launch_geometry(int head_blocks, int fwd_heads_per_block) {
   if (head_blocks < 0 || fwd_heads_per_block < 0) return SSD_ERR_INVALID_ARG;
@@ -48,12 +56,28 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_dDp, slot_ddtb, seqstart,
-      total;
+  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, cbt, offd, endd, slot_dA, slot_dD, slot_dDp, slot_ddtb,
+      seqstart, total;
   int nc, ntg;
+  bool fused;
 };
 
 bool is_bf16(const ssd_shape* s) { return s->io_dtype == SSD_IO_BF16; }
+
+// The group stage (dCB, dC, dB) runs split (k_dcb, k_dc, k_db: one block per
+// (batch, group, chunk, dstate tile of k_dc / k_db)) when that grid has at
+// least 256 blocks, one per CU of an MI355X; below that, fused (k_cb, k_grp),
+// whose 64-row slabs multiply the blocks by Q / 64.  A function of the shape
+// only (or the test override); the two paths add the same terms in
+// different orders, so their results agree to rounding, not bit for bit.
+bool group_fused(const ssd_shape* s) {
+  const int ov = ssd::group_path_override();
+  if (ov == 1) return true;
+  if (ov == 2) return false;
+  const int64_t nc = (s->seqlen + s->chunk_size - 1) / s->chunk_size;
+  const int64_t ntg = s->dstate / ssd::group_ntile(static_cast<int>(s->dstate), is_bf16(s));
+  return s->batch * s->ngroups * nc * ntg < 256;
+}
 
 int check_shape(const ssd_shape* s) {
   if (!s) return SSD_ERR_INVALID_ARG;
@@ -72,11 +96,15 @@ int check_shape(const ssd_shape* s) {
   if (s->seqlen > (int64_t(1) << 30) || s->batch * s->nheads * nc > (int64_t(1) << 30) ||
       s->nheads > (1 << 20) || s->batch > (1 << 20) || s->nseqs > (int64_t(1) << 30))
     return SSD_ERR_UNSUPPORTED_SHAPE;
-  const int ntg_w = ssd::group_ntile(static_cast<int>(N), is_bf16(s));
   const size_t lim = 160 * 1024;
-  if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
-      ssd::dcb_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim ||
-      ssd::dbdc_lds_bytes(static_cast<int>(Q), static_cast<int>(P), ntg_w, is_bf16(s)) > lim ||
+  const bool fused = group_fused(s);
+  const size_t group_lds =
+      fused ? ssd::grp_lds_bytes(static_cast<int>(Q), static_cast<int>(P),
+                                 ssd::grp_ntile(static_cast<int>(N), is_bf16(s)), is_bf16(s))
+            : std::max(ssd::dcb_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)),
+                       ssd::dbdc_lds_bytes(static_cast<int>(Q), static_cast<int>(P),
+                                           ssd::group_ntile(static_cast<int>(N), is_bf16(s)), is_bf16(s)));
+  if (ssd::head_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim || group_lds > lim ||
       ssd::fwd_lds_bytes(static_cast<int>(Q), static_cast<int>(P), is_bf16(s)) > lim)
     return SSD_ERR_UNSUPPORTED_SHAPE;
   return SSD_OK;
@@ -86,7 +114,9 @@ Layout make_layout(const ssd_shape* s) {
   Layout L;
   const size_t B = s->batch, H = s->nheads, Q = s->chunk_size, P = s->headdim, N = s->dstate;
   const size_t nc = (s->seqlen + s->chunk_size - 1) / s->chunk_size;
-  const size_t ntg = N / ssd::group_ntile(static_cast<int>(N), is_bf16(s));
+  L.fused = group_fused(s);
+  const size_t ntg = N / (L.fused ? ssd::grp_ntile(static_cast<int>(N), is_bf16(s))
+                                  : ssd::group_ntile(static_cast<int>(N), is_bf16(s)));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -101,8 +131,9 @@ Layout make_layout(const ssd_shape* s) {
   const size_t es = is_bf16(s) ? 2 : 4;
   L.hin = take(B * H * nc * P * N * es);
   L.dstate = take(B * H * nc * P * N * es);
-  L.dcb = take(B * s->ngroups * nc * Q * Q * es);
-  L.dcbt = take(B * s->ngroups * nc * Q * Q * es);
+  const size_t dcb_bytes = L.fused ? 0 : B * s->ngroups * nc * Q * Q * es;
+  L.dcb = take(dcb_bytes);
+  L.dcbt = take(dcb_bytes);
   L.cbt = take(B * s->ngroups * nc * (Q * (Q + 16) / 2) * 4);
   L.offd = take(B * H * nc * ntg * Q * 4);
   L.endd = take(B * H * nc * ntg * 4);
@@ -273,8 +304,10 @@ int run_bwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const 
     pb.dy = dx;
   }
   if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess || !mark(3)) return SSD_ERR_HIP;
-  if (ssd::launch_dcb(pb, bf16, s) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
-  if (ssd::launch_dbdc(pb, bf16, s) != hipSuccess || !mark(5)) return SSD_ERR_HIP;
+  if ((L.fused ? ssd::launch_cb(pb, bf16, s) : ssd::launch_dcb(pb, bf16, s)) != hipSuccess || !mark(4))
+    return SSD_ERR_HIP;
+  if ((L.fused ? ssd::launch_grp(pb, bf16, s) : ssd::launch_dbdc(pb, bf16, s)) != hipSuccess || !mark(5))
+    return SSD_ERR_HIP;
   if (ssd::launch_head_bwd(pb, bf16, s) != hipSuccess || !mark(6)) return SSD_ERR_HIP;
   if (ssd::launch_reduce(pb, s) != hipSuccess || !mark(7)) return SSD_ERR_HIP;
   return SSD_OK;

@@ -23,7 +23,7 @@ __host__ __device__ inline int seg_rank(int v) { return v >> 16; }
 
 struct Problem {
   int B, L, H, P, G, N, Q, nc, hpg, nseqs;
-  int ntg;  // number of dstate tiles of the dB/dC kernel
+  int ntg;  // number of dstate tiles of the group kernel (dC, dB, offd, endd)
   // inputs
   const void* x;
   const float* dt;
@@ -66,8 +66,8 @@ struct Problem {
   float* dfe;        // (B, H, nc, Q): d dtc / d raw dt (written and read only with a dt front-end)
   void* hin;         // (B, H, nc, P, N), I/O dtype
   void* dstate;      // (B, H, nc, P, N), I/O dtype
-  void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB
-  void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose
+  void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB (split group path)
+  void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose (split group path)
   float* cbt;        // (B, G, nc, Q(Q+16)/512 tiles, 256): C B^T causal tiles, fp32, in the
                      // causal split's (wave, tile) order and accumulator lane layout
   float* offd;       // (B, H, nc, ntg, Q)
@@ -114,8 +114,12 @@ constexpr int kHeadBlocks = 256;
 hipError_t launch_prep(const Problem& pb, hipStream_t s);
 hipError_t launch_state_fwd(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_state_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
+// the group stage, split: dCB and C B^T tiles (k_dcb), then dC (k_dc) and dB (k_db)
 hipError_t launch_dcb(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_dbdc(const Problem& pb, bool io_bf16, hipStream_t s);
+// the group stage, fused: C B^T tiles (k_cb), then dCB, dC and dB per 64-row slab (k_grp)
+hipError_t launch_cb(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_grp(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_head_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
 hipError_t launch_reduce(const Problem& pb, hipStream_t s);
 // forward: sequence start table, then C B^T tiles, y and (if requested) the
@@ -131,9 +135,14 @@ hipError_t launch_fwd_out(const Problem& pb, bool io_bf16, hipStream_t s);
 
 // Shape support (host side): true when kernels exist for this combination
 // and fit the LDS of one workgroup.
-int group_ntile(int N, bool io_bf16);
+int group_ntile(int N, bool io_bf16);   // dstate tile of k_dc / k_db
+int grp_ntile(int N, bool io_bf16);     // dstate tile of k_grp
+// Which group path a shape takes (0: by shape, 1: fused, 2: split), as
+// overridden through ssd_set_group_path.
+int group_path_override();
 size_t dcb_lds_bytes(int Q, int P, bool io_bf16);
 size_t dbdc_lds_bytes(int Q, int P, int NTG, bool io_bf16);
+size_t grp_lds_bytes(int Q, int P, int NTG, bool io_bf16);
 size_t head_lds_bytes(int Q, int P, bool io_bf16);
 size_t fwd_lds_bytes(int Q, int P, bool io_bf16);
 

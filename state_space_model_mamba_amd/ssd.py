@@ -23,7 +23,7 @@ SSD_WS_ACS, SSD_WS_HIN, SSD_WS_DSTATE = 0, 1, 2
 
 EXPORTED = ("ssd_bwd", "ssd_bwd_workspace_size", "ssd_bwd_workspace_region", "ssd_status_string",
             "ssd_bwd_version", "ssd_bwd_profiled", "ssd_bwd_stage_count", "ssd_bwd_stage_name", "ssd_fwd",
-            "ssd_fwd_ex", "ssd_bwd_ex", "ssd_set_launch_geometry", "ssd_bwd_noalloc")
+            "ssd_fwd_ex", "ssd_bwd_ex", "ssd_set_launch_geometry", "ssd_bwd_noalloc", "ssd_set_group_path")
 # bytes of the library's own device workspace used by ssd_bwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -86,6 +86,8 @@ def load_library(path: str = LIBRARY):
     lib.ssd_bwd_stage_name.argtypes = [ctypes.c_int]
     lib.ssd_bwd_noalloc.restype = ctypes.c_int
     lib.ssd_bwd_noalloc.argtypes = [sp] + [vp] * 17
+    lib.ssd_set_group_path.restype = ctypes.c_int
+    lib.ssd_set_group_path.argtypes = [ctypes.c_int]
     lib.ssd_set_launch_geometry.restype = ctypes.c_int
     lib.ssd_set_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int]
     _lib = lib
@@ -377,6 +379,16 @@ def set_launch_geometry(head_blocks: int = 0, fwd_heads_per_block: int = 0) -> N
     rc = load_library().ssd_set_launch_geometry(int(head_blocks), int(fwd_heads_per_block))
     if rc:
         raise SsdError(rc, "ssd_set_launch_geometry")
+
+
+GROUP_PATH_BY_SHAPE, GROUP_PATH_FUSED, GROUP_PATH_SPLIT = 0, 1, 2
+
+
+def set_group_path(path: int = GROUP_PATH_BY_SHAPE) -> None:
+    """Force the fused or the split group kernels (or restore the choice by shape); see include/ssd_bwd.h."""
+    rc = load_library().ssd_set_group_path(int(path))
+    if rc:
+        raise SsdError(rc, "ssd_set_group_path")
 
 
 def workspace_view(result: dict, region: int) -> torch.Tensor:

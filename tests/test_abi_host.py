@@ -152,3 +152,17 @@ def test_launch_geometry_hook_checks_its_arguments():
     assert lib.ssd_set_launch_geometry(-1, 0) == -1
     assert lib.ssd_set_launch_geometry(0, -3) == -1
     assert lib.ssd_set_launch_geometry(0, 0) == 0
+
+
+def test_group_path_hook_checks_its_argument_and_sizes_the_workspace():
+    lib = ssd.load_library()
+    assert lib.ssd_set_group_path(3) == -1 and lib.ssd_set_group_path(-1) == -1
+    sh = shape()   # 1 x 2048, 128 heads, 8 groups, N = 128: 64 blocks, the fused path by shape
+    try:
+        sizes = {}
+        for path in (0, 1, 2):
+            assert lib.ssd_set_group_path(path) == 0
+            sizes[path] = ssd.workspace_size(sh)
+        assert sizes[0] == sizes[1] < sizes[2]   # the split path holds dCB and its transpose
+    finally:
+        lib.ssd_set_group_path(0)

@@ -147,6 +147,40 @@ def test_varlen_N256_shortened_all_outputs():
     check(inputs, w.chunk, TOL["bf16"], w.name)
 
 
+# Both implementations of the group stage (dCB, dC, dB): the fused slab kernel
+# and the split kernels, each forced on shapes that exercise segments, ragged
+# tails, several dstate tiles and every chunk size.
+GROUP_CASES = [
+    ("f32 packed ragged", lambda: packed(make_inputs(small("gp_f32", batch=2, seqlen=200, nheads=4, ngroups=2,
+                                                             headdim=16, dstate=32, chunk=64)),
+                                         [[64, 40, 1, 95], [200]]), 64, "f32"),
+    ("f32 P64 Q128 N48", lambda: packed(make_inputs(small("gp_f32b", seqlen=300, nheads=4, ngroups=2, headdim=64,
+                                                            dstate=48, chunk=128, seed=3)), [[100, 150, 50]]),
+     128, "f32"),
+    ("bf16 Q256 N256 packed", lambda: packed(make_inputs(Workload("gp_bf16", batch=2, seqlen=700, nheads=8,
+                                                                  headdim=64, ngroups=2, dstate=256, chunk=256,
+                                                                  dtype="bf16", seed=11)),
+                                             [[300, 256, 144], [700]]), 256, "bf16"),
+    ("bf16 Q128 P32 N64", lambda: make_inputs(Workload("gp_bf16b", batch=1, seqlen=520, nheads=6, headdim=32,
+                                                       ngroups=3, dstate=64, chunk=128, dtype="bf16", seed=12)),
+     128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("path", [ssd.GROUP_PATH_FUSED, ssd.GROUP_PATH_SPLIT], ids=["fused", "split"])
+@pytest.mark.parametrize("case", range(len(GROUP_CASES)), ids=[c[0] for c in GROUP_CASES])
+def test_group_paths_match_oracle(path, case):
+    label, make, chunk, dt = GROUP_CASES[case]
+    inputs = make()
+    ssd.set_group_path(path)
+    try:
+        res, got, ref = check(inputs, chunk, TOL[dt], f"{label} ({'fused' if path == 1 else 'split'})")
+        again = run_library(inputs, chunk, fill="garbage")
+        assert bytes_equal(res, again) == []
+    finally:
+        ssd.set_group_path(ssd.GROUP_PATH_BY_SHAPE)
+
+
 # --------------------------------------------------------------------------- edge cases
 def test_single_token_and_short_sequences():
     w = small("L1", seqlen=1)
