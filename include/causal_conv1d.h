@@ -15,9 +15,10 @@
  *     out[b,t,c] = pre[b,t,c]                        (CONV1D_ACT_NONE)
  *                = pre[b,t,c] * sigmoid(pre[b,t,c])  (CONV1D_ACT_SILU)
  *
- * with m(t, s) = 1 when s >= 0 and row s is in the same sequence as row t
- * (seq_idx[b,s] == seq_idx[b,t]; every row is one sequence when seq_idx is
- * NULL), else 0.  conv1d_bwd returns the gradients of l = sum dout * out:
+ * with m(t, s) = 1 when s >= 0 and rows s and t are in the same sequence,
+ * else 0.  As for ssd_bwd, a sequence starts at row r when r == 0 or
+ * seq_idx[b, r] != seq_idx[b, r-1], so rows s <= t share a sequence when no
+ * sequence starts in (s, t]; with seq_idx NULL every row is one sequence.  conv1d_bwd returns the gradients of l = sum dout * out:
  * dx (like x), dweight (like w) and dbias (like bias), recomputing pre from
  * x; nothing from the forward is needed.
  *

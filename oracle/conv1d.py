@@ -12,10 +12,12 @@ input x (batch, seqlen, channels) and a filter w (channels, width):
     pre[b, t, c] = bias[c] + sum_k  w[c, k] * x[b, t - (W-1) + k, c] * m(t, t - (W-1) + k)
     out[b, t, c] = act(pre[b, t, c]),   act = identity or SiLU (u * sigmoid(u))
 
-where the mask m(t, s) is 1 when 0 <= s and row s belongs to the same
-sequence as row t (seq_idx[b, s] == seq_idx[b, t] when a packed batch gives
-seq_idx), else 0: the filter never reaches across a sequence start or before
-the first row.
+where the mask m(t, s) is 1 when 0 <= s and rows s and t belong to the same
+sequence, else 0: the filter never reaches across a sequence start or before
+the first row.  A sequence starts at row r when r = 0 or seq_idx[b, r] !=
+seq_idx[b, r - 1] (the SSD's own definition of a packed batch), so rows s <= t
+share a sequence when no sequence starts in (s, t]; without seq_idx every row
+is one sequence.
 
 The backward follows from the chain rule applied to that definition, with
 g = dout * act'(pre):
@@ -36,13 +38,22 @@ import numpy as np
 ACTIVATIONS = ("none", "silu")
 
 
+def _sequence_number(seq_idx: np.ndarray) -> np.ndarray:
+    """Number of sequence starts at or before each row: (batch, L) int64."""
+    seq_idx = np.asarray(seq_idx)
+    starts = np.ones(seq_idx.shape, dtype=np.int64)
+    starts[:, 1:] = seq_idx[:, 1:] != seq_idx[:, :-1]
+    return np.cumsum(starts, axis=1)
+
+
 def _mask(L: int, shift: int, seq_idx: Optional[np.ndarray], batch: int) -> np.ndarray:
     """m(t, t - shift) for t in [0, L): shape (batch, L, 1), 0/1 float64."""
     t = np.arange(L)
     ok = np.broadcast_to((t - shift >= 0)[None, :], (batch, L)).astype(np.float64)
     if seq_idx is not None and shift > 0:
+        num = _sequence_number(seq_idx)   # equal for two rows exactly when no start lies between them
         same = np.zeros((batch, L))
-        same[:, shift:] = (seq_idx[:, shift:] == seq_idx[:, :-shift])
+        same[:, shift:] = (num[:, shift:] == num[:, :-shift])
         ok = ok * same
     return ok[:, :, None]
 

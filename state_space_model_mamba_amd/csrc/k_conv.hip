@@ -15,10 +15,11 @@
 //   in the backward, the last W values of g = dout * act'(pre)) in registers,
 //   with DEPTH rows of loads in flight ahead of the row it computes.  The
 //   W-1 rows before its first row are read once more as a halo.
-// * The sequence ids of a block's rows (plus halos) are staged in LDS.  A
-//   window of W rows that lies in one sequence (nearly all of them) takes
-//   the unmasked path; a window across a sequence start, the first row or
-//   the end of the input takes the masked one.  Both tests are wave-uniform.
+// * Each staged row's sequence key (the number of sequence starts in the
+//   block's rows up to it) is staged in LDS.  A window of W rows that lies in
+//   one sequence (nearly all of them) takes the unmasked path; a window
+//   across a sequence start, the first row or the end of the input takes the
+//   masked one.  Both tests are wave-uniform.
 // * Backward: the filter and bias gradients of the block's NWAVE * TT rows are
 //   summed in registers (row order), then over the block's 4 waves in wave
 //   order through LDS, and parked in the block's own slot of the workspace;
@@ -117,9 +118,17 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
   const bool cok = c0 < C;
   const int64_t cl = cok ? c0 : C - VEC;                 // loads stay in bounds for idle lanes
 
+  // Sequence key of each staged row: a sequence starts at row t when t == 0
+  // or seq_idx changes at t, and a real row's key counts the starts among
+  // the staged rows up to it, so two rows less than W apart have equal keys
+  // exactly when no sequence starts between them.  Rows before the first and
+  // past the last get the sentinels.  (Start flags first, then one wave's
+  // prefix sum over the window.)
   for (int i = tid; i < SEQN; i += NTHR) {
     const int64_t t = tb0 - (W - 1) + i;
-    s_seq[i] = t < 0 ? BEFORE_START : t >= L ? PAST_END : (a.seq ? a.seq[b * L + t] : 0);
+    int st = 0;
+    if (t >= 0 && t < L) st = (t == 0) || (a.seq && a.seq[b * L + t] != a.seq[b * L + t - 1]);
+    s_seq[i] = st;
   }
   float wt[W][VEC], bi[VEC];
 #pragma unroll
@@ -127,6 +136,32 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
 #pragma unroll
     for (int k = 0; k < W; ++k) wt[k][e] = a.w[(cl + e) * W + k];
     bi[e] = a.bias ? a.bias[cl + e] : 0.f;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    constexpr int PER = (SEQN + WAVE - 1) / WAVE;   // consecutive entries per lane
+    int loc[PER], run = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = lane * PER + e;
+      run += i < SEQN ? s_seq[i] : 0;
+      loc[e] = run;
+    }
+    int incl = run;   // inclusive scan of the lanes' totals
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+      const int u = __shfl_up(incl, off, WAVE);
+      if (lane >= off) incl += u;
+    }
+    const int base = incl - run;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = lane * PER + e;
+      if (i < SEQN) {
+        const int64_t t = tb0 - (W - 1) + i;
+        s_seq[i] = t < 0 ? BEFORE_START : t >= L ? PAST_END : base + loc[e];
+      }
+    }
   }
   __syncthreads();
 

@@ -90,6 +90,25 @@ def test_fp32_packed_sequences_on_block_and_wave_boundaries():
     check(inputs, "silu", TOL["f32"], "fp32 packed boundaries")
 
 
+def test_fp32_recurring_sequence_ids():
+    # A sequence starts wherever seq_idx changes, so an id that comes back opens a new
+    # sequence: ids alternate between two values, with runs of one and two rows (shorter
+    # than the filter) and starts next to the walks' wave and block boundaries; row 1 of
+    # the batch uses other ids and lengths
+    lengths0 = [30, 1, 2, 97, 1, 380, 2, 1, 300, 1, 185]
+    lengths1 = [1, 2, 1, 510, 2, 484]
+    rows = []
+    for lengths, ids in ((lengths0, [0, 1] * 6), (lengths1, [5, 7] * 3)):
+        rows.append(torch.repeat_interleave(torch.tensor(ids[:len(lengths)], dtype=torch.int32),
+                                            torch.tensor(lengths)))
+    L = sum(lengths0)
+    assert L == sum(lengths1)
+    w = ConvWorkload("conv_f32_recur", batch=2, seqlen=L, channels=72, width=4, dtype="f32", seed=2115)
+    inputs = make_conv_inputs(w)
+    inputs["seq_idx"] = torch.stack(rows).contiguous()
+    check(inputs, "silu", TOL["f32"], "fp32 recurring ids")
+
+
 def test_bf16_packed_no_bias_short_rows():
     w = ConvWorkload("conv_bf16_packed", batch=1, seqlen=1500, channels=1032, width=4, dtype="bf16", seed=2120,
                      nseqs_packed=5, min_len=3)

@@ -78,6 +78,41 @@ def test_packed_row_is_separate_sequences():
     np.testing.assert_allclose(g["dbias"], db, rtol=0, atol=1e-11)
 
 
+def packed_equals_separate(mod, sidx, lengths, seed=30):
+    """mod's forward and gradients on one packed row equal its separate runs of the given lengths."""
+    L = sum(lengths)
+    x, w, bias, dout = rand((1, L, 3), seed), rand((3, 4), seed + 1), rand((3,), seed + 2), rand((1, L, 3), seed + 3)
+    out = mod.forward(x, w, bias, sidx, "silu")
+    g = mod.backward(x, w, bias, sidx, dout, "silu")
+    ok, t0, dw = True, 0, np.zeros_like(w)
+    for n in lengths:
+        sl = slice(t0, t0 + n)
+        gs = mod.backward(x[:, sl], w, bias, None, dout[:, sl], "silu")
+        ok &= np.allclose(out[:, sl], mod.forward(x[:, sl], w, bias, None, "silu"), rtol=0, atol=1e-12)
+        ok &= np.allclose(g["dx"][:, sl], gs["dx"], rtol=0, atol=1e-12)
+        dw += gs["dw"]
+        t0 += n
+    return bool(ok and np.allclose(g["dw"], dw, rtol=0, atol=1e-11))
+
+
+def test_sequences_start_where_seq_idx_changes():
+    """A sequence starts wherever seq_idx changes (the SSD's definition), so an id that comes back
+    later opens a new sequence: ids 0, 1, 0, 2, 0 in runs of 5, 1, 6, 2, 4 are five sequences, and
+    the packed row equals the five run separately.  Masking by equal ids instead would let the
+    width-4 filter join the runs of id 0 across the shorter runs between them, and must fail the
+    same check."""
+    lengths = [5, 1, 6, 2, 4]
+    sidx = np.repeat(np.array([0, 1, 0, 2, 0], dtype=np.int32), lengths)[None, :]
+    assert packed_equals_separate(oc, sidx, lengths)
+    src = open(oc.__file__).read()
+    old = "same[:, shift:] = (num[:, shift:] == num[:, :-shift])"
+    assert src.count(old) == 1
+    mod = types.ModuleType("conv1d_equal_ids")
+    exec(compile(src.replace(old, "same[:, shift:] = (seq_idx[:, shift:] == seq_idx[:, :-shift])"), mod.__name__,
+                 "exec"), mod.__dict__)
+    assert not packed_equals_separate(mod, sidx, lengths)
+
+
 def fd_grads(mod, x, w, bias, sidx, dout, act, eps=1e-6):
     """Central differences of l = sum dout * forward."""
     def loss(xx, ww, bb):
