@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "SSD bwd ms/layer + tokens/s at L=16K (1 GPU); bitwise repeat + % roofline"
+LEG_STEPS, LEG_WARMUP, CONFIG_STEPS = 100, 20, 50   # floors for the measurements beside the headline
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -539,6 +540,8 @@ def main():
                     help="skip the causal-conv1d forward / backward measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="time the headline workload only (not the other workloads of the family)")
+    ap.add_argument("--group-path", choices=("auto", "fused", "split"), default="auto",
+                    help="force one implementation of the group stage (default: the library's choice by shape)")
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -576,6 +579,11 @@ def main():
         sys.exit(1)
     w = WORKLOADS[args.workload or HEADLINE]
     dev = torch.device("cuda:0")
+    forced = {"auto": ssd.GROUP_PATH_BY_SHAPE, "fused": ssd.GROUP_PATH_FUSED, "split": ssd.GROUP_PATH_SPLIT}
+    ssd.set_group_path(forced[args.group_path])
+    global group_fused
+    if args.group_path != "auto":
+        group_fused = (lambda wl: True) if args.group_path == "fused" else (lambda wl: False)
     print(f"[bench] {w.name}: {args.warmup} warm-up and {args.steps} timed calls", file=sys.stderr, flush=True)
     rec, inputs, d, S, ws, z = measure_backward(torch, ssd, w, args.steps, args.warmup, dev)
     stage_ms = rec["stages_ms"]
@@ -619,19 +627,22 @@ def main():
         "stages_ms": stage_ms,
         "bitwise_repeat": rec["bitwise_repeat"],
     }
+    # the secondary measurements take at least LEG_WARMUP warm-up and LEG_STEPS timed calls, so that a
+    # short run of the headline (few warm-up calls) still times them warm
+    leg_steps, leg_warmup = max(args.steps, LEG_STEPS), max(args.warmup, LEG_WARMUP)
     if not args.no_forward:
-        res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=args.steps, warmup=args.warmup)
+        res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=leg_steps, warmup=leg_warmup)
     if not args.no_forward and not args.no_options:
-        res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=args.steps,
-                                                            warmup=args.warmup)
+        res["backward_with_dt_frontend"] = measure_frontend(torch, ssd, w, d, S, ws, steps=leg_steps,
+                                                            warmup=leg_warmup)
         # output gate: z ~ N(0, 1) (seeded), in the I/O dtype
         gz = torch.Generator().manual_seed(w.seed + 1)
         zg = torch.randn(tuple(d["x"].shape), generator=gz).to(d["x"].dtype).to(dev)
         res["backward_with_dt_frontend_and_gate"] = measure_frontend(
-            torch, ssd, w, d, S, ws, steps=args.steps, warmup=args.warmup, z=zg)
+            torch, ssd, w, d, S, ws, steps=leg_steps, warmup=leg_warmup, z=zg)
         del zg
     if not args.no_conv and not args.no_options:
-        res["causal_conv1d"] = measure_conv1d(torch, steps=args.steps, warmup=args.warmup,
+        res["causal_conv1d"] = measure_conv1d(torch, steps=leg_steps, warmup=leg_warmup,
                                               dev=dev, cpu=not args.no_cpu_baseline)
     del d, ws
     torch.cuda.empty_cache()
@@ -641,7 +652,7 @@ def main():
         res["configs"] = {}
         for name in ("bf16_L2048_H128", "bf16_B2_L4096_H128", "bf16_varlen7_L16384_N256"):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            crec = measure_backward(torch, ssd, WORKLOADS[name], args.steps, args.warmup, dev)[0]
+            crec = measure_backward(torch, ssd, WORKLOADS[name], max(args.steps, CONFIG_STEPS), leg_warmup, dev)[0]
             res["configs"][name] = crec
             torch.cuda.empty_cache()
     if args.calibration_copy:
