@@ -76,6 +76,8 @@ typedef struct {
   int64_t dstate;     /* N: multiple of 16 (f32) or 32 (bf16), <= 256 */
   int64_t chunk_size; /* Q: 64, 128 or 256 */
   int64_t nseqs;      /* number of sequence starts (see above); == batch without seq_idx */
+                      /* also: chunk_size * nheads * headdim and chunk_size * ngroups * dstate
+                         elements of the io dtype span at most 2^31 bytes */
   int32_t io_dtype;   /* ssd_io_dtype */
   int32_t reserved;   /* must be 0 */
 } ssd_shape;

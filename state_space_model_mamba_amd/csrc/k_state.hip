@@ -248,30 +248,50 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
   auto xhas = [&](int k) { return Cf::XV % NTHR == 0 || tid + NTHR * k < Cf::XV; };
   auto bhas = [&](int k) { return Cf::BV % NTHR == 0 || tid + NTHR * k < Cf::BV; };
 
+  // Addresses as in the forward walk: wave-uniform bases plus per-lane
+  // 32-bit offsets fixed for the whole walk.
+  const int vz = vgpr_zero();
+  const float* acs_bh = pb.acs + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * Q;
+  const int* seg_b = pb.segpos + static_cast<int64_t>(b) * pb.nc * Q;
+  const int* ci_b = pb.cinfo + static_cast<int64_t>(b) * pb.nc * CINFO;
+  const T* y_bh = ys + (static_cast<int64_t>(b) * pb.L * pb.H + h) * P;       // + t H P
+  const T* c_bg = cs + (static_cast<int64_t>(b) * pb.L * pb.G + g) * pb.N + n0;  // + t G N
+  const uint32_t xrb = static_cast<uint32_t>(pb.H * P * sizeof(T)), brb = static_cast<uint32_t>(pb.G * pb.N * sizeof(T));
+  auto xoff = [&](int k, int j) { return static_cast<uint32_t>(j) * xrb + ((tid + NTHR * k) % (P / VEC)) * 16u; };
+  auto boff = [&](int k, int j) { return static_cast<uint32_t>(j) * brb + ((tid + NTHR * k) % (NT / VEC)) * 16u; };
+  uint32_t xo[NXV], bo[NBV];
+#pragma unroll
+  for (int k = 0; k < NXV; ++k) xo[k] = xoff(k, xrow(k));
+#pragma unroll
+  for (int k = 0; k < NBV; ++k) bo[k] = boff(k, brow(k));
+  const int own = min(tid, Q - 1);
+
   uint4 xr[NXV], br[NBV];
   BwdRaw<NXV> raw;
   auto request = [&](int c) {
     c = max(c, 0);   // (before the first chunk: a harmless reload)
-    const int vz = vgpr_zero();
-    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-    raw.acs_end = pb.acs[bhc * Q + Q - 1 + vz];
-    raw.nstart = pb.cinfo[bc * CINFO + 0 + vz];
-    raw.seqbase = pb.cinfo[bc * CINFO + 3 + vz];
-    raw.seg0 = pb.segpos[bc * Q + vz];
-    raw.seg_own = pb.segpos[bc * Q + min(tid, Q - 1)];
+    const float* ac = acs_bh + c * Q;
+    const int* sg = seg_b + c * Q;
+    raw.acs_end = ac[Q - 1 + vz];
+    raw.nstart = ci_b[c * CINFO + 0 + vz];
+    raw.seqbase = ci_b[c * CINFO + 3 + vz];
+    raw.seg0 = sg[vz];
+    raw.seg_own = sg[own];
+    const int lastrow = pb.L - 1 - c * Q;   // rows past it are clamped (uniform)
+    const T* yc = y_bh + static_cast<int64_t>(c) * Q * pb.H * P;
+    const T* cc = c_bg + static_cast<int64_t>(c) * Q * pb.G * pb.N;
 #pragma unroll
     for (int k = 0; k < NXV; ++k) {
-      raw.acs[k] = pb.acs[bhc * Q + xrow(k)];
-      const int t = min(c * Q + xrow(k), pb.L - 1);
-      const int pv = (tid + NTHR * k) % (P / VEC);
-      if (xhas(k)) xr[k] = ld_global16(ys + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * VEC);
+      raw.acs[k] = ac[xrow(k)];
+      uint32_t o = xo[k];
+      if (lastrow < Q - 1) o = xoff(k, min(xrow(k), lastrow));
+      if (xhas(k)) xr[k] = ld_global16_at(yc, o);
     }
 #pragma unroll
     for (int k = 0; k < NBV; ++k) {
-      const int t = min(c * Q + brow(k), pb.L - 1);
-      const int nv = (tid + NTHR * k) % (NT / VEC);
-      if (bhas(k)) br[k] = ld_global16(cs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * VEC);
+      uint32_t o = bo[k];
+      if (lastrow < Q - 1) o = boff(k, min(brow(k), lastrow));
+      if (bhas(k)) br[k] = ld_global16_at(cc, o);
     }
   };
   struct Upd {
@@ -326,6 +346,8 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
 
   // the gradient at the end of the last chunk: zero, or the one handed in for the
   // state after the row's last position (padded positions leave the state unchanged)
+  // (as in the forward walk, this lane holds state row p = 16 pt + lane % 16
+  // and columns n0 + 16 nt + 4 (lane / 16) + r)
   f32x4_t dout[Cf::TPW];
 #pragma unroll
   for (int k = 0; k < Cf::TPW; ++k) {
@@ -335,10 +357,11 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
       const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dout[k][r] = pb.dlast[((static_cast<int64_t>(b) * pb.H + h) * P + pt * 16 + 4 * kg + r) * pb.N + n0 +
-                              nt * 16 + r16];
+        dout[k][r] = pb.dlast[((static_cast<int64_t>(b) * pb.H + h) * P + pt * 16 + r16) * pb.N + n0 +
+                              nt * 16 + 4 * kg + r];
     }
   }
+  T* const dst_bh = static_cast<T*>(pb.dstate) + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * P * pb.N;
   request(pb.nc - 1);
   Upd cur = stage(pb.nc - 1, 0);
   request(pb.nc - 2);
@@ -348,7 +371,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     Upd nxt = cur;
     if (c > 0) nxt = stage(c - 1, par ^ 1);   // (uniform)
     request(c - 2);
-    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
+    T* const dc = dst_bh + static_cast<int64_t>(c) * P * pb.N;   // this chunk's [P][N] state gradient
     const T* s_dyt = s_x0 + par * Bc::XSZ;
     const T* s_ct = s_b0 + par * Bc::BSZ;
     const int* s_seg = s_t0 + par * Bc::TSZ;
@@ -358,15 +381,13 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
       const int tile = w + Cf::NW * k;
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
-        const int n = n0 + nt * 16 + r16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          static_cast<T*>(pb.dstate)[(bhc * P + pt * 16 + 4 * kg + r) * pb.N + n] = Elem<T>::from_f(dout[k][r]);
+        const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
+        store4f<T>(dc + p * pb.N + n, dout[k]);
         if (cur.nstart == 0) {
           f32x4_t R = zero4();
 #pragma unroll
           for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
-            R = Mma<T>::mma(Cf::XTile::frag(s_dyt, pt * 16, k0), Cf::BTile::frag(s_ct, nt * 16, k0), R);
+            R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0), Cf::XTile::frag(s_dyt, pt * 16, k0), R);
 #pragma unroll
           for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + cur.decay * dout[k][r];
         } else {
@@ -375,8 +396,8 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
             const int lo = s_segstart[m], hi = s_segstart[m + 1];
             f32x4_t R = zero4();
             for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
-              R = Mma<T>::mma(mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi),
-                              Cf::BTile::frag(s_ct, nt * 16, k0), R);
+              R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0),
+                              mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi), R);
             const int rank = seg_rank(s_seg[lo]);
             if (rank == 0) {
               dhoff = R;
@@ -384,10 +405,9 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
               const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const int p = pt * 16 + 4 * kg + r;
                 float v = R[r];
                 if (hi == Q) v += cur.decay * dout[k][r];
-                pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n] = v;
+                pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n + r] = v;
               }
             }
           }

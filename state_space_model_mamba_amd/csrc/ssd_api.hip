@@ -96,6 +96,11 @@ int check_shape(const ssd_shape* s) {
   if (s->seqlen > (int64_t(1) << 30) || s->batch * s->nheads * nc > (int64_t(1) << 30) ||
       s->nheads > (1 << 20) || s->batch > (1 << 20) || s->nseqs > (int64_t(1) << 30))
     return SSD_ERR_UNSUPPORTED_SHAPE;
+  // the rows of one chunk of x / dy (all heads) and of B / C (all groups) are
+  // addressed with 32-bit byte offsets from the chunk's first row
+  const int64_t esize = is_bf16(s) ? 2 : 4;
+  if (Q * s->nheads * P * esize > (int64_t(1) << 31) || Q * s->ngroups * N * esize > (int64_t(1) << 31))
+    return SSD_ERR_UNSUPPORTED_SHAPE;
   const size_t lim = 160 * 1024;
   const bool fused = group_fused(s);
   const size_t group_lds =

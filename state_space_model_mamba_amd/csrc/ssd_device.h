@@ -176,19 +176,19 @@ __device__ __forceinline__ f32x4_t tile_mma_kk(f32x4_t acc, const T* a_base, int
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
-// A zero the compiler cannot see through.  Adding it to an LDS base pointer
-// inside a loop keeps the per-tile addresses derived from that base from
-// being hoisted out of the loop and held live (which otherwise costs one
-// register per address per tile across the whole loop).
-// zero in a vector register: an address offset by it makes the load a
+// A zero in a vector register: an address offset by it makes the load a
 // vector memory load (counted by vmcnt) rather than a scalar one, whose
-// completion every later LDS wait would also have to cover
+// completion every later LDS wait would also have to cover.
 __device__ __forceinline__ int vgpr_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
 }
 
+// A zero the compiler cannot see through.  Adding it to an LDS base pointer
+// inside a loop keeps the per-tile addresses derived from that base from
+// being hoisted out of the loop and held live (which otherwise costs one
+// register per address per tile across the whole loop).
 __device__ __forceinline__ int opaque_zero() {
   int z;
   asm volatile("; opaque zero" : "=s"(z) : "0"(0));

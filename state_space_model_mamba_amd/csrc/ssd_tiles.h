@@ -13,6 +13,14 @@ __device__ __forceinline__ uint4 ld_global16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte load at a 32-bit byte offset from a wave-uniform base: the 64-bit
+// base stays in scalar registers and the offset in one vector register (the
+// scalar-base form of the global load), so no 64-bit address arithmetic runs
+// per lane.
+__device__ __forceinline__ uint4 ld_global16_at(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+}
+
 __device__ __forceinline__ uint4 zero_u4() { return uint4{0u, 0u, 0u, 0u}; }
 
 // element e of a 16-byte vector holding T values
