@@ -542,6 +542,10 @@ def main():
                     help="time the headline workload only (not the other workloads of the family)")
     ap.add_argument("--group-path", choices=("auto", "fused", "split"), default="auto",
                     help="force one implementation of the group stage (default: the library's choice by shape)")
+    ap.add_argument("--exact-steps", action="store_true",
+                    help="time every measurement with exactly --steps / --warmup (short profiling runs); by "
+                         "default the measurements beside the headline take at least %d warm-up and %d timed calls"
+                         % (LEG_WARMUP, LEG_STEPS))
     ap.add_argument("--cpu-groups", type=int, default=0,
                     help="groups of heads the CPU baseline covers (0 = all)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -630,6 +634,9 @@ def main():
     # the secondary measurements take at least LEG_WARMUP warm-up and LEG_STEPS timed calls, so that a
     # short run of the headline (few warm-up calls) still times them warm
     leg_steps, leg_warmup = max(args.steps, LEG_STEPS), max(args.warmup, LEG_WARMUP)
+    config_steps = max(args.steps, CONFIG_STEPS)
+    if args.exact_steps:
+        leg_steps, leg_warmup, config_steps = args.steps, args.warmup, args.steps
     if not args.no_forward:
         res["forward"] = measure_forward(torch, ssd, w, d, S, ws, z, steps=leg_steps, warmup=leg_warmup)
     if not args.no_forward and not args.no_options:
@@ -652,7 +659,7 @@ def main():
         res["configs"] = {}
         for name in ("bf16_L2048_H128", "bf16_B2_L4096_H128", "bf16_varlen7_L16384_N256"):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            crec = measure_backward(torch, ssd, WORKLOADS[name], max(args.steps, CONFIG_STEPS), leg_warmup, dev)[0]
+            crec = measure_backward(torch, ssd, WORKLOADS[name], config_steps, leg_warmup, dev)[0]
             res["configs"][name] = crec
             torch.cuda.empty_cache()
     if args.calibration_copy:
