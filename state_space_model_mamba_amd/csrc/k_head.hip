@@ -192,6 +192,7 @@ __device__ __forceinline__ void tile_load(TileIn<T, Q, P, UNI>& in, int I, const
 
 template <typename T, int Q, int P, bool UNI, bool PF>
 __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&dxt)[2][P / 16], float (&ddti)[2],
+                                           float& mdiag,
                                            const T* s_xk, const T* s_dyk, const float* s_acs, const float* s_dt,
                                            const float* s_er, const int* s_seg, float* s_share, int w,
                                            B2Operands<T, Q, P>& b2, const float* cbsrc) {
@@ -272,6 +273,10 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
     sfx[1] = v[1] + sfx[2];
     sfx[0] = v[0] + sfx[1];
     if (diag) {
+      // this lane's entries of M's diagonal, M[i][i] = dy_i . x_i (their sum over
+      // the chunk is the head's dD term)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mdiag += (r16 == 4 * kg + r) ? m[r] : 0.f;
       // S[kappa][j] = sum over rows i >= kappa of V[i][j] (all of column j's
       // tiles below included), kept for j < kappa only, then summed over j
       const int sl = k == Split::NOFF ? 0 : 1;   // a constant once unrolled
@@ -467,18 +472,9 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   st_x.store(s_xk, LDP);
   st_dy.store(s_dyk, LDP);
   __syncthreads();
-  if (!pb.d_hp) {   // (uniform) dD of the head: sum of dy . x over the chunk
-    float dd = 0.f;
-    for (int v = tid; v < Q * P / VEC; v += NTHR) {
-      const int i = v / (P / VEC), p0 = (v % (P / VEC)) * VEC;
-      const uint4 dv = *reinterpret_cast<const uint4*>(s_dyk + i * LDP + p0);
-      const uint4 xv = *reinterpret_cast<const uint4*>(s_xk + i * LDP + p0);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dd += vget<T>(dv, e) * vget<T>(xv, e);
-    }
-    dd = wave_sum(dd);
-    if (l == 0) s_red[w] = dd;
-  } else {          // per channel: a thread's vectors all start at p0 = VEC (tid mod P / VEC)
+  // dD of the head (scalar D): the trace of M = dy x^T, summed from the
+  // diagonal tiles of phase B; per channel (d_hp): the channel sums of dy x
+  if (pb.d_hp) {    // (uniform) a thread's vectors all start at p0 = VEC (tid mod P / VEC)
     static_assert(NTHR % (P / VEC) == 0 && WAVE % (P / VEC) == 0, "fixed channel group per thread");
     float dd[VEC];
 #pragma unroll
@@ -517,10 +513,15 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
                           : nullptr;
   }
   constexpr bool PF = Mma<T>::KW == 8;   // bf16: first B2 round prefetched during phase B
+  float mdiag = 0.f;   // this lane's part of the trace of M
   if (uniform)
-    head_tiles<T, Q, P, true, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
+    head_tiles<T, Q, P, true, PF>(cb, dxt, ddti, mdiag, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
   else
-    head_tiles<T, Q, P, false, PF>(cb, dxt, ddti, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
+    head_tiles<T, Q, P, false, PF>(cb, dxt, ddti, mdiag, s_xk, s_dyk, s_acs, s_dt, s_er, s_seg, s_share, w, b2, cbsrc);
+  if (!pb.d_hp) {   // (uniform) the wave's share of the trace, summed over waves in phase D
+    const float dd = wave_sum(mdiag);
+    if (l == 0) s_red[w] = dd;
+  }
 
   // ---- phase B2: Z^T = dS B^T for the owned column tiles, in rounds of NBLK
   // dstate columns: dS rows from LDS (A operand), the owned columns' B rows
