@@ -70,12 +70,20 @@ def test_workspace_size_and_regions():
     (dict(batch=0), -1),
     (dict(seqlen=0), -1),
     (dict(io_dtype=ssd.SSD_IO_F32, chunk_size=256), -2),  # fp32 stops at chunk 128
+    # one chunk of x rows (Q H P) or of B rows (Q G N) beyond 2^31 bytes
+    (dict(nheads=65544, ngroups=8), -2),
+    (dict(nheads=16400, ngroups=16400, dstate=256), -2),
 ])
 def test_unsupported_shapes_are_rejected(kw, code):
     n = ctypes.c_size_t(0)
     rc = ssd.load_library().ssd_bwd_workspace_size(ctypes.byref(shape(**kw)), ctypes.byref(n))
     assert rc == code
     assert ssd.status_string(rc) != "unknown status"
+
+
+def test_largest_chunk_of_rows_is_supported():
+    # Q H P bf16 elements of exactly 2^31 bytes
+    assert ssd.workspace_size(shape(nheads=65536, ngroups=8)) > 0
 
 
 def test_supported_fp32_shape():
