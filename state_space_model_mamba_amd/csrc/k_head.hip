@@ -135,6 +135,31 @@ __device__ __forceinline__ float rowsum_quads(const float (&x)[4], int r16) {
   return rsum;
 }
 
+// One step of an inclusive segmented prefix sum over the lanes of a wave
+// (a lane whose flag is set starts a segment): the value and flag of the lane
+// that the DPP control CTRL reads in the rows ROWS (0 where it reads none)
+// join this lane's unless this lane's range already holds a segment start.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void seg_scan_step(float& v, int& f) {
+  const float tv = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+  const int tf = __builtin_amdgcn_update_dpp(0, f, CTRL, ROWS, 0xF, false);
+  v = f ? v : v + tv;
+  f |= tf;
+}
+
+// Inclusive segmented prefix sum over the 64 lanes in a fixed order: a
+// doubling scan within each row of 16 lanes (row_shr 1, 2, 4, 8), then row
+// 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the first
+// half's total into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ void seg_prefix_lanes(float& v, int& f) {
+  seg_scan_step<0x111, 0xF>(v, f);
+  seg_scan_step<0x112, 0xF>(v, f);
+  seg_scan_step<0x114, 0xF>(v, f);
+  seg_scan_step<0x118, 0xF>(v, f);
+  seg_scan_step<0x142, 0xA>(v, f);
+  seg_scan_step<0x143, 0xC>(v, f);
+}
+
 // LDS operands of one causal tile, requested one tile ahead so that their
 // latency hides behind the previous tile's arithmetic.
 template <typename T, int Q, int P, bool UNI>
@@ -628,12 +653,15 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   __syncthreads();
   if (w == 0) {
     tail = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tail)));
-    // reverse in-chunk, in-segment cumulative sum of ddAcs (fixed order)
+    // reverse in-chunk, in-segment cumulative sum of ddAcs (fixed order).  The
+    // lanes hold the positions in reverse order (lane l: positions from
+    // (63 - l) R), so the sum over later positions is a prefix over lanes.
+    const int lp = (WAVE - 1 - l) * R;   // this lane's first position
     float v[R], loc[R];
     int f[R];
 #pragma unroll
     for (int e = 0; e < R; ++e) {
-      const int i = l * R + e;
+      const int i = lp + e;
       v[e] = s_dd[i];
       if (i == Q - 1) v[e] += tail;
       f[e] = (i == Q - 1) || (seg_lo(s_seg[i + 1]) == i + 1);
@@ -650,25 +678,19 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
       }
       loc[e] = run;
     }
+    // lane l's run continues into the lanes below it (earlier positions) until
+    // a lane that holds a segment end: the segmented prefix over lanes, and the
+    // carry into lane l is lane l - 1's value (wave_shr:1; 0 for lane 0)
     float vl = run;
     int fl = any;
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-      const float vu = __shfl_down(vl, off, WAVE);
-      const int fu = __shfl_down(fl, off, WAVE);
-      if (l + off < WAVE) {
-        if (!fl) vl = vl + vu;
-        fl |= fu;
-      }
-    }
-    float carry = __shfl_down(vl, 1, WAVE);
-    if (l == WAVE - 1) carry = 0.f;
+    seg_prefix_lanes(vl, fl);
+    const float carry = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, vl), 0x138, 0xF, 0xF, false));
     int seen = 0;
     float dap = 0.f, dbp = 0.f;
     float da_k[R];
 #pragma unroll
     for (int e = R - 1; e >= 0; --e) {
-      const int k = l * R + e;
+      const int k = lp + e;
       if (f[e]) seen = 1;
       const float rc = seen ? loc[e] : loc[e] + carry;
       da_k[e] = s_daint[k] + rc;
@@ -677,13 +699,13 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     if (!pb.fe) {   // (uniform) ddt with respect to the dt the recurrence uses
 #pragma unroll
       for (int e = R - 1; e >= 0; --e) {
-        const int k = l * R + e, t = c * Q + k;
+        const int k = lp + e, t = c * Q + k;
         if (t < pb.L) pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = s_ddtp[k] + Ah * da_k[e];
       }
     } else {        // ... and on to the raw dt, through the front-end's derivative
 #pragma unroll
       for (int e = R - 1; e >= 0; --e) {
-        const int k = l * R + e, t = c * Q + k;
+        const int k = lp + e, t = c * Q + k;
         const float ddt = (s_ddtp[k] + Ah * da_k[e]) * s_dfe[k];
         if (t < pb.L) {
           pb.ddt[(static_cast<int64_t>(b) * pb.L + t) * pb.H + h] = ddt;
