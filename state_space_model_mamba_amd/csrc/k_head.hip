@@ -374,17 +374,35 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
   }
 }
 
+// Coordinates of item lb: items run head-in-group fastest, then chunk, then
+// group, then batch.  In 32-bit arithmetic (the shape check keeps the item
+// count below 2^30): a 64-bit division is a long software sequence, and the
+// items are decoded twice per item.
+struct ItemCoords {
+  int b, g, c, hh, h;
+};
+
+__device__ __forceinline__ ItemCoords item_coords(const Problem& pb, int64_t lb) {
+  const uint32_t x = static_cast<uint32_t>(lb);
+  const uint32_t hpg = static_cast<uint32_t>(pb.hpg), nc = static_cast<uint32_t>(pb.nc);
+  const uint32_t G = static_cast<uint32_t>(pb.G);
+  const uint32_t r1 = x / hpg, r2 = r1 / nc, b = r2 / G;
+  ItemCoords it;
+  it.hh = static_cast<int>(x - r1 * hpg);
+  it.c = static_cast<int>(r1 - r2 * nc);
+  it.g = static_cast<int>(r2 - b * G);
+  it.b = static_cast<int>(b);
+  it.h = it.g * pb.hpg + it.hh;
+  return it;
+}
+
 // x and dy rows of item lb -> registers (rows past L read as zero).
 template <typename T, int Q, int P>
 __device__ __forceinline__ void load_item_rows(const Problem& pb, int64_t lb,
                                                RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_x,
                                                RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy) {
-  const int hh = static_cast<int>(lb % pb.hpg);
-  int64_t rest = lb / pb.hpg;
-  const int c = static_cast<int>(rest % pb.nc);
-  rest /= pb.nc;
-  const int g = static_cast<int>(rest % pb.G), b = static_cast<int>(rest / pb.G);
-  const int h = g * pb.hpg + hh;
+  const ItemCoords it = item_coords(pb, lb);
+  const int c = it.c, b = it.b, h = it.h;
   auto row = [&](const void* base) {
     return [=, &pb](int i) -> const T* {
       const int t = c * Q + i;
@@ -428,13 +446,8 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   float* s_redp = s_red + ((W + 8 + 3) & ~3);   // (16-byte aligned)
   float* s_Dp = s_redp + W * P;   // D of this head, per channel (the scalar D repeated)
 
-  const int hh = static_cast<int>(lb % pb.hpg);
-  int64_t rest = lb / pb.hpg;
-  const int c = static_cast<int>(rest % pb.nc);
-  rest /= pb.nc;
-  const int g = static_cast<int>(rest % pb.G);
-  const int b = static_cast<int>(rest / pb.G);
-  const int h = g * pb.hpg + hh;
+  const ItemCoords it = item_coords(pb, lb);
+  const int c = it.c, g = it.g, b = it.b, h = it.h;
   const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
   const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
