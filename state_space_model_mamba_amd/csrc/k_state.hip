@@ -53,7 +53,15 @@ struct StateFwdCfg {
   using Cf = StateCfg<T, Q, P, NT>;
   static constexpr int XSZ = Q * Cf::XTile::LD;   // elements of one x buffer
   static constexpr int BSZ = Q * Cf::BTile::LD;
-  static constexpr size_t LDS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T);
+  static constexpr size_t LDS_ROWS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T);
+  // Hin leaves through LDS when it fits: each chunk's state tile [P][NT] is
+  // written there (two buffers, taking turns) and stored during the next
+  // chunk as whole rows, 16 bytes per lane
+  static constexpr int LDH = NT + Cf::VEC;          // row pitch of a staged state tile
+  static constexpr int HSZ = P * LDH;
+  static constexpr bool HSTAGE = LDS_ROWS + 2 * static_cast<size_t>(HSZ) * sizeof(T) <= 160 * 1024;
+  static constexpr size_t LDS = LDS_ROWS + (HSTAGE ? 2 * static_cast<size_t>(HSZ) * sizeof(T) : 0);
+  static constexpr int HV = P * NT / Cf::VEC;       // 16-byte vectors of one state tile
 };
 
 // What a chunk's staging needs, as loaded (nothing derived, so nothing waits
@@ -73,6 +81,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* const s_x0 = reinterpret_cast<T*>(smem);
   T* const s_b0 = s_x0 + 2 * Fc::XSZ;
+  T* const s_h0 = s_b0 + 2 * Fc::BSZ;   // (HSTAGE) the two staged state tiles
 
   const int ntiles = pb.N / NT;
   const int64_t total = static_cast<int64_t>(pb.B) * pb.H * ntiles;
@@ -84,6 +93,15 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   const T* xs = static_cast<const T*>(pb.x);
   const T* bs = static_cast<const T*>(pb.Bm);
+  // (HSTAGE) the staged state tile of chunk c (buffer c & 1) -> Hin_c, whole rows
+  auto store_staged = [&](int c) {
+    const T* sh = s_h0 + (c & 1) * Fc::HSZ;
+    T* hc = static_cast<T*>(pb.hin) + ((static_cast<int64_t>(b) * pb.H + h) * pb.nc + c) * P * pb.N + n0;
+    for (int v = tid; v < Fc::HV; v += NTHR) {
+      const int p = v / (NT / VEC), q = (v % (NT / VEC)) * VEC;
+      *reinterpret_cast<uint4*>(hc + p * pb.N + q) = *reinterpret_cast<const uint4*>(sh + p * Fc::LDH + q);
+    }
+  };
 
   // the thread's staged vectors: x vector k is row xrow(k), B vector k row
   // brow(k); on small shapes some threads have fewer vectors than others
@@ -171,6 +189,9 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
     Upd nxt = cur;
     if (c + 1 < pb.nc) nxt = stage(c + 1);   // (uniform)
     request(c + 2);
+    if constexpr (Fc::HSTAGE) {
+      if (c > 0) store_staged(c - 1);   // (staged before the last barrier)
+    }
     const T* sx = s_x0 + (c & 1) * Fc::XSZ;
     const T* sb = s_b0 + (c & 1) * Fc::BSZ;
 #pragma unroll
@@ -186,7 +207,10 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int p = pt * 16 + 4 * kg + r;
-          static_cast<T*>(pb.hin)[(bhc * P + p) * pb.N + n] = Elem<T>::from_f(st[k][r]);
+          if constexpr (Fc::HSTAGE)
+            s_h0[(c & 1) * Fc::HSZ + p * Fc::LDH + nt * 16 + r16] = Elem<T>::from_f(st[k][r]);
+          else
+            static_cast<T*>(pb.hin)[(bhc * P + p) * pb.N + n] = Elem<T>::from_f(st[k][r]);
           if (cur.nstart == 0) {
             st[k][r] = cur.decay * st[k][r] + S[r];
           } else {
@@ -200,6 +224,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
     __syncthreads();
     cur = nxt;
   }
+  if constexpr (Fc::HSTAGE) store_staged(pb.nc - 1);
 }
 
 // Backward walk, chunks from the last down, with the forward walk's
@@ -212,7 +237,14 @@ struct StateBwdCfg {
   static constexpr int XSZ = Q * Cf::XTile::LD;
   static constexpr int BSZ = Q * Cf::BTile::LD;
   static constexpr int TSZ = 2 * Q + 1;   // segpos[Q], segment starts[Q + 1]
-  static constexpr size_t LDS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T) + 2 * TSZ * sizeof(int);
+  static constexpr size_t LDS_ROWS = 2 * static_cast<size_t>(XSZ + BSZ) * sizeof(T) + 2 * TSZ * sizeof(int);
+  // dS leaves through LDS as whole rows when it fits (as Hin in the forward walk)
+  static constexpr int LDH = NT + Cf::VEC;
+  static constexpr int HSZ = P * LDH;
+  static constexpr size_t OFF_H = (LDS_ROWS + 15) / 16 * 16;   // the staged tiles (16-byte aligned)
+  static constexpr bool HSTAGE = OFF_H + 2 * static_cast<size_t>(HSZ) * sizeof(T) <= 160 * 1024;
+  static constexpr size_t LDS = HSTAGE ? OFF_H + 2 * static_cast<size_t>(HSZ) * sizeof(T) : LDS_ROWS;
+  static constexpr int HV = P * NT / Cf::VEC;
 };
 
 template <int NXV>
@@ -362,6 +394,16 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     }
   }
   T* const dst_bh = static_cast<T*>(pb.dstate) + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * P * pb.N;
+  // (HSTAGE) the two staged state-gradient tiles, after the segment tables
+  T* const s_h0 = reinterpret_cast<T*>(smem + Bc::OFF_H);
+  auto store_staged = [&](int c, int buf) {
+    const T* sh = s_h0 + buf * Bc::HSZ;
+    T* dc = dst_bh + static_cast<int64_t>(c) * P * pb.N + n0;
+    for (int v = tid; v < Bc::HV; v += NTHR) {
+      const int p = v / (NT / VEC), q = (v % (NT / VEC)) * VEC;
+      *reinterpret_cast<uint4*>(dc + p * pb.N + q) = *reinterpret_cast<const uint4*>(sh + p * Bc::LDH + q);
+    }
+  };
   request(pb.nc - 1);
   Upd cur = stage(pb.nc - 1, 0);
   request(pb.nc - 2);
@@ -371,6 +413,9 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     Upd nxt = cur;
     if (c > 0) nxt = stage(c - 1, par ^ 1);   // (uniform)
     request(c - 2);
+    if constexpr (Bc::HSTAGE) {
+      if (c < pb.nc - 1) store_staged(c + 1, par ^ 1);   // (staged before the last barrier)
+    }
     T* const dc = dst_bh + static_cast<int64_t>(c) * P * pb.N;   // this chunk's [P][N] state gradient
     const T* s_dyt = s_x0 + par * Bc::XSZ;
     const T* s_ct = s_b0 + par * Bc::BSZ;
@@ -382,7 +427,10 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
       if (tile < Cf::NTILE) {
         const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
         const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
-        store4f<T>(dc + p * pb.N + n, dout[k]);
+        if constexpr (Bc::HSTAGE)
+          store4f<T>(s_h0 + par * Bc::HSZ + p * Bc::LDH + nt * 16 + 4 * kg, dout[k]);
+        else
+          store4f<T>(dc + p * pb.N + n, dout[k]);
         if (cur.nstart == 0) {
           f32x4_t R = zero4();
 #pragma unroll
@@ -418,6 +466,7 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     __syncthreads();
     cur = nxt;
   }
+  if constexpr (Bc::HSTAGE) store_staged(0, (pb.nc - 1) & 1);
 }
 
 // N-tile width of the state kernels.
