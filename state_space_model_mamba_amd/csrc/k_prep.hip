@@ -22,6 +22,26 @@ namespace ssd {
 
 constexpr int PREP_HEADS = 4;    // heads per block of k_prep
 
+// The double that the DPP control CTRL reads from another lane (rows ROWS;
+// +0.0 where it reads none), both halves moved the same way.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, ROWS, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, ROWS, 0xF, false));
+  return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
+// One step of the segmented inclusive scan over the wave's lanes (a lane
+// whose flag is set starts a segment)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void seg_step_f64(double& v, int& f) {
+  const double tv = dpp_f64<CTRL, ROWS>(v);
+  const int tf = __builtin_amdgcn_update_dpp(0, f, CTRL, ROWS, 0xF, false);
+  v = f ? v : tv + v;
+  f |= tf;
+}
+
 template <int Q>
 __global__ __launch_bounds__(256) void k_prep(Problem pb) {
   static_assert(Q % WAVE == 0 && Q <= 256, "chunk size");
@@ -60,23 +80,23 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
     s_rank[tid] = st;
   }
   __syncthreads();
-  // integer inclusive scans (max for the segment start, sum for the rank)
-  for (int off = 1; off < Q; off <<= 1) {
-    int lo = 0, rk = 0;
-    const bool act = tid < Q && tid >= off;
-    if (act) {
-      lo = s_lo[tid - off];
-      rk = s_rank[tid - off];
-    }
-    __syncthreads();
-    if (act) {
-      s_lo[tid] = max(s_lo[tid], lo);
-      s_rank[tid] += rk;
-    }
-    __syncthreads();
-  }
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-  if (blockIdx.z == 0) {
+  if (blockIdx.z == 0) {   // (uniform) the chunk's segment table, written by its first block of heads
+    // integer inclusive scans (max for the segment start, sum for the rank)
+    for (int off = 1; off < Q; off <<= 1) {
+      int lo = 0, rk = 0;
+      const bool act = tid < Q && tid >= off;
+      if (act) {
+        lo = s_lo[tid - off];
+        rk = s_rank[tid - off];
+      }
+      __syncthreads();
+      if (act) {
+        s_lo[tid] = max(s_lo[tid], lo);
+        s_rank[tid] += rk;
+      }
+      __syncthreads();
+    }
     if (tid < Q) pb.segpos[bc * Q + tid] = s_lo[tid] | (s_rank[tid] << 16);
     if (tid == 0) {
       pb.cinfo[bc * CINFO + 0] = s_rank[Q - 1];
@@ -88,8 +108,10 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
   // Segmented inclusive cumsum of a = dt A over the chunk, per head, in one
   // order fixed by Q alone: the chunk is cut into R runs of 64 positions
   // (lane l holds position 64 e + l); each run is scanned across the wave
-  // with a Hillis-Steele segmented scan (shuffle offsets 1, 2, ..., 32), and
-  // each run starts from the carry of the previous one.
+  // with a segmented scan in DPP steps (a doubling scan within each row of
+  // 16 lanes, then row 0's total into row 1 and row 2's into row 3, then the
+  // first half's total into rows 2 and 3), and each run starts from the
+  // carry of the previous one.
   const int w = wave_id(), l = lane_id();
   for (int hh = w; hh < PREP_HEADS && h0 + hh < pb.H; hh += 4) {
     const int h = h0 + hh;
@@ -102,21 +124,20 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
       const float d = s_dt[i * LDD + hh];
       int fl = (i == 0) || s_flag[i];
       double v = static_cast<double>(d) * Ah;
-#pragma unroll
-      for (int off = 1; off < WAVE; off <<= 1) {
-        const double vu = __shfl_up(v, off, WAVE);
-        const int fu = __shfl_up(fl, off, WAVE);
-        if (l >= off) {
-          if (!fl) v = vu + v;
-          fl |= fu;
-        }
-      }
+      seg_step_f64<0x111, 0xF>(v, fl);   // row_shr:1
+      seg_step_f64<0x112, 0xF>(v, fl);   // row_shr:2
+      seg_step_f64<0x114, 0xF>(v, fl);   // row_shr:4
+      seg_step_f64<0x118, 0xF>(v, fl);   // row_shr:8
+      seg_step_f64<0x142, 0xA>(v, fl);   // row_bcast:15 into rows 1 and 3
+      seg_step_f64<0x143, 0xC>(v, fl);   // row_bcast:31 into rows 2 and 3
       // positions not preceded by a start within this run continue the carry
       const double acs = fl ? v : carry + v;
       pb.acs[out + i] = static_cast<float>(acs);
       pb.dtc[out + i] = d;
       if (pb.fe) pb.dfe[out + i] = s_dfe[i * LDD + hh];
-      carry = __shfl(acs, WAVE - 1, WAVE);
+      const uint64_t cu = __builtin_bit_cast(uint64_t, acs);   // lane 63's value, to every lane
+      carry = __builtin_bit_cast(double, static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(cu)), WAVE - 1))) |
+                                             (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(cu >> 32)), WAVE - 1))) << 32));
     }
   }
 }
