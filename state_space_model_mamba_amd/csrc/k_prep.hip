@@ -143,29 +143,32 @@ __global__ __launch_bounds__(256) void k_prep(Problem pb) {
 }
 
 // Global numbering of sequence starts: exclusive prefix sum of the per-chunk
-// start counts in row-major (batch, chunk) order.  One block; integer only.
-__global__ __launch_bounds__(256) void k_seqbase(Problem pb) {
-  __shared__ int s[256];
-  __shared__ int s_run;
-  const int tid = threadIdx.x;
+// start counts in row-major (batch, chunk) order.  One wave; integer only:
+// 64 counts at a time, each batch a DPP inclusive scan over the lanes (a
+// doubling scan within each row of 16, then row 0's total into row 1 and row
+// 2's into row 3, then the first half's into rows 2 and 3) plus the running
+// total of the batches before.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int scan_step_i32(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+
+__global__ __launch_bounds__(64) void k_seqbase(Problem pb) {
+  const int l = threadIdx.x;
   const int total = pb.B * pb.nc;
-  if (tid == 0) s_run = 0;
-  __syncthreads();
-  for (int base = 0; base < total; base += 256) {
-    const int idx = base + tid;
+  int run = 0;
+  for (int base = 0; base < total; base += WAVE) {
+    const int idx = base + l;
     const int v = idx < total ? pb.cinfo[static_cast<int64_t>(idx) * CINFO] : 0;
-    s[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int u = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += u;
-      __syncthreads();
-    }
-    if (idx < total) pb.cinfo[static_cast<int64_t>(idx) * CINFO + 3] = s_run + s[tid] - v;
-    __syncthreads();
-    if (tid == 255) s_run += s[255];
-    __syncthreads();
+    int incl = v;
+    incl = scan_step_i32<0x111, 0xF>(incl);   // row_shr:1
+    incl = scan_step_i32<0x112, 0xF>(incl);   // row_shr:2
+    incl = scan_step_i32<0x114, 0xF>(incl);   // row_shr:4
+    incl = scan_step_i32<0x118, 0xF>(incl);   // row_shr:8
+    incl = scan_step_i32<0x142, 0xA>(incl);   // row_bcast:15 into rows 1 and 3
+    incl = scan_step_i32<0x143, 0xC>(incl);   // row_bcast:31 into rows 2 and 3
+    if (idx < total) pb.cinfo[static_cast<int64_t>(idx) * CINFO + 3] = run + incl - v;
+    run += __builtin_amdgcn_readlane(incl, WAVE - 1);
   }
 }
 
@@ -222,7 +225,7 @@ hipError_t launch_prep(const Problem& pb, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_seqbase, dim3(1), dim3(256), 0, s, pb);
+  hipLaunchKernelGGL(k_seqbase, dim3(1), dim3(WAVE), 0, s, pb);
   return hipGetLastError();
 }
 
