@@ -9,8 +9,9 @@
 // as dA add many such terms with heavy cancellation, so Acs is scanned in
 // double and rounded to float once.  The scan order is fixed by the chunk
 // size alone: the chunk is scanned as Q/64 runs of 64 positions, each with a
-// 64-lane Hillis-Steele segmented scan (shuffle offsets 1, 2, ..., 32) that
-// starts from the previous run's last value.
+// 64-lane segmented scan in DPP steps (row shifts by 1, 2, 4 and 8 lanes, then
+// the row-broadcast steps across rows) that starts from the previous run's
+// last value.
 // A block handles PREP_HEADS (4) heads of one (batch, chunk), one per wave.  That page
 // reports that a cumsum whose result changes with the block shape broke
 // run-to-run reproducibility; here the result does not depend on how many

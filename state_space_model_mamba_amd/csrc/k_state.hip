@@ -35,8 +35,14 @@ struct StateCfg {
   static constexpr int NXV = (XV + NTHR - 1) / NTHR;
   static constexpr int BV = Q * NT / VEC;      // vectors of one B/C chunk tile
   static constexpr int NBV = (BV + NTHR - 1) / NTHR;
-  static constexpr int PT = P / 16, NTT = NT / 16, NTILE = PT * NTT, TPW = (NTILE + NW - 1) / NW;
-  static_assert(NW % NTT == 0, "a wave's tiles share their state-column tile");
+  static constexpr int PT = P / 16, NTT = NT / 16;
+  // The chunk product is register-blocked: wave w < NBLK forms a BNB x BPB
+  // block of 16 x 16 tiles (state columns x state rows), so each operand
+  // fragment read from LDS serves two tiles and the LDS reads of a chunk are
+  // half those of one tile per wave; the other waves only stage rows.
+  static constexpr int BPB = PT % 2 == 0 ? 2 : 1, BNB = NTT % 2 == 0 ? 2 : 1;
+  static constexpr int NBN = NTT / BNB, NBLK = (PT / BPB) * NBN;
+  static_assert(NBLK <= NW, "a wave per block");
   static_assert(NTHR >= Q, "one thread per chunk position");
   static_assert(P % 16 == 0 && NT % 16 == 0 && Q % Mma<T>::KSTEP == 0, "tile shape");
 };
@@ -110,30 +116,50 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
   auto xhas = [&](int k) { return Cf::XV % NTHR == 0 || tid + NTHR * k < Cf::XV; };
   auto bhas = [&](int k) { return Cf::BV % NTHR == 0 || tid + NTHR * k < Cf::BV; };
 
+  // Addresses: wave-uniform bases per chunk plus per-lane 32-bit offsets
+  // fixed for the whole walk (recomputed only for a chunk that passes L).
+  const int vz = vgpr_zero();
+  const float* acs_bh = pb.acs + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * Q;
+  const float* dt_bh = pb.dtc + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * Q;
+  const int* seg_b = pb.segpos + static_cast<int64_t>(b) * pb.nc * Q;
+  const int* ci_b = pb.cinfo + static_cast<int64_t>(b) * pb.nc * CINFO;
+  const T* x_bh = xs + (static_cast<int64_t>(b) * pb.L * pb.H + h) * P;       // + t H P
+  const T* b_bg = bs + (static_cast<int64_t>(b) * pb.L * pb.G + g) * pb.N + n0;  // + t G N
+  const uint32_t xrb = static_cast<uint32_t>(pb.H * P * sizeof(T)), brb = static_cast<uint32_t>(pb.G * pb.N * sizeof(T));
+  auto xoff = [&](int k, int j) { return static_cast<uint32_t>(j) * xrb + ((tid + NTHR * k) % (P / VEC)) * 16u; };
+  auto boff = [&](int k, int j) { return static_cast<uint32_t>(j) * brb + ((tid + NTHR * k) % (NT / VEC)) * 16u; };
+  uint32_t xo[NXV], bo[NBV];
+#pragma unroll
+  for (int k = 0; k < NXV; ++k) xo[k] = xoff(k, xrow(k));
+#pragma unroll
+  for (int k = 0; k < NBV; ++k) bo[k] = boff(k, brow(k));
+
   uint4 xr[NXV], br[NBV];
   FwdRaw<NXV> raw;
   auto request = [&](int c) {
     c = min(c, pb.nc - 1);   // (past the last chunk: a harmless reload)
-    const int vz = vgpr_zero();
-    const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
-    raw.acs_end = pb.acs[bhc * Q + Q - 1 + vz];
-    raw.seg_last = pb.segpos[bc * Q + Q - 1 + vz];
-    raw.nstart = pb.cinfo[bc * CINFO + 0 + vz];
-    raw.seqbase = pb.cinfo[bc * CINFO + 3 + vz];
+    const float* ac = acs_bh + c * Q;
+    const float* dc = dt_bh + c * Q;
+    raw.acs_end = ac[Q - 1 + vz];
+    raw.seg_last = seg_b[c * Q + Q - 1 + vz];
+    raw.nstart = ci_b[c * CINFO + 0 + vz];
+    raw.seqbase = ci_b[c * CINFO + 3 + vz];
+    const int lastrow = pb.L - 1 - c * Q;   // rows past it are clamped (uniform)
+    const T* xc = x_bh + static_cast<int64_t>(c) * Q * pb.H * P;
+    const T* bc = b_bg + static_cast<int64_t>(c) * Q * pb.G * pb.N;
 #pragma unroll
     for (int k = 0; k < NXV; ++k) {
-      raw.acs[k] = pb.acs[bhc * Q + xrow(k)];
-      raw.dt[k] = pb.dtc[bhc * Q + xrow(k)];
-      const int t = min(c * Q + xrow(k), pb.L - 1);
-      const int pv = (tid + NTHR * k) % (P / VEC);
-      if (xhas(k)) xr[k] = ld_global16(xs + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P + pv * VEC);
+      raw.acs[k] = ac[xrow(k)];
+      raw.dt[k] = dc[xrow(k)];
+      uint32_t o = xo[k];
+      if (lastrow < Q - 1) o = xoff(k, min(xrow(k), lastrow));
+      if (xhas(k)) xr[k] = ld_global16_at(xc, o);
     }
 #pragma unroll
     for (int k = 0; k < NBV; ++k) {
-      const int t = min(c * Q + brow(k), pb.L - 1);
-      const int nv = (tid + NTHR * k) % (NT / VEC);
-      if (bhas(k)) br[k] = ld_global16(bs + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + n0 + nv * VEC);
+      uint32_t o = bo[k];
+      if (lastrow < Q - 1) o = boff(k, min(brow(k), lastrow));
+      if (bhas(k)) br[k] = ld_global16_at(bc, o);
     }
   };
   // per-chunk values the state update needs
@@ -177,9 +203,13 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
     return u;
   };
 
-  f32x4_t st[Cf::TPW];
+  constexpr int BPB = Cf::BPB, BNB = Cf::BNB, NBN = Cf::NBN, NBLK = Cf::NBLK;
+  f32x4_t st[BNB][BPB];   // (waves w < NBLK) the state of this wave's tiles
 #pragma unroll
-  for (int k = 0; k < Cf::TPW; ++k) st[k] = zero4();
+  for (int i = 0; i < BNB; ++i)
+#pragma unroll
+    for (int j = 0; j < BPB; ++j) st[i][j] = zero4();
+  const int bp = w / NBN, bn = w % NBN;
   request(0);
   Upd cur = stage(0);
   request(1);
@@ -194,32 +224,48 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_fwd(Pro
     }
     const T* sx = s_x0 + (c & 1) * Fc::XSZ;
     const T* sb = s_b0 + (c & 1) * Fc::BSZ;
+    if (w < NBLK) {   // (wave-uniform)
+      // S^T (the B tiles as the A operand): for tile (i, j) this lane holds
+      // state row p = 16 pt + lane % 16 and the four columns n .. n + 3,
+      // n = n0 + 16 nt + 4 (lane / 16), with pt = BPB bp + j, nt = BNB bn + i
+      f32x4_t S[BNB][BPB];
 #pragma unroll
-    for (int k = 0; k < Cf::TPW; ++k) {
-      const int tile = w + Cf::NW * k;
-      if (tile < Cf::NTILE) {
-        const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
-        f32x4_t S = zero4();
+      for (int i = 0; i < BNB; ++i)
 #pragma unroll
-        for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
-          S = Mma<T>::mma(Cf::XTile::frag(sx, pt * 16, k0), Cf::BTile::frag(sb, nt * 16, k0), S);
-        const int n = n0 + nt * 16 + r16;
+        for (int j = 0; j < BPB; ++j) S[i][j] = zero4();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int p = pt * 16 + 4 * kg + r;
+      for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP) {
+        typename Mma<T>::frag af[BNB], bfr[BPB];
+#pragma unroll
+        for (int i = 0; i < BNB; ++i) af[i] = Cf::BTile::frag(sb, (BNB * bn + i) * 16, k0);
+#pragma unroll
+        for (int j = 0; j < BPB; ++j) bfr[j] = Cf::XTile::frag(sx, (BPB * bp + j) * 16, k0);
+#pragma unroll
+        for (int i = 0; i < BNB; ++i)
+#pragma unroll
+          for (int j = 0; j < BPB; ++j) S[i][j] = Mma<T>::mma(af[i], bfr[j], S[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < BNB; ++i)
+#pragma unroll
+        for (int j = 0; j < BPB; ++j) {
+          const int pt = BPB * bp + j, nt = BNB * bn + i;
+          const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
           if constexpr (Fc::HSTAGE)
-            s_h0[(c & 1) * Fc::HSZ + p * Fc::LDH + nt * 16 + r16] = Elem<T>::from_f(st[k][r]);
+            store4f<T>(s_h0 + (c & 1) * Fc::HSZ + p * Fc::LDH + nt * 16 + 4 * kg, st[i][j]);
           else
-            static_cast<T*>(pb.hin)[(bhc * P + p) * pb.N + n] = Elem<T>::from_f(st[k][r]);
-          if (cur.nstart == 0) {
-            st[k][r] = cur.decay * st[k][r] + S[r];
-          } else {
-            float init = 0.f;
-            if (pb.h0) init = cur.decay * pb.h0[((static_cast<int64_t>(cur.s_last) * pb.H + h) * P + p) * pb.N + n];
-            st[k][r] = S[r] + init;
+            store4f<T>(static_cast<T*>(pb.hin) + (bhc * P + p) * pb.N + n, st[i][j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (cur.nstart == 0) {
+              st[i][j][r] = cur.decay * st[i][j][r] + S[i][j][r];
+            } else {
+              float init = 0.f;
+              if (pb.h0) init = cur.decay * pb.h0[((static_cast<int64_t>(cur.s_last) * pb.H + h) * P + p) * pb.N + n + r];
+              st[i][j][r] = S[i][j][r] + init;
+            }
           }
         }
-      }
     }
     __syncthreads();
     cur = nxt;
@@ -378,21 +424,25 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
 
   // the gradient at the end of the last chunk: zero, or the one handed in for the
   // state after the row's last position (padded positions leave the state unchanged)
-  // (as in the forward walk, this lane holds state row p = 16 pt + lane % 16
-  // and columns n0 + 16 nt + 4 (lane / 16) + r)
-  f32x4_t dout[Cf::TPW];
+  // (as in the forward walk, for tile (i, j) of its block this lane holds
+  // state row p = 16 pt + lane % 16 and columns n0 + 16 nt + 4 (lane / 16) + r,
+  // pt = BPB bp + j, nt = BNB bn + i)
+  constexpr int BPB = Cf::BPB, BNB = Cf::BNB, NBN = Cf::NBN, NBLK = Cf::NBLK;
+  const int bp = w / NBN, bn = w % NBN;
+  f32x4_t dout[BNB][BPB];
 #pragma unroll
-  for (int k = 0; k < Cf::TPW; ++k) {
-    dout[k] = zero4();
-    const int tile = w + Cf::NW * k;
-    if (pb.dlast && tile < Cf::NTILE) {
-      const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
+  for (int i = 0; i < BNB; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        dout[k][r] = pb.dlast[((static_cast<int64_t>(b) * pb.H + h) * P + pt * 16 + r16) * pb.N + n0 +
-                              nt * 16 + 4 * kg + r];
+    for (int j = 0; j < BPB; ++j) {
+      dout[i][j] = zero4();
+      const int pt = BPB * bp + j, nt = BNB * bn + i;
+      if (pb.dlast && w < NBLK) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dout[i][j][r] = pb.dlast[((static_cast<int64_t>(b) * pb.H + h) * P + pt * 16 + r16) * pb.N + n0 +
+                                   nt * 16 + 4 * kg + r];
+      }
     }
-  }
   T* const dst_bh = static_cast<T*>(pb.dstate) + (static_cast<int64_t>(b) * pb.H + h) * pb.nc * P * pb.N;
   // (HSTAGE) the two staged state-gradient tiles, after the segment tables
   T* const s_h0 = reinterpret_cast<T*>(smem + Bc::OFF_H);
@@ -421,46 +471,71 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
     const T* s_ct = s_b0 + par * Bc::BSZ;
     const int* s_seg = s_t0 + par * Bc::TSZ;
     const int* s_segstart = s_seg + Q;
+    if (w < NBLK) {   // (wave-uniform)
 #pragma unroll
-    for (int k = 0; k < Cf::TPW; ++k) {
-      const int tile = w + Cf::NW * k;
-      if (tile < Cf::NTILE) {
-        const int pt = tile / Cf::NTT, nt = tile % Cf::NTT;
-        const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
-        if constexpr (Bc::HSTAGE)
-          store4f<T>(s_h0 + par * Bc::HSZ + p * Bc::LDH + nt * 16 + 4 * kg, dout[k]);
-        else
-          store4f<T>(dc + p * pb.N + n, dout[k]);
-        if (cur.nstart == 0) {
-          f32x4_t R = zero4();
+      for (int i = 0; i < BNB; ++i)
 #pragma unroll
-          for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP)
-            R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0), Cf::XTile::frag(s_dyt, pt * 16, k0), R);
+        for (int j = 0; j < BPB; ++j) {
+          const int pt = BPB * bp + j, nt = BNB * bn + i;
+          const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
+          if constexpr (Bc::HSTAGE)
+            store4f<T>(s_h0 + par * Bc::HSZ + p * Bc::LDH + nt * 16 + 4 * kg, dout[i][j]);
+          else
+            store4f<T>(dc + p * pb.N + n, dout[i][j]);
+        }
+      if (cur.nstart == 0) {
+        f32x4_t R[BNB][BPB];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dout[k][r] = R[r] + cur.decay * dout[k][r];
-        } else {
-          f32x4_t dhoff = zero4();
-          for (int m = 0; m < cur.nseg; ++m) {
-            const int lo = s_segstart[m], hi = s_segstart[m + 1];
-            f32x4_t R = zero4();
-            for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
-              R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0),
-                              mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi), R);
-            const int rank = seg_rank(s_seg[lo]);
-            if (rank == 0) {
-              dhoff = R;
-            } else if (pb.dinit) {
-              const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
+        for (int i = 0; i < BNB; ++i)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                float v = R[r];
-                if (hi == Q) v += cur.decay * dout[k][r];
-                pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n + r] = v;
+          for (int j = 0; j < BPB; ++j) R[i][j] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < Q; k0 += Mma<T>::KSTEP) {
+          typename Mma<T>::frag af[BNB], bfr[BPB];
+#pragma unroll
+          for (int i = 0; i < BNB; ++i) af[i] = Cf::BTile::frag(s_ct, (BNB * bn + i) * 16, k0);
+#pragma unroll
+          for (int j = 0; j < BPB; ++j) bfr[j] = Cf::XTile::frag(s_dyt, (BPB * bp + j) * 16, k0);
+#pragma unroll
+          for (int i = 0; i < BNB; ++i)
+#pragma unroll
+            for (int j = 0; j < BPB; ++j) R[i][j] = Mma<T>::mma(af[i], bfr[j], R[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < BNB; ++i)
+#pragma unroll
+          for (int j = 0; j < BPB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dout[i][j][r] = R[i][j][r] + cur.decay * dout[i][j][r];
+      } else {
+#pragma unroll
+        for (int i = 0; i < BNB; ++i)
+#pragma unroll
+          for (int j = 0; j < BPB; ++j) {
+            const int pt = BPB * bp + j, nt = BNB * bn + i;
+            const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
+            f32x4_t dhoff = zero4();
+            for (int m = 0; m < cur.nseg; ++m) {
+              const int lo = s_segstart[m], hi = s_segstart[m + 1];
+              f32x4_t R = zero4();
+              for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
+                R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0),
+                                mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi), R);
+              const int rank = seg_rank(s_seg[lo]);
+              if (rank == 0) {
+                dhoff = R;
+              } else if (pb.dinit) {
+                const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  float v = R[r];
+                  if (hi == Q) v += cur.decay * dout[i][j][r];
+                  pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n + r] = v;
+                }
               }
             }
+            dout[i][j] = dhoff;
           }
-          dout[k] = dhoff;
-        }
       }
     }
     __syncthreads();
