@@ -120,22 +120,27 @@ __device__ __forceinline__ void dcb_slab_product(const Problem& pb, const DbdcBl
     }
     constexpr int KS = KSL / Mma<T>::KSTEP;
     const int l = lane_id();
+    // both owned row tiles take each column fragment from one LDS read
+    bool live[2];
+    typename Mma<T>::frag af[2][KS];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int R = own[a];
-      const bool live = lower ? (k0 <= 16 * R + 15) : (k0 + KSL > 16 * R);
-      if (!live) continue;
-      typename Mma<T>::frag af[KS];
+      live[a] = lower ? (k0 <= 16 * R + 15) : (k0 + KSL > 16 * R);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        af[ks] = Mma<T>::load_k(s_a + (16 * R + (l & 15)) * Cf::LDA + (l >> 4) * Mma<T>::KW + ks * Mma<T>::KSTEP);
+        af[a][ks] = Mma<T>::load_k(s_a + (16 * R + (l & 15)) * Cf::LDA + (l >> 4) * Mma<T>::KW + ks * Mma<T>::KSTEP);
+    }
 #pragma unroll
-      for (int nt = 0; nt < NTG / 16; ++nt) {
+    for (int nt = 0; nt < NTG / 16; ++nt) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc[a][nt] = Mma<T>::mma(af[ks], load_kn<T>(s_k + 16 * nt, Cf::LDK, ks * Mma<T>::KSTEP), acc[a][nt]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const typename Mma<T>::frag bf = load_kn<T>(s_k + 16 * nt, Cf::LDK, ks * Mma<T>::KSTEP);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          if (live[a]) acc[a][nt] = Mma<T>::mma(af[a][ks], bf, acc[a][nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -297,36 +302,45 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
         __syncthreads();
       }
       if (!esrc.p) continue;
+      // both owned row tiles take each E fragment from one LDS read
+      bool live[2];
+      typename Mma<T>::frag af[2][KP];   // dy rows of tile I over p
+      f32x4_t sv[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int I = own[a];
-        if (16 * I + 15 < lo || 16 * I >= hi) continue;
-        typename Mma<T>::frag af[KP];   // dy rows of tile I over p
+        live[a] = !(16 * I + 15 < lo || 16 * I >= hi);
 #pragma unroll
         for (int ks = 0; ks < KP; ++ks)
-          af[ks] = Mma<T>::load_k(s_rows + (16 * I + r16) * LDP + kg * Mma<T>::KW + ks * Mma<T>::KSTEP);
-        f32x4_t sv;
+          af[a][ks] = Mma<T>::load_k(s_rows + (16 * I + r16) * LDP + kg * Mma<T>::KW + ks * Mma<T>::KSTEP);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * I + 4 * kg + r;
-          sv[r] = (i >= lo && i < hi) ? s_v[i] : 0.f;
+          sv[a][r] = (i >= lo && i < hi) ? s_v[i] : 0.f;
         }
+      }
 #pragma unroll
-        for (int nt = 0; nt < NCT; ++nt) {
+      for (int nt = 0; nt < NCT; ++nt) {
+        typename Mma<T>::frag ef[KP];
+#pragma unroll
+        for (int ks = 0; ks < KP; ++ks) ef[ks] = load_kn<T>(s_e + 16 * nt, LDE, ks * Mma<T>::KSTEP);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          if (!live[a]) continue;
+          const int I = own[a];
           f32x4_t y = zero4();
 #pragma unroll
-          for (int ks = 0; ks < KP; ++ks)
-            y = Mma<T>::mma(af[ks], load_kn<T>(s_e + 16 * nt, LDE, ks * Mma<T>::KSTEP), y);
+          for (int ks = 0; ks < KP; ++ks) y = Mma<T>::mma(af[a][ks], ef[ks], y);
           // C[i][n] in the accumulator layout
           const typename Mma<T>::rfrag cf = Mma<T>::rfrag_load_kn(s_c + 16 * I * LDK + 16 * nt, LDK);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float yv = y[r] * sv[r];
+            const float yv = y[r] * sv[a][r];
             acc[a][nt][r] += yv;
             offp[a][r] += yv * Elem<T>::to_f(static_cast<T>(cf[r]));
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const int64_t offd_base = (bhc * pb.ntg + k.ntile) * Q;
@@ -414,25 +428,34 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
     if (tid < Q) s_v[tid] = (tid >= k.lolast) ? Elem<T>::exp(acs_end_n - acs_n) * dt_n : 0.f;
     __syncthreads();
     if (PF && hh + 1 < pb.hpg) load_head(hh + 1);
+    // both owned column tiles take each dS fragment from one LDS read
+    bool live[2];
+    typename Mma<T>::frag af[2][KP];   // x rows of tile J over p
+    f32x4_t wv[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int J = own[a];
-      if (16 * J + 15 < k.lolast) continue;
-      typename Mma<T>::frag af[KP];   // x rows of tile J over p
+      live[a] = 16 * J + 15 >= k.lolast;
 #pragma unroll
       for (int ks = 0; ks < KP; ++ks)
-        af[ks] = Mma<T>::load_k(s_rows + (16 * J + r16) * LDP + kg * Mma<T>::KW + ks * Mma<T>::KSTEP);
-      const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(s_v + 16 * J + 4 * kg);
+        af[a][ks] = Mma<T>::load_k(s_rows + (16 * J + r16) * LDP + kg * Mma<T>::KW + ks * Mma<T>::KSTEP);
+      wv[a] = *reinterpret_cast<const f32x4_t*>(s_v + 16 * J + 4 * kg);
+    }
 #pragma unroll
-      for (int nt = 0; nt < NCT; ++nt) {
+    for (int nt = 0; nt < NCT; ++nt) {
+      typename Mma<T>::frag ef[KP];
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) ef[ks] = load_kn<T>(s_e + 16 * nt, LDE, ks * Mma<T>::KSTEP);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        if (!live[a]) continue;
         f32x4_t u = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KP; ++ks)
-          u = Mma<T>::mma(af[ks], load_kn<T>(s_e + 16 * nt, LDE, ks * Mma<T>::KSTEP), u);
+        for (int ks = 0; ks < KP; ++ks) u = Mma<T>::mma(af[a][ks], ef[ks], u);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[a][nt][r] += wv[r] * u[r];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 0; r < 4; ++r) acc[a][nt][r] += wv[a][r] * u[r];
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   write_rows<T, Q, NTG>(pb, k, pb.dB, acc, own);
