@@ -62,7 +62,9 @@ struct HeadCfg {
   static constexpr size_t RV_FLOATS = size_t(12) * Q + ((W + 8 + 3) & ~3) + size_t(W + 1) * P;
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
-  static constexpr size_t LDS = OFF_RV + RV_FLOATS * 4;
+  // two sets of vectors, taken by consecutive items of a block in turn
+  static constexpr size_t RV_BYTES = (RV_FLOATS * 4 + 15) / 16 * 16;
+  static constexpr size_t LDS = OFF_RV + 2 * RV_BYTES;
 };
 
 // Phase B over the wave's causal tiles (see the top of the file): G, M,
@@ -420,7 +422,7 @@ __device__ __forceinline__ void load_item_rows(const Problem& pb, int64_t lb,
 template <typename T, int Q, int P>
 __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* smem,
                                           RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_x,
-                                          RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy, int64_t lb_next) {
+                                          RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy, int64_t lb_next, int par) {
   using Cf = HeadCfg<T, Q, P>;
   constexpr int T16 = Cf::T16, W = Cf::W, NTHR = Cf::NTHR, PT = Cf::PT, VEC = Cf::VEC;
   constexpr int LDP = Cf::LDP, LDSN = Cf::LDSN;
@@ -430,7 +432,7 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   T* s_dyk = s_xk + Q * LDP;
   T* s_dsk = s_dyk + Q * LDP;   // dS rows [p][n] in the I/O dtype
   float* s_share = reinterpret_cast<float*>(smem + Cf::OFF_RS);
-  float* s_acs = reinterpret_cast<float*>(smem + Cf::OFF_RV);
+  float* s_acs = reinterpret_cast<float*>(smem + Cf::OFF_RV + par * Cf::RV_BYTES);
   float* s_dt = s_acs + Q;
   float* s_w = s_dt + Q;
   float* s_ee = s_w + Q;
@@ -454,22 +456,26 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   const T* Bg = static_cast<const T*>(pb.Bm);
   const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
 
-  // per-position metadata (thread tid owns position tid), loaded first so
-  // that the bulk loads below do not delay it
+  // per-position metadata, loaded first so that the bulk loads below do not
+  // delay it.  The second half of the threads owns the positions (thread tid
+  // position tid - Q): wave 0, which may still be finishing the previous
+  // item's phase D, then has only its rows to store before phase B.
+  static_assert(NTHR == 2 * Q, "a thread per position in each half of the block");
+  const int pos = tid - Q;
   float acs_i = 0.f, dt_i = 0.f, offd_i = 0.f, dfe_i = 1.f;
   int seg_i = 0;
-  if (tid < Q) {
-    acs_i = pb.acs[bhc * Q + tid];
-    dt_i = pb.dtc[bhc * Q + tid];
-    if (pb.fe) dfe_i = pb.dfe[bhc * Q + tid];
-    seg_i = pb.segpos[bc * Q + tid];
-    for (int nt = 0; nt < pb.ntg; ++nt) offd_i += pb.offd[(bhc * pb.ntg + nt) * Q + tid];
+  if (pos >= 0) {
+    acs_i = pb.acs[bhc * Q + pos];
+    dt_i = pb.dtc[bhc * Q + pos];
+    if (pb.fe) dfe_i = pb.dfe[bhc * Q + pos];
+    seg_i = pb.segpos[bc * Q + pos];
+    for (int nt = 0; nt < pb.ntg; ++nt) offd_i += pb.offd[(bhc * pb.ntg + nt) * Q + pos];
   }
   const float acs_end = pb.acs[bhc * Q + Q - 1];
   const int lolast = seg_lo(pb.segpos[bc * Q + Q - 1]);
   const float Dh = pb.D && !pb.d_hp ? pb.D[h] : 0.f;
   float Dp = Dh;
-  if (pb.d_hp && pb.D && tid < P) Dp = pb.D[h * P + tid];
+  if (pb.d_hp && pb.D && pos >= 0 && pos < P) Dp = pb.D[h * P + pos];
   const float Ah = pb.A[h];
   float endd = 0.f;   // the chunk-end term's dstate-tile partials, in tile order (used by wave 0)
   if (tid < WAVE)
@@ -491,19 +497,17 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   // er_i = exp(Acs_i - Acs_{16I}) tabled once per block.
   const bool uniform = __builtin_amdgcn_readfirstlane(lolast) == 0;
   const float acs_tile0 = __shfl(acs_i, l & ~15, WAVE);
-  if (tid < Q) {
-    s_acs[tid] = acs_i;
-    s_dt[tid] = dt_i;
-    s_seg[tid] = seg_i;
-    s_ddacs[tid] = offd_i;
-    const float e = (tid >= lolast) ? Elem<T>::exp(acs_end - acs_i) : 0.f;
-    s_ee[tid] = e;
-    s_w[tid] = e * dt_i;
-    s_er[tid] = uniform ? Elem<T>::exp(acs_i - acs_tile0) : 0.f;
-    s_dfe[tid] = dfe_i;
-  }
-  if (tid < P) {
-    s_Dp[tid] = Dp;
+  if (pos >= 0) {
+    s_acs[pos] = acs_i;
+    s_dt[pos] = dt_i;
+    s_seg[pos] = seg_i;
+    s_ddacs[pos] = offd_i;
+    const float e = (pos >= lolast) ? Elem<T>::exp(acs_end - acs_i) : 0.f;
+    s_ee[pos] = e;
+    s_w[pos] = e * dt_i;
+    s_er[pos] = uniform ? Elem<T>::exp(acs_i - acs_tile0) : 0.f;
+    s_dfe[pos] = dfe_i;
+    if (pos < P) s_Dp[pos] = Dp;
   }
 
   // ---- phase B: x, dy rows; decays; M; ddt_intra; da shares; dx_intra
@@ -644,8 +648,8 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
     for (int k = 0; k < W; ++k) dd += s_redp[k * P + tid];
     pb.slot_dDp[(bc * pb.H + h) * P + tid] = dd;
   }
-  if (tid < Q) {
-    const int k = tid, K = k / 16;
+  if (pos >= 0) {   // (the second half, as in phase A: wave 0 forms the tail meanwhile)
+    const int k = pos, K = k / 16;
     float da = 0.f;
 #pragma unroll
     for (int J = 0; J < T16; ++J) {
@@ -758,12 +762,17 @@ __global__ __launch_bounds__((HeadCfg<T, Q, P>::NTHR)) void k_head_bwd(Problem p
   const int64_t begin = xcd * q + (xcd < r ? xcd : r), count = q + (xcd < r ? 1 : 0);
   RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR> st_x, st_dy;
   if (slot < count) load_item_rows<T, Q, P>(pb, begin + slot, st_x, st_dy);
-  for (int64_t k = slot; k < count; k += nb_x) {
-    __syncthreads();   // the previous item's LDS reads are done
+  // No barrier between items: an item's phase A writes its x and dy rows,
+  // which the previous item last read before its phase-C barrier, and its own
+  // set of vectors (the two sets alternate), which the previous item's phase
+  // D may still be reading in wave 0; so the other waves start the item while
+  // wave 0 finishes the previous one's scan.
+  int par = 0;
+  for (int64_t k = slot; k < count; k += nb_x, par ^= 1) {
     // (after the last item the rows requested are its own again: unused, but
     // keeps the request unconditional)
     const int64_t next = k + nb_x < count ? begin + k + nb_x : begin + k;
-    head_item<T, Q, P>(pb, begin + k, smem, st_x, st_dy, next);
+    head_item<T, Q, P>(pb, begin + k, smem, st_x, st_dy, next, par);
   }
 }
 
