@@ -57,9 +57,9 @@ struct HeadCfg {
   static constexpr size_t RA = (size_t(2) * Q * LDP + size_t(P) * LDSN) * sizeof(T);  // x, dy, dS rows
   // da shares: [column tile J][position]
   static constexpr size_t RS_FLOATS = size_t(T16) * Q;
-  // vectors: acs dt w ee ddacs ddtp sj dd daint er dfe (11 Q floats) + seg (Q ints) + red (W + 8)
+  // vectors: acs dt w ee ddacs ddtp sj daint er dfe (10 Q floats) + seg (Q ints) + red (W + 8)
   // + per-channel dD partials (W x P) + the head's D per channel (P)
-  static constexpr size_t RV_FLOATS = size_t(12) * Q + ((W + 8 + 3) & ~3) + size_t(W + 1) * P;
+  static constexpr size_t RV_FLOATS = size_t(11) * Q + ((W + 8 + 3) & ~3) + size_t(W + 1) * P;
   static constexpr size_t OFF_RS = (RA + 15) / 16 * 16;
   static constexpr size_t OFF_RV = OFF_RS + RS_FLOATS * 4;
   // two sets of vectors, taken by consecutive items of a block in turn
@@ -439,8 +439,7 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
   float* s_ddacs = s_ee + Q;
   float* s_ddtp = s_ddacs + Q;
   float* s_sj = s_ddtp + Q;
-  float* s_dd = s_sj + Q;
-  float* s_daint = s_dd + Q;
+  float* s_daint = s_sj + Q;
   float* s_er = s_daint + Q;
   float* s_dfe = s_er + Q;
   int* s_seg = reinterpret_cast<int*>(s_dfe + Q);
@@ -581,6 +580,26 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
       if (nb > 0) __syncthreads();   // the previous round's dS rows are read
       b2.store_ds(nb, s_dsk);
       __syncthreads();
+      if (nb == 0) {
+        // every wave's phase B is done: the intra-chunk da of each position
+        // (the second half of the block, as in phase A) and, per channel, the
+        // dD slot of this (b, c, h), waves in order
+        if (pos >= 0) {
+          const int k = pos, K = k / 16;
+          float da = 0.f;
+#pragma unroll
+          for (int J = 0; J < T16; ++J) {
+            const float v = s_share[J * Q + k];
+            da += (J <= K) ? v : 0.f;
+          }
+          s_daint[k] = da;
+        }
+        if (pb.d_hp && tid < P) {
+          float dd = 0.f;
+          for (int k = 0; k < W; ++k) dd += s_redp[k * P + tid];
+          pb.slot_dDp[(bc * pb.H + h) * P + tid] = dd;
+        }
+      }
       const int ncols = b2.cols(nb);
       if constexpr (KW == 8) {
 #pragma unroll
@@ -642,34 +661,18 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
 
   load_item_rows<T, Q, P>(pb, lb_next, st_x, st_dy);
 
-  // ---- phase D: da and its consumers
-  if (pb.d_hp && tid < P) {   // per-channel dD slot of this (b, c, h), waves in order
-    float dd = 0.f;
-    for (int k = 0; k < W; ++k) dd += s_redp[k * P + tid];
-    pb.slot_dDp[(bc * pb.H + h) * P + tid] = dd;
-  }
-  if (pos >= 0) {   // (the second half, as in phase A: wave 0 forms the tail meanwhile)
-    const int k = pos, K = k / 16;
-    float da = 0.f;
+  // ---- phase D: da and its consumers, in wave 0 alone (the intra-chunk da
+  // was formed during phase B2; the other waves go on to the next item)
+  if (w == 0) {
+    float tail;   // chunk-end terms of ddAcs at position Q-1
+    {
+      float v = 0.f;
 #pragma unroll
-    for (int J = 0; J < T16; ++J) {
-      const float v = s_share[J * Q + k];
-      da += (J <= K) ? v : 0.f;
+      for (int e = 0; e < R; ++e) v += s_sj[l * R + e];
+      const float sum_s = wave_sum(v);
+      tail = sum_s + Elem<T>::exp(acs_end) * endd;
+      tail = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tail)));
     }
-    s_daint[k] = da;
-    s_dd[k] = s_ddacs[k] - s_sj[k];
-  }
-  float tail = 0.f;   // chunk-end terms of ddAcs at position Q-1 (wave 0, lane 0)
-  if (w == 0) {
-    float v = 0.f;
-#pragma unroll
-    for (int e = 0; e < R; ++e) v += s_sj[l * R + e];
-    const float sum_s = wave_sum(v);
-    tail = sum_s + Elem<T>::exp(acs_end) * endd;
-  }
-  __syncthreads();
-  if (w == 0) {
-    tail = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, tail)));
     // reverse in-chunk, in-segment cumulative sum of ddAcs (fixed order).  The
     // lanes hold the positions in reverse order (lane l: positions from
     // (63 - l) R), so the sum over later positions is a prefix over lanes.
@@ -679,7 +682,7 @@ __device__ __forceinline__ void head_item(const Problem& pb, int64_t lb, char* s
 #pragma unroll
     for (int e = 0; e < R; ++e) {
       const int i = lp + e;
-      v[e] = s_dd[i];
+      v[e] = s_ddacs[i] - s_sj[i];
       if (i == Q - 1) v[e] += tail;
       f[e] = (i == Q - 1) || (seg_lo(s_seg[i + 1]) == i + 1);
     }
