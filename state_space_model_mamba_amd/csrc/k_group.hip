@@ -9,6 +9,10 @@
 //   CB  = C B^T over the causal tiles (head independent; fp32, for the head kernel)
 //   dCB = sum_h W_h o (dy_h x_h^T),  W_h[i,j] = exp(Acs_i - Acs_j) dt_j  (j <= i, same segment)
 //   written as a Q x Q tile and as its transpose (zeros above the diagonal).
+// On a grid too small for the GPU the group's heads are cut into nslice
+// slices of consecutive heads, one block each: every block sums its slice in
+// ascending head order into fp32 tiles parked in a workspace slot, and
+// k_dcb_out adds the slots in slice order and writes the two tiles.
 #include "ssd_problem.h"
 #include "ssd_tiles.h"
 
@@ -169,6 +173,56 @@ __device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, con
   }
 }
 
+// dCB of one (batch, group, chunk) (the wave's causal tiles, fp32) -> dcb
+// (row-major) and dcbt (its transpose), in full (zeros above the diagonal),
+// RB rows at a time through the block's LDS (the x / dy rows' region): the
+// block is cleared, each wave writes its tiles into it, and the rows leave
+// with 16-byte stores.  Starts with a barrier (the LDS may still be in use).
+template <typename T, int Q, int P>
+__device__ __forceinline__ void dcb_write(const Problem& pb, int64_t bgc, const f32x4_t (&dcb)[DcbCfg<T, Q, P>::NOWN],
+                                          char* smem) {
+  using Cf = DcbCfg<T, Q, P>;
+  constexpr int NTHR = Cf::NTHR, VEC = Cf::VEC;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  T* s_xk = reinterpret_cast<T*>(smem);
+  constexpr int RB = Cf::RB, LDR = Cf::LDR, CPR = Q / VEC;   // 16-byte chunks per row
+  T* s_out = s_xk;
+  T* dcb_out = static_cast<T*>(pb.dcb) + bgc * Q * Q;
+  T* dcbt_out = static_cast<T*>(pb.dcbt) + bgc * Q * Q;
+#pragma unroll 1
+  for (int pass = 0; pass < 2 * (Q / RB); ++pass) {
+    const bool trans = pass >= Q / RB;
+    const int r0 = (trans ? pass - Q / RB : pass) * RB;   // first output row of the pass
+    __syncthreads();   // the x / dy rows (first pass) or the previous pass's rows are read
+    for (int v = tid; v < RB * CPR; v += NTHR)
+      *reinterpret_cast<uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC) = zero_u4();
+    __syncthreads();
+#pragma clang loop unroll(full)
+    for (int k = 0; k < Cf::NOWN; ++k) {
+      int I, J;
+      bool second;
+      Cf::Split::tile(w, k, I, J, second);
+      if (!trans && 16 * I >= r0 && 16 * I < r0 + RB) {
+        // rows 16 I + 4 kg + r of dCB, column 16 J + r16
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_out[(16 * I + 4 * kg + r - r0) * LDR + 16 * J + r16] = Elem<T>::from_f(dcb[k][r]);
+      }
+      if (trans && 16 * J >= r0 && 16 * J < r0 + RB) {
+        // row 16 J + r16 of dCB^T, columns 16 I + 4 kg .. + 3
+        T* dst = s_out + (16 * J + r16 - r0) * LDR + 16 * I + 4 * kg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[r] = Elem<T>::from_f(dcb[k][r]);
+      }
+    }
+    __syncthreads();
+    T* gout = (trans ? dcbt_out : dcb_out) + static_cast<int64_t>(r0) * Q;
+    for (int v = tid; v < RB * CPR; v += NTHR)
+      *reinterpret_cast<uint4*>(gout + static_cast<int64_t>(v / CPR) * Q + (v % CPR) * VEC) =
+          *reinterpret_cast<const uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC);
+  }
+}
+
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   using Cf = DcbCfg<T, Q, P>;
@@ -181,23 +235,31 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   float* s_er = s_dt + Q;
   int* s_lo = reinterpret_cast<int*>(s_er + Q);
 
-  const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
-  const int64_t lb = xcd_logical_block(blockIdx.x, total);
+  // logical blocks: the slices of one (batch, group, chunk) are consecutive
+  const int S = pb.nslice;
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc * S;
+  const int64_t lbs = xcd_logical_block(blockIdx.x, total);
+  const int sl = static_cast<int>(lbs % S);
+  const int64_t lb = lbs / S;
   const int c = static_cast<int>(lb % pb.nc);
   const int64_t bg = lb / pb.nc;
   const int g = static_cast<int>(bg % pb.G), b = static_cast<int>(bg / pb.G);
-  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id();
   const int64_t bc = static_cast<int64_t>(b) * pb.nc + c;
   const T* xg = static_cast<const T*>(pb.x);
   const T* dyg = static_cast<const T*>(pb.dy);
+  // this block's heads of the group: [hh_lo, hh_hi) (empty for a trailing slice)
+  const int hps = (pb.hpg + S - 1) / S;
+  const int hh_lo = sl * hps, hh_hi = min(pb.hpg, hh_lo + hps);
 
   const int64_t bgc = (static_cast<int64_t>(b) * pb.G + g) * pb.nc + c;
   for (int i = tid; i < Q; i += NTHR) s_lo[i] = seg_lo(pb.segpos[bc * Q + i]);
 
   // ---- CB = C B^T over the owned causal tiles.  It is the same for every
-  // head of the group, so it is formed once here and stored for the head
-  // kernel in fp32, in that kernel's (wave, tile) order and lane layout.
-  {
+  // head of the group, so it is formed once here (by the first slice) and
+  // stored for the head kernel in fp32, in that kernel's (wave, tile) order
+  // and lane layout.
+  if (sl == 0) {   // (uniform)
     constexpr int NS = Cf::NS, NSL = Cf::NSL, LDN = Cf::LDN;
     T* s_ck = s_xk;   // the x / dy rows are not staged yet
     T* s_bk = s_ck + Q * LDN;
@@ -282,9 +344,9 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   // both factors <= 1.
   const bool uniform = __builtin_amdgcn_readfirstlane(seg_lo(pb.segpos[bc * Q + Q - 1])) == 0;
   __syncthreads();   // (keeps the first head's loads out of the CB phase's registers)
-  load_head(0);
+  if (hh_lo < hh_hi) load_head(hh_lo);
 
-  for (int hh = 0; hh < pb.hpg; ++hh) {
+  for (int hh = hh_lo; hh < hh_hi; ++hh) {
     __syncthreads();
     st_x.store(s_xk, LDP);
     st_dy.store(s_dyk, LDP);
@@ -297,7 +359,7 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
       }
     }
     __syncthreads();
-    if (hh + 1 < pb.hpg) load_head(hh + 1);
+    if (hh + 1 < hh_hi) load_head(hh + 1);
 
     const int z = opaque_zero();
     const int wz = w + z;
@@ -313,55 +375,52 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
       dcb_tiles<T, Q, P, false, Cf::NOWN>(dcb, xk, dyk, acs, dtv, erv, lov, wz);
   }
 
-  // write dCB (row-major) and dCB^T in full (zeros above the diagonal), RB
-  // rows at a time through the LDS that held the x / dy rows: the block is
-  // cleared, each wave writes its tiles into it, and the rows leave with
-  // 16-byte stores
-  constexpr int RB = Cf::RB, LDR = Cf::LDR, CPR = Q / VEC;   // 16-byte chunks per row
-  T* s_out = s_xk;
-  T* dcb_out = static_cast<T*>(pb.dcb) + bgc * Q * Q;
-  T* dcbt_out = static_cast<T*>(pb.dcbt) + bgc * Q * Q;
-#pragma unroll 1
-  for (int pass = 0; pass < 2 * (Q / RB); ++pass) {
-    const bool trans = pass >= Q / RB;
-    const int r0 = (trans ? pass - Q / RB : pass) * RB;   // first output row of the pass
-    __syncthreads();   // the x / dy rows (first pass) or the previous pass's rows are read
-    for (int v = tid; v < RB * CPR; v += NTHR)
-      *reinterpret_cast<uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC) = zero_u4();
-    __syncthreads();
-#pragma clang loop unroll(full)
-    for (int k = 0; k < Cf::NOWN; ++k) {
-      int I, J;
-      bool second;
-      Cf::Split::tile(w, k, I, J, second);
-      if (!trans && 16 * I >= r0 && 16 * I < r0 + RB) {
-        // rows 16 I + 4 kg + r of dCB, column 16 J + r16
+  if (S == 1) {
+    dcb_write<T, Q, P>(pb, bgc, dcb, smem);
+  } else {   // this slice's sums -> its slot, in the CB tiles' (wave, tile) order and lane layout
+    float* dst = pb.dcbp + ((bgc * S + sl) * Cf::W + w) * Cf::NOWN * 256 + l * 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s_out[(16 * I + 4 * kg + r - r0) * LDR + 16 * J + r16] = Elem<T>::from_f(dcb[k][r]);
-      }
-      if (trans && 16 * J >= r0 && 16 * J < r0 + RB) {
-        // row 16 J + r16 of dCB^T, columns 16 I + 4 kg .. + 3
-        T* dst = s_out + (16 * J + r16 - r0) * LDR + 16 * I + 4 * kg;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[r] = Elem<T>::from_f(dcb[k][r]);
-      }
-    }
-    __syncthreads();
-    T* gout = (trans ? dcbt_out : dcb_out) + static_cast<int64_t>(r0) * Q;
-    for (int v = tid; v < RB * CPR; v += NTHR)
-      *reinterpret_cast<uint4*>(gout + static_cast<int64_t>(v / CPR) * Q + (v % CPR) * VEC) =
-          *reinterpret_cast<const uint4*>(s_out + (v / CPR) * LDR + (v % CPR) * VEC);
+    for (int k = 0; k < Cf::NOWN; ++k) *reinterpret_cast<f32x4_t*>(dst + k * 256) = dcb[k];
   }
+}
+
+// The slices' dCB tiles of one (batch, group, chunk), added in slice order,
+// -> dcb and dcbt (the grid: one block per (batch, group, chunk)).
+template <typename T, int Q, int P>
+__global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb_out(Problem pb) {
+  using Cf = DcbCfg<T, Q, P>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
+  const int64_t bgc = xcd_logical_block(blockIdx.x, total);   // (batch, group, chunk), row-major
+  const int S = pb.nslice, w = wave_id_s(), l = lane_id();
+  f32x4_t dcb[Cf::NOWN];
+  const float* src = pb.dcbp + (bgc * S * Cf::W + w) * Cf::NOWN * 256 + l * 4;
+#pragma unroll
+  for (int k = 0; k < Cf::NOWN; ++k) dcb[k] = *reinterpret_cast<const f32x4_t*>(src + k * 256);
+  for (int s = 1; s < S; ++s) {
+    const float* q = src + static_cast<int64_t>(s) * Cf::W * Cf::NOWN * 256;
+#pragma unroll
+    for (int k = 0; k < Cf::NOWN; ++k) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(q + k * 256);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dcb[k][r] += v[r];
+    }
+  }
+  dcb_write<T, Q, P>(pb, bgc, dcb, smem);
 }
 
 template <typename T, int Q, int P>
 static hipError_t launch_dcb_t(const Problem& pb, hipStream_t s) {
   using C1 = DcbCfg<T, Q, P>;
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dcb<T, Q, P>), C1::LDS);
+  if (e == hipSuccess && pb.nslice > 1)
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dcb_out<T, Q, P>), C1::LDS);
   if (e != hipSuccess) return e;
   const int64_t b1 = static_cast<int64_t>(pb.B) * pb.G * pb.nc;
-  hipLaunchKernelGGL((k_dcb<T, Q, P>), dim3(static_cast<unsigned>(b1)), dim3(C1::NTHR), C1::LDS, s, pb);
+  hipLaunchKernelGGL((k_dcb<T, Q, P>), dim3(static_cast<unsigned>(b1 * pb.nslice)), dim3(C1::NTHR), C1::LDS, s, pb);
+  e = hipGetLastError();
+  if (e != hipSuccess || pb.nslice == 1) return e;
+  hipLaunchKernelGGL((k_dcb_out<T, Q, P>), dim3(static_cast<unsigned>(b1)), dim3(C1::NTHR), C1::LDS, s, pb);
   return hipGetLastError();
 }
 

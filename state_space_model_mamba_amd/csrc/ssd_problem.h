@@ -68,6 +68,8 @@ struct Problem {
   void* dstate;      // (B, H, nc, P, N), I/O dtype
   void* dcb;         // (B, G, nc, Q, Q) io dtype: head-summed intra-chunk dCB (split group path)
   void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose (split group path)
+  int nslice;        // head slices of the split group path's dCB kernel (1: one block per (b, g, c))
+  float* dcbp;       // (B, G, nc, nslice, causal tiles, 256) fp32: the slices' dCB sums (nslice > 1)
   float* cbt;        // (B, G, nc, Q(Q+16)/512 tiles, 256): C B^T causal tiles, fp32, in the
                      // causal split's (wave, tile) order and accumulator lane layout
   float* offd;       // (B, H, nc, ntg, Q)

@@ -174,3 +174,21 @@ def test_group_path_hook_checks_its_argument_and_sizes_the_workspace():
         assert sizes[0] == sizes[1] < sizes[2]   # the split path holds dCB and its transpose
     finally:
         lib.ssd_set_group_path(0)
+
+
+def test_many_heads_per_group_take_the_split_path_with_head_slices():
+    # 64 blocks of (batch, group, chunk), but 64 heads in the one group: the split
+    # path by shape, its dCB kernel cut into 4 head slices (256 blocks) whose fp32
+    # sums take a workspace region of their own
+    lib = ssd.load_library()
+    sh = shape(seqlen=16384, nheads=64, ngroups=1, dstate=256, nseqs=7)
+    try:
+        sizes = {}
+        for path in (0, 1, 2):
+            assert lib.ssd_set_group_path(path) == 0
+            sizes[path] = ssd.workspace_size(sh)
+        assert sizes[0] == sizes[2] > sizes[1]
+        nc, tiles = 64, 256 * (256 + 16) // 2
+        assert sizes[2] - sizes[1] >= 4 * nc * tiles * 4 + 2 * nc * 256 * 256 * 2   # slices' sums, dCB and dCB^T
+    finally:
+        lib.ssd_set_group_path(0)
