@@ -14,6 +14,10 @@
 // the previous chunk's sequence, the sequence's initial state otherwise.
 // offd and endd are the off-diagonal and chunk-end ddA_cumsum terms; they go
 // to slots owned by (batch, head, chunk, tile), summed later in tile order.
+// On a grid too small for the GPU the group's heads are cut into nslice_bd
+// slices of consecutive heads, one block each (the first also takes the dCB
+// product): each block parks its fp32 rows in a workspace slot and k_bd_out
+// adds the slots in slice order.
 //
 // Every operand whose contraction index is its row index (B, C, E, dS) is
 // staged row-major with 16-byte (or 8-byte) stores and read as MFMA
@@ -54,6 +58,7 @@ struct DbdcCfg {
 // Block coordinates and the chunk's segment list, shared by both kernels.
 struct DbdcBlock {
   int b, g, c, ntile, n0;
+  int sl, hh_lo, hh_hi;   // head slice and its heads of the group, [hh_lo, hh_hi)
   int64_t bc, bgc;
   int nstart, seqbase, start0, nseg, lolast;
 };
@@ -62,8 +67,14 @@ template <int Q, int NTHR>
 __device__ __forceinline__ DbdcBlock dbdc_block(const Problem& pb, int* s_seg, int* s_segstart) {
   DbdcBlock k;
   const int tid = threadIdx.x;
-  const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg;
-  const int64_t lb = xcd_logical_block(blockIdx.x, total);
+  const int S = pb.nslice_bd;
+  const int64_t total = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg * S;
+  const int64_t lbs = xcd_logical_block(blockIdx.x, total);   // the slices of one tile are consecutive
+  k.sl = static_cast<int>(lbs % S);
+  const int64_t lb = lbs / S;
+  const int hps = (pb.hpg + S - 1) / S;
+  k.hh_lo = k.sl * hps;
+  k.hh_hi = min(pb.hpg, k.hh_lo + hps);
   k.ntile = static_cast<int>(lb % pb.ntg);
   int64_t rest = lb / pb.ntg;
   k.c = static_cast<int>(rest % pb.nc);
@@ -145,10 +156,22 @@ __device__ __forceinline__ void dcb_slab_product(const Problem& pb, const DbdcBl
   }
 }
 
+// The block's rows: to dC / dB (out) when it has all of the group's heads,
+// else as fp32 to its slice's slot (part: [(b, g, c, tile)][slice][Q][NTG]).
 template <typename T, int Q, int NTG>
-__device__ __forceinline__ void write_rows(const Problem& pb, const DbdcBlock& k, void* out,
+__device__ __forceinline__ void write_rows(const Problem& pb, const DbdcBlock& k, void* out, float* part,
                                            const f32x4_t (&acc)[2][NTG / 16], const int (&own)[2]) {
   const int l = lane_id(), r16 = l & 15, kg = l >> 4;
+  if (pb.nslice_bd > 1) {   // (uniform)
+    float* dst = part + ((k.bgc * pb.ntg + k.ntile) * pb.nslice_bd + k.sl) * Q * NTG;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nt = 0; nt < NTG / 16; ++nt) dst[(16 * own[a] + 4 * kg + r) * NTG + 16 * nt + r16] = acc[a][nt][r];
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -195,8 +218,9 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt) acc[a][nt] = zero4();
-  dcb_slab_product<T, Q, P, NTG>(pb, k, acc, own, static_cast<const T*>(pb.dcb) + k.bgc * Q * Q, Bg, true, s_a,
-                                 s_k);
+  if (k.sl == 0)   // (uniform) the dCB part, once per tile
+    dcb_slab_product<T, Q, P, NTG>(pb, k, acc, own, static_cast<const T*>(pb.dcb) + k.bgc * Q * Q, Bg, true, s_a,
+                                   s_k);
 
   // the chunk's C rows (this tile), for the offd row dots (visible to all
   // waves after the first barrier of the head loop)
@@ -259,9 +283,9 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   // single-segment chunk (the segment loop below reuses the same registers)
   constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + 2 * RowStage<T, P, NTG, NTHR>::IT <= 16;
   const bool pf = PF && single;
-  if (pf) load_head(0);
+  if (pf && k.hh_lo < k.hh_hi) load_head(k.hh_lo);
 
-  for (int hh = 0; hh < pb.hpg; ++hh) {
+  for (int hh = k.hh_lo; hh < k.hh_hi; ++hh) {
     const int h = k.g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(k.b) * pb.H + h) * pb.nc + k.c;
     float endp = 0.f;
@@ -277,7 +301,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     }
     if (tid < Q) s_v[tid] = Elem<T>::exp(acs_n);
     __syncthreads();
-    if (pf && hh + 1 < pb.hpg) load_head(hh + 1);
+    if (pf && hh + 1 < k.hh_hi) load_head(hh + 1);
 
     float offp[2][4];
 #pragma unroll
@@ -360,7 +384,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
       pb.endd[bhc * pb.ntg + k.ntile] = s;
     }
   }
-  write_rows<T, Q, NTG>(pb, k, pb.dC, acc, own);
+  write_rows<T, Q, NTG>(pb, k, pb.dC, pb.dcp, acc, own);
 }
 
 // ----------------------------------------------------------------------------
@@ -394,8 +418,9 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt) acc[a][nt] = zero4();
-  dcb_slab_product<T, Q, P, NTG>(pb, k, acc, own, static_cast<const T*>(pb.dcbt) + k.bgc * Q * Q, Cg, false, s_a,
-                                 s_k);
+  if (k.sl == 0)   // (uniform) the dCB part, once per tile
+    dcb_slab_product<T, Q, P, NTG>(pb, k, acc, own, static_cast<const T*>(pb.dcbt) + k.bgc * Q * Q, Cg, false, s_a,
+                                   s_k);
 
   // next head's rows: x, dS, and this thread's Acs / dt
   RowStage<T, Q, P, NTHR> st_x;
@@ -418,16 +443,16 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
   };
   constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + RowStage<T, P, NTG, NTHR>::IT <= 16;
   __syncthreads();   // the slab phase is done with the LDS the head phase reuses
-  if (PF) load_head(0);
+  if (PF && k.hh_lo < k.hh_hi) load_head(k.hh_lo);
 
-  for (int hh = 0; hh < pb.hpg; ++hh) {
+  for (int hh = k.hh_lo; hh < k.hh_hi; ++hh) {
     if (!PF) load_head(hh);
     __syncthreads();
     st_x.store(s_rows, LDP);
     st_s.store(s_e, LDE);
     if (tid < Q) s_v[tid] = (tid >= k.lolast) ? Elem<T>::exp(acs_end_n - acs_n) * dt_n : 0.f;
     __syncthreads();
-    if (PF && hh + 1 < pb.hpg) load_head(hh + 1);
+    if (PF && hh + 1 < k.hh_hi) load_head(hh + 1);
     // both owned column tiles take each dS fragment from one LDS read
     bool live[2];
     typename Mma<T>::frag af[2][KP];   // x rows of tile J over p
@@ -458,7 +483,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  write_rows<T, Q, NTG>(pb, k, pb.dB, acc, own);
+  write_rows<T, Q, NTG>(pb, k, pb.dB, pb.dbp, acc, own);
 }
 
 // dstate tile width of k_dc / k_db
@@ -470,17 +495,53 @@ int group_ntile(int N, bool io_bf16) {
   return 16;
 }
 
+// dC or dB rows from the slices' slots, added in slice order: one thread per
+// 4 consecutive columns of one row of one (batch, group, chunk, tile)
+template <typename T, int Q, int NTG>
+__global__ __launch_bounds__(256) void k_bd_out(Problem pb, const float* part, void* out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int CV = NTG / 4;   // 4-column groups per row
+  const int64_t ntile_all = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg;
+  if (i >= ntile_all * Q * CV) return;
+  const int cv = static_cast<int>(i % CV);
+  const int row = static_cast<int>((i / CV) % Q);
+  const int64_t bt = i / (static_cast<int64_t>(CV) * Q);   // (b, g, c, tile)
+  const int ntile = static_cast<int>(bt % pb.ntg);
+  const int64_t bgc = bt / pb.ntg;
+  const int c = static_cast<int>(bgc % pb.nc);
+  const int64_t bg = bgc / pb.nc;
+  const int g = static_cast<int>(bg % pb.G), b = static_cast<int>(bg / pb.G);
+  const int t = c * Q + row;
+  if (t >= pb.L) return;
+  const float* src = part + bt * pb.nslice_bd * Q * NTG + row * NTG + 4 * cv;
+  f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
+  for (int s = 1; s < pb.nslice_bd; ++s) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(s) * Q * NTG);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += u[r];
+  }
+  store4f<T>(static_cast<T*>(out) + ((static_cast<int64_t>(b) * pb.L + t) * pb.G + g) * pb.N + ntile * NTG + 4 * cv, v);
+}
+
 template <typename T, int Q, int P, int NTG>
 static hipError_t launch_dbdc_t(const Problem& pb, hipStream_t s) {
   using Cf = DbdcCfg<T, Q, P, NTG>;
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG>), Cf::LDS);
   if (e == hipSuccess) e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_db<T, Q, P, NTG>), Cf::LDS_DB);
   if (e != hipSuccess) return e;
-  const int64_t blocks = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg;
+  const int64_t tiles = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg, blocks = tiles * pb.nslice_bd;
   hipLaunchKernelGGL((k_dc<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_db<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS_DB, s, pb);
+  e = hipGetLastError();
+  if (e != hipSuccess || pb.nslice_bd == 1) return e;
+  const int64_t nthr = tiles * Q * (NTG / 4);
+  const dim3 grid(static_cast<unsigned>((nthr + 255) / 256));
+  hipLaunchKernelGGL((k_bd_out<T, Q, NTG>), grid, dim3(256), 0, s, pb, static_cast<const float*>(pb.dcp), pb.dC);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bd_out<T, Q, NTG>), grid, dim3(256), 0, s, pb, static_cast<const float*>(pb.dbp), pb.dB);
   return hipGetLastError();
 }
 

@@ -56,21 +56,35 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, dcbp, cbt, offd, endd, slot_dA, slot_dD, slot_dDp,
-      slot_ddtb, seqstart, total;
-  int nc, ntg, nslice;
+  size_t segpos, cinfo, acs, dtc, dfe, hin, dstate, dcb, dcbt, dcbp, dcp, dbp, cbt, offd, endd, slot_dA, slot_dD,
+      slot_dDp, slot_ddtb, seqstart, total;
+  int nc, ntg, nslice, nslice_bd;
   bool fused;
 };
 
 bool is_bf16(const ssd_shape* s) { return s->io_dtype == SSD_IO_BF16; }
 
+// head slices of the split path's k_dc / k_db: doubled while their grid (one
+// block per (batch, group, chunk, widest dstate tile, slice)) has fewer than
+// 256 blocks and a slice keeps at least one head
+int split_slices_bd(const ssd_shape* s) {
+  const int64_t nc = (s->seqlen + s->chunk_size - 1) / s->chunk_size;
+  const int64_t hpg = s->nheads / s->ngroups;
+  const int64_t tiles = s->batch * s->ngroups * nc * (s->dstate / ssd::group_ntile(static_cast<int>(s->dstate), is_bf16(s)));
+  int S = 1;
+  while (tiles * S < 256 && 2 * S <= hpg) S *= 2;
+  return S;
+}
+
 // dstate tile of the split path's k_dc / k_db: the widest that divides N,
-// halved (down to 32 columns) while that grid has fewer than 256 blocks
+// halved (down to 32 columns) while that grid, with its head slices, has
+// fewer than 256 blocks
 int split_ntile(const ssd_shape* s) {
   const int N = static_cast<int>(s->dstate);
   int nt = ssd::group_ntile(N, is_bf16(s));
   const int64_t nc = (s->seqlen + s->chunk_size - 1) / s->chunk_size;
-  while (nt > 32 && N % (nt / 2) == 0 && s->batch * s->ngroups * nc * (N / nt) < 256) nt /= 2;
+  const int64_t S = split_slices_bd(s);
+  while (nt > 32 && N % (nt / 2) == 0 && s->batch * s->ngroups * nc * (N / nt) * S < 256) nt /= 2;
   return nt;
 }
 
@@ -89,10 +103,10 @@ int split_slices(const ssd_shape* s) {
 // least 256 blocks, one per CU of an MI355X.  Below that it runs fused
 // (k_cb, k_grp, whose 64-row slabs multiply the blocks by Q / 64) when a
 // group has at most 16 heads; with more heads per group, every fused block
-// walks them all, and the split path, with narrower dstate tiles and k_dcb's
-// heads cut into slices, is faster (measured: 7 packed sequences of 16384
-// rows, 64 heads in one group, group stage 0.58 against 0.85 ms; 2048 rows,
-// 8 groups of 16 heads, fused 0.11 against 0.13 ms).  A function of the shape
+// walks them all, and the split path, with its kernels' heads cut into
+// slices, is faster (measured: 7 packed sequences of 16384 rows, 64 heads in
+// one group, group stage 0.48 against 0.85 ms; 2048 rows, 8 groups of 16
+// heads, fused 0.11 against 0.13 ms).  A function of the shape
 // only (or the test override); the two paths add the same terms in different
 // orders, so their results agree to rounding, not bit for bit.
 bool group_fused(const ssd_shape* s) {
@@ -146,6 +160,7 @@ Layout make_layout(const ssd_shape* s) {
   L.fused = group_fused(s);
   const size_t ntg = N / (L.fused ? ssd::grp_ntile(static_cast<int>(N), is_bf16(s)) : split_ntile(s));
   L.nslice = L.fused ? 1 : split_slices(s);
+  L.nslice_bd = L.fused ? 1 : split_slices_bd(s);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -164,6 +179,9 @@ Layout make_layout(const ssd_shape* s) {
   L.dcb = take(dcb_bytes);
   L.dcbt = take(dcb_bytes);
   L.dcbp = take(L.nslice > 1 ? B * s->ngroups * nc * L.nslice * (Q * (Q + 16) / 2) * 4 : 0);
+  const size_t bd_bytes = L.nslice_bd > 1 ? B * s->ngroups * nc * L.nslice_bd * Q * N * 4 : 0;
+  L.dcp = take(bd_bytes);
+  L.dbp = take(bd_bytes);
   L.cbt = take(B * s->ngroups * nc * (Q * (Q + 16) / 2) * 4);
   L.offd = take(B * H * nc * ntg * Q * 4);
   L.endd = take(B * H * nc * ntg * 4);
@@ -250,6 +268,9 @@ void fill_problem(const ssd_shape* shape, const Layout& L, void* workspace, ssd:
   pb.dcbt = ws + L.dcbt;
   pb.nslice = L.nslice;
   pb.dcbp = reinterpret_cast<float*>(ws + L.dcbp);
+  pb.nslice_bd = L.nslice_bd;
+  pb.dcp = reinterpret_cast<float*>(ws + L.dcp);
+  pb.dbp = reinterpret_cast<float*>(ws + L.dbp);
   pb.cbt = reinterpret_cast<float*>(ws + L.cbt);
   pb.offd = reinterpret_cast<float*>(ws + L.offd);
   pb.endd = reinterpret_cast<float*>(ws + L.endd);

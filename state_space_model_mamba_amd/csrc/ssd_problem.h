@@ -70,6 +70,9 @@ struct Problem {
   void* dcbt;        // (B, G, nc, Q, Q) io dtype: its transpose (split group path)
   int nslice;        // head slices of the split group path's dCB kernel (1: one block per (b, g, c))
   float* dcbp;       // (B, G, nc, nslice, causal tiles, 256) fp32: the slices' dCB sums (nslice > 1)
+  int nslice_bd;     // head slices of the split path's dC / dB kernels (1: one block per (b, g, c, tile))
+  float* dcp;        // (B, G, nc, ntg, nslice_bd, Q, N / ntg) fp32: the slices' dC rows (nslice_bd > 1)
+  float* dbp;        // the same for dB
   float* cbt;        // (B, G, nc, Q(Q+16)/512 tiles, 256): C B^T causal tiles, fp32, in the
                      // causal split's (wave, tile) order and accumulator lane layout
   float* offd;       // (B, H, nc, ntg, Q)
