@@ -164,6 +164,11 @@ GROUP_CASES = [
     ("bf16 Q128 P32 N64", lambda: make_inputs(Workload("gp_bf16b", batch=1, seqlen=520, nheads=6, headdim=32,
                                                        ngroups=3, dstate=64, chunk=128, dtype="bf16", seed=12)),
      128, "bf16"),
+    # 5 heads in one group on a tiny grid: the split kernels' head slices
+    # (4 slices of 2, 2, 1 and no heads) with sequences starting inside chunks
+    ("f32 5 heads sliced", lambda: packed(make_inputs(small("gp_f32s", batch=1, seqlen=250, nheads=5, ngroups=1,
+                                                              headdim=16, dstate=64, chunk=64, seed=13)),
+                                          [[70, 100, 80]]), 64, "f32"),
 ]
 
 
