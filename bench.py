@@ -331,14 +331,15 @@ def measure_forward(torch, ssd, w, d, S, ws, z, steps, warmup):
             "bitwise_repeat": bitwise}
 
 
-def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup, z=None):
+def measure_frontend(torch, ssd, w, d, S, ws, steps, warmup, z=None, y_pre=None):
     """ssd_bwd with the dt front-end (the raw draws, dt_bias, softplus) on the same workload:
     the same step as the headline plus the activation and the dt_bias gradient (and, with z,
-    the output gate: a recomputation of y and the gated dy and dz first)."""
+    the output gate: the gated dy and dz first, from y recomputed, or with y_pre from the
+    forward's saved pre-gate y, as the autograd function does)."""
     def call():
         return ssd.ssd_bwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d["dy"],
                            initial_states=d.get("initial_states"), seq_idx=d.get("seq_idx"), chunk_size=w.chunk,
-                           nseqs=S, workspace=ws, dt_bias=d["dt_bias"], dt_softplus=True, z=z)
+                           nseqs=S, workspace=ws, dt_bias=d["dt_bias"], dt_softplus=True, z=z, y_pre_gate=y_pre)
     for _ in range(warmup):
         ref = call()
     torch.cuda.synchronize()
@@ -645,9 +646,15 @@ def main():
         # output gate: z ~ N(0, 1) (seeded), in the I/O dtype
         gz = torch.Generator().manual_seed(w.seed + 1)
         zg = torch.randn(tuple(d["x"].shape), generator=gz).to(d["x"].dtype).to(dev)
+        # the forward's pre-gate y (outside the timed region), as the autograd function keeps it
+        y_pre = ssd.ssd_fwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], d.get("initial_states"),
+                            d.get("seq_idx"), chunk_size=w.chunk, nseqs=S, workspace=ws, dt_bias=d["dt_bias"],
+                            dt_softplus=True, z=zg, want_y_pre_gate=True)["y_pre_gate"]
         res["backward_with_dt_frontend_and_gate"] = measure_frontend(
+            torch, ssd, w, d, S, ws, steps=leg_steps, warmup=leg_warmup, z=zg, y_pre=y_pre)
+        res["backward_with_dt_frontend_and_gate_recompute"] = measure_frontend(
             torch, ssd, w, d, S, ws, steps=leg_steps, warmup=leg_warmup, z=zg)
-        del zg
+        del zg, y_pre
     if not args.no_conv and not args.no_options:
         res["causal_conv1d"] = measure_conv1d(torch, steps=leg_steps, warmup=leg_warmup,
                                               dev=dev, cpu=not args.no_cpu_baseline)

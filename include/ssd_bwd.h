@@ -163,6 +163,12 @@ typedef struct {
    * the gradient arriving for the state after position seqlen-1 of each batch row (the final
    * state of the row's last sequence).  The loss becomes l + sum_b <d_last_states[b], h_{L-1}>. */
   const float* d_last_states;
+  /* (batch, seqlen, nheads, headdim) in the I/O dtype, or NULL; used only with an output
+   * gate z.  ssd_fwd_ex writes y before the gate there (the value it multiplies by silu(z),
+   * rounded to the I/O dtype); ssd_bwd_ex reads it back instead of recomputing y, so that its
+   * gate pass is one elementwise pass over dy, z and this array.  The results are the same
+   * bits either way.  It may alias none of the other arrays of the call. */
+  void* y_pre_gate;
 } ssd_options;
 
 /*
@@ -180,8 +186,9 @@ typedef struct {
  * `out` and writes `dz` (same shape and dtype as z; required with z):
  *   dz = dy * y * sigmoid(z) (1 + z (1 - sigmoid(z))),
  * and the gradients of everything else through dy * silu(z).  y is
- * recomputed from the inputs.  The gated dy is held, rounded to the I/O
- * dtype, in the dx buffer until dx overwrites it.
+ * recomputed from the inputs, or read from opt->y_pre_gate when the forward
+ * saved it there.  The gated dy is held, rounded to the I/O dtype, in the dx
+ * buffer until dx overwrites it.
  *
  * The gate is not on the pages either: it is the output gate of the usual
  * Mamba-2 layer, the second half of the same "next" step as the front-end.

@@ -24,6 +24,23 @@
 
 namespace ssd {
 
+// The backward's gate pass for one 16-byte piece of dout (du), z (zu) and y
+// (yu, rounded to the I/O dtype): the gated dy = dout silu(z) and
+// dz = dout y sigmoid(z) (1 + z (1 - sigmoid(z))), rounded to the I/O dtype.
+template <typename T>
+__device__ __forceinline__ void gate_grads(uint4 du, uint4 zu, uint4 yu, T* dy_out, T* dz_out) {
+  constexpr int VEC = Vec16<T>::N;
+  T dyo[VEC], dzo[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz)), dv = vget<T>(du, e);
+    dyo[e] = Elem<T>::from_f(dv * zz * sg);
+    dzo[e] = Elem<T>::from_f(dv * vget<T>(yu, e) * sg * (1.f + zz * (1.f - sg)));
+  }
+  *reinterpret_cast<uint4*>(dy_out) = *reinterpret_cast<const uint4*>(dyo);
+  *reinterpret_cast<uint4*>(dz_out) = *reinterpret_cast<const uint4*>(dzo);
+}
+
 // ----------------------------------------------------------------------------
 // k_seqstart: seqstart[s] = b L + t of sequence s's first position
 // ----------------------------------------------------------------------------
@@ -531,21 +548,43 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
             o[e] = Elem<T>::from_f(vget<T>(yu, e) * zz * sg);
           }
           *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = *reinterpret_cast<const uint4*>(o);
+          if (pb.ypre) *reinterpret_cast<uint4*>(static_cast<T*>(pb.ypre) + off) = yu;   // (uniform)
         } else {
           const uint4 du = ld_global16(static_cast<const T*>(pb.dout) + off);
-          T dyo[VEC], dzo[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz)), dv = vget<T>(du, e);
-            dyo[e] = Elem<T>::from_f(dv * zz * sg);
-            dzo[e] = Elem<T>::from_f(dv * vget<T>(yu, e) * sg * (1.f + zz * (1.f - sg)));
-          }
-          *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = *reinterpret_cast<const uint4*>(dyo);
-          *reinterpret_cast<uint4*>(static_cast<T*>(pb.dz) + off) = *reinterpret_cast<const uint4*>(dzo);
+          gate_grads<T>(du, zu, yu, static_cast<T*>(pb.y) + off, static_cast<T*>(pb.dz) + off);
         }
       }
     }
   }
+}
+
+// ----------------------------------------------------------------------------
+// k_gate_bwd: the backward's gate pass from the y the forward saved
+// ----------------------------------------------------------------------------
+// One thread per 16-byte piece of (B, L, H, P): the gated dy into dx's place
+// and dz, from dout, z and the saved y (the same arithmetic as the output
+// kernel's gate pass, so the same bits).
+template <typename T>
+__global__ __launch_bounds__(256) void k_gate_bwd(Problem pb, int64_t npiece) {
+  constexpr int VEC = Vec16<T>::N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= npiece) return;
+  const int64_t off = i * VEC;
+  const uint4 du = ld_global16(static_cast<const T*>(pb.dout) + off);
+  const uint4 zu = ld_global16(static_cast<const T*>(pb.z) + off);
+  const uint4 yu = ld_global16(static_cast<const T*>(pb.ypre) + off);
+  gate_grads<T>(du, zu, yu, static_cast<T*>(pb.y) + off, static_cast<T*>(pb.dz) + off);
+}
+
+hipError_t launch_gate_bwd(const Problem& pb, bool io_bf16, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(pb.B) * pb.L * pb.H * pb.P;
+  const int64_t npiece = n / (io_bf16 ? Vec16<bf16_t>::N : Vec16<float>::N);
+  const dim3 grid(static_cast<unsigned>((npiece + 255) / 256));
+  if (io_bf16)
+    hipLaunchKernelGGL((k_gate_bwd<bf16_t>), grid, dim3(256), 0, s, pb, npiece);
+  else
+    hipLaunchKernelGGL((k_gate_bwd<float>), grid, dim3(256), 0, s, pb, npiece);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------

@@ -313,6 +313,10 @@ int run_bwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const 
   if (ddt_bias && !(fe && fe->dt_bias)) return SSD_ERR_INVALID_ARG;
   if ((z != nullptr) != (dz != nullptr)) return SSD_ERR_INVALID_ARG;
   if (z && (z == dx || dz == dx || dz == dy)) return SSD_ERR_INVALID_ARG;   // dx holds the gated dy
+  if (const void* yp = fe ? fe->y_pre_gate : nullptr) {
+    if (!aligned16(yp)) return SSD_ERR_MISALIGNED;
+    if (yp == dx || yp == dz || yp == dy || yp == z || yp == x) return SSD_ERR_INVALID_ARG;
+  }
   for (const void* p : {static_cast<const void*>(ddt_bias), z, static_cast<const void*>(dz)})
     if (p && !aligned16(p)) return SSD_ERR_MISALIGNED;
   if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC || !workspace)
@@ -349,11 +353,14 @@ int run_bwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const 
   if (ssd::launch_prep(pb, s) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
   if (ssd::launch_state_fwd(pb, bf16, s) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
   if (z) {
-    // gate pass: recompute y, write the gated dy into dx's place and dz; the
-    // stages below read dy from there
+    // gate pass: the gated dy into dx's place and dz, with y recomputed, or
+    // read from the forward's saved copy in one elementwise pass; the stages
+    // below read dy from there
     ssd::Problem pg = pb;
     pg.z = z; pg.dout = dy; pg.dz = dz; pg.y = dx;
-    if (ssd::launch_fwd_out(pg, bf16, s) != hipSuccess) return SSD_ERR_HIP;
+    pg.ypre = fe ? fe->y_pre_gate : nullptr;
+    if ((pg.ypre ? ssd::launch_gate_bwd(pg, bf16, s) : ssd::launch_fwd_out(pg, bf16, s)) != hipSuccess)
+      return SSD_ERR_HIP;
     pb.dy = dx;
   }
   if (ssd::launch_state_bwd(pb, bf16, s) != hipSuccess || !mark(3)) return SSD_ERR_HIP;
@@ -407,6 +414,10 @@ int run_fwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const 
   if (rc) return rc;
   if (z && !aligned16(z)) return SSD_ERR_MISALIGNED;
   if (!x || !dt || !A || !B || !C || !y || !workspace) return SSD_ERR_INVALID_ARG;
+  if (const void* yp = fe ? fe->y_pre_gate : nullptr) {
+    if (!aligned16(yp)) return SSD_ERR_MISALIGNED;
+    if (yp == y || yp == z || yp == x) return SSD_ERR_INVALID_ARG;
+  }
   if (!seq_idx && (initial_states || final_states) && shape->nseqs != shape->batch) return SSD_ERR_INVALID_ARG;
   if ((initial_states || final_states) && shape->nseqs < 1) return SSD_ERR_INVALID_ARG;
   const void* ptrs[] = {x, dt, A, B, C, D, initial_states, seq_idx, y, final_states, workspace};
@@ -420,6 +431,7 @@ int run_fwd(const ssd_shape* shape, const ssd_options* fe, const void* x, const 
   pb.x = x; pb.dt = dt; pb.A = A; pb.Bm = B; pb.Cm = C; pb.D = D;
   pb.h0 = initial_states; pb.seq_idx = seq_idx;
   pb.y = y; pb.final = final_states; pb.z = z;
+  pb.ypre = z && fe ? fe->y_pre_gate : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = is_bf16(shape);
   if (ssd::launch_prep(pb, s) != hipSuccess) return SSD_ERR_HIP;

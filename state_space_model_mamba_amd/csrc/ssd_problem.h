@@ -57,6 +57,8 @@ struct Problem {
   void* dz;          // gate pass only
   // forward outputs
   void* y;           // (B, L, H, P), I/O dtype
+  void* ypre;        // (B, L, H, P), I/O dtype, nullable: y before the output gate (forward writes,
+                     // the backward's elementwise gate pass reads)
   float* final;      // (nseqs, H, P, N) fp32, nullable
   // workspace
   int32_t* segpos;   // (B, nc, Q)
@@ -131,6 +133,7 @@ hipError_t launch_reduce(const Problem& pb, hipStream_t s);
 // sequences' final states
 hipError_t launch_seqstart(const Problem& pb, hipStream_t s);
 hipError_t launch_fwd_out(const Problem& pb, bool io_bf16, hipStream_t s);
+hipError_t launch_gate_bwd(const Problem& pb, bool io_bf16, hipStream_t s);
 
 // The (chunk_size, headdim) pairs compiled for each io dtype.  bf16 needs
 // headdim % 32 == 0 (one MFMA k-step over P); fp32 stops at chunk 128 so that

@@ -38,7 +38,7 @@ class SsdShape(ctypes.Structure):
 class SsdOptions(ctypes.Structure):
     _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
                 ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float), ("d_per_channel", ctypes.c_int32),
-                ("d_last_states", ctypes.c_void_p)]
+                ("d_last_states", ctypes.c_void_p), ("y_pre_gate", ctypes.c_void_p)]
 
 
 class SsdError(RuntimeError):
@@ -137,17 +137,18 @@ def _check(t, name, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last=None):
-    """The C options struct (dt front-end, per-channel D, last-state gradient), or None when it
-    would change nothing."""
+def _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last=None, y_pre=None):
+    """The C options struct (dt front-end, per-channel D, last-state gradient, saved pre-gate
+    output), or None when it would change nothing."""
     lo, hi = float(dt_limit[0]), float(dt_limit[1])
     per_channel = D is not None and D.dim() == 2
     _check(D, "D", torch.float32, (H, P) if per_channel else (H,), dev)
     if (dt_bias is None and not dt_softplus and lo == -math.inf and hi == math.inf and not per_channel
-            and d_last is None):
+            and d_last is None and y_pre is None):
         return None
     _check(dt_bias, "dt_bias", torch.float32, (H,), dev)
-    return SsdOptions(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, 1 if per_channel else 0, _ptr(d_last))
+    return SsdOptions(_ptr(dt_bias), 1 if dt_softplus else 0, lo, hi, 1 if per_channel else 0, _ptr(d_last),
+                      _ptr(y_pre))
 
 
 def shape_of(x, B, chunk_size, nseqs) -> SsdShape:
@@ -161,7 +162,7 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
             nseqs: Optional[int] = None, want_d_initial_states: bool = True,
             workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, events=None,
             dt_bias=None, dt_softplus: bool = False, dt_limit=(-math.inf, math.inf), z=None,
-            d_last_states=None):
+            d_last_states=None, y_pre_gate=None):
     """Gradients of sum(dy * y) of the SSD layer, computed by libssd_bwd.
 
     x, dy: (b, L, H, P) and B, C: (b, L, G, N) in bf16 or fp32 (one dtype);
@@ -177,6 +178,8 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     gradient of y * silu(z) and the dict also holds dz.  ``d_last_states``
     (b, H, P, N) fp32: the gradient handed in for the state after each row's
     last position (the hand-off of a sequence split across calls).
+    ``y_pre_gate`` (like x, with z): y before the gate as ssd_fwd saved it; the
+    gate pass then reads it instead of recomputing y (same bits).
     """
     lib = load_library()
     dev = x.device
@@ -204,8 +207,12 @@ def ssd_bwd(x, dt, A, B, C, D, dy, initial_states=None, seq_idx=None, chunk_size
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
     _check(d_last_states, "d_last_states", torch.float32, (b, H, P, N), dev)
-    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last_states)
     _check(z, "z", io, (b, L, H, P), dev)
+    if y_pre_gate is not None:
+        if z is None:
+            raise ValueError("y_pre_gate goes with the gate z")
+        _check(y_pre_gate, "y_pre_gate", io, (b, L, H, P), dev)
+    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, d_last_states, y_pre_gate)
     if (fe is not None or z is not None) and events is not None:
         raise ValueError("stage events are not available with the dt front-end or the gate")
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
@@ -285,14 +292,15 @@ def ssd_bwd_noalloc(x, dt, A, B, C, D, dy, out: dict, initial_states=None, seq_i
 def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_size: int = 256,
             nseqs: Optional[int] = None, want_final_states: bool = False,
             workspace: Optional[torch.Tensor] = None, dt_bias=None, dt_softplus: bool = False,
-            dt_limit=(-math.inf, math.inf), z=None):
+            dt_limit=(-math.inf, math.inf), z=None, want_y_pre_gate: bool = False):
     """The SSD layer's forward, computed by libssd_bwd: y, and optionally the
     state after each sequence's last position.
 
     Same argument conventions as ssd_bwd (including the dt front-end and the
     output gate z: y is then multiplied by silu(z)).
     Returns a dict with y (the I/O dtype, shaped like x) and final_states
-    ((S, H, P, N) fp32, or None).
+    ((S, H, P, N) fp32, or None); with z and ``want_y_pre_gate`` also
+    y_pre_gate, y before the gate (for ssd_bwd's ``y_pre_gate``).
     """
     lib = load_library()
     dev = x.device
@@ -318,8 +326,9 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
     _check(A, "A", torch.float32, (H,), dev)
     _check(initial_states, "initial_states", torch.float32, (S, H, P, N), dev)
     _check(seq_idx, "seq_idx", torch.int32, (b, L), dev)
-    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev)
     _check(z, "z", io, (b, L, H, P), dev)
+    y_pre = torch.empty_like(x) if (z is not None and want_y_pre_gate) else None
+    fe = _options(dt_bias, dt_softplus, dt_limit, D, H, P, dev, y_pre=y_pre)
     shape = make_shape(b, L, H, P, G, N, chunk_size, S, SSD_IO_BF16 if io == torch.bfloat16 else SSD_IO_F32)
     nbytes = workspace_size(shape)
     if workspace is None or workspace.numel() < nbytes:
@@ -336,30 +345,33 @@ def ssd_fwd(x, dt, A, B, C, D=None, initial_states=None, seq_idx=None, chunk_siz
                             *args[6:])
     if rc:
         raise SsdError(rc, "ssd_fwd")
-    return {"y": y, "final_states": fin, "workspace": workspace, "shape": shape}
+    return {"y": y, "final_states": fin, "y_pre_gate": y_pre, "workspace": workspace, "shape": shape}
 
 
 class SsdChunkScan(torch.autograd.Function):
     """The SSD layer as an autograd function: ``forward`` is ssd_fwd (y only)
     and ``backward`` is ssd_bwd, which recomputes the chunk states from the
-    saved inputs, so nothing but the inputs is kept between the two."""
+    saved inputs, so nothing but the inputs (and, with the gate z, y before
+    the gate) is kept between the two."""
 
     @staticmethod
     def forward(ctx, x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z, chunk_size, nseqs, dt_softplus,
                 dt_limit):
         fe = dict(dt_bias=dt_bias, dt_softplus=dt_softplus, dt_limit=dt_limit)
-        y = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs, z=z, **fe)["y"]
-        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z)
+        r = ssd_fwd(x, dt, A, B, C, D, initial_states, seq_idx, chunk_size=chunk_size, nseqs=nseqs, z=z,
+                    want_y_pre_gate=z is not None, **fe)
+        y = r["y"]
+        ctx.save_for_backward(x, dt, A, B, C, D, initial_states, seq_idx, dt_bias, z, r["y_pre_gate"])
         ctx.chunk_size, ctx.nseqs, ctx.dt_softplus, ctx.dt_limit = chunk_size, nseqs, dt_softplus, dt_limit
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x, dt, A, B, C, D, h0, seq_idx, dt_bias, z = ctx.saved_tensors
+        x, dt, A, B, C, D, h0, seq_idx, dt_bias, z, y_pre = ctx.saved_tensors
         want_h0 = h0 is not None and ctx.needs_input_grad[6]
         g = ssd_bwd(x, dt, A, B, C, D, dy.contiguous(), h0, seq_idx, chunk_size=ctx.chunk_size, nseqs=ctx.nseqs,
                     want_d_initial_states=want_h0, dt_bias=dt_bias, dt_softplus=ctx.dt_softplus,
-                    dt_limit=ctx.dt_limit, z=z)
+                    dt_limit=ctx.dt_limit, z=z, y_pre_gate=y_pre)
         return (g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"], g["dD"], g["d_initial_states"] if want_h0 else None,
                 None, g.get("ddt_bias"), g.get("dz"), None, None, None, None)
 

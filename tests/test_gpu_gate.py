@@ -1,7 +1,9 @@
 """GPU parity of the output gate (out = y silu(z); ssd_fwd_ex / ssd_bwd_ex)
 with the oracle's forward_ex / backward_ex: the gated y, every gradient and
 dz, with and without the dt front-end; bitwise repeats; the autograd
-function with z as a leaf; the caller's dy left untouched."""
+function with z as a leaf (its backward takes the forward's saved pre-gate y,
+and matches the recomputing entry point byte for byte); the saved pre-gate y
+against the recomputation; the caller's dy left untouched."""
 import math
 
 import numpy as np
@@ -112,6 +114,43 @@ def test_gate_bitwise_repeat_and_autograd():
     assert torch.equal(leaves["x"].grad.view(torch.int16), g1["dx"].view(torch.int16))
     assert torch.equal(leaves["dt_raw"].grad.view(torch.int32), g1["ddt"].view(torch.int32))
     assert torch.equal(leaves["dt_bias"].grad.view(torch.int32), g1["ddt_bias"].view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_from_saved_pre_gate_output(dtype):
+    """The forward's y before the gate, handed to the backward, gives the same
+    bytes as the backward's own recomputation of y (one elementwise gate
+    pass instead of the output kernel), and it is the oracle's ungated y."""
+    if dtype == "f32":
+        w = small("gate_pre_f32", batch=2, seqlen=200, nheads=4, ngroups=2, headdim=16, dstate=32, chunk=64)
+        inputs = with_gate(packed(make_inputs(w), [[64, 40, 1, 95], [200]]), 8)
+        chunk = 64
+    else:
+        w = Workload("gate_pre_bf16", batch=1, seqlen=700, nheads=8, headdim=64, ngroups=2, dstate=64, chunk=128,
+                     dtype="bf16", seed=73)
+        inputs = with_gate(packed(make_inputs(w), [[250, 450]]), 9)
+        chunk = 128
+    print(f"[case] gate from the saved pre-gate output {dtype}", flush=True)
+    d = to_device(inputs)
+    nseqs = inputs["initial_states"].shape[0]
+    kw = dict(z=d["z"], dt_bias=d["dt_bias"], dt_softplus=True)
+    args = (d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"])
+    f = ssd.ssd_fwd(*args, d["initial_states"], d["seq_idx"], chunk_size=chunk, nseqs=nseqs, want_y_pre_gate=True,
+                    **kw)
+    g_re = ssd.ssd_bwd(*args, d["dy"], d["initial_states"], d["seq_idx"], chunk_size=chunk, nseqs=nseqs, **kw)
+    g_pre = ssd.ssd_bwd(*args, d["dy"], d["initial_states"], d["seq_idx"], chunk_size=chunk, nseqs=nseqs,
+                        y_pre_gate=f["y_pre_gate"], **kw)
+    torch.cuda.synchronize()
+    assert bytes_equal(g_re, g_pre, GRADS + ("ddt_bias", "dz")) == []
+    fz = to_f64_numpy(inputs)
+    y_ref = oracle.forward_ex(fz["x"], fz["dt_raw"], fz["A"], fz["B"], fz["C"], fz["D"], fz["initial_states"],
+                              fz["seq_idx"], dt_bias=fz["dt_bias"], dt_softplus=True)
+    e = normwise_err(f["y_pre_gate"].double().cpu().numpy(), y_ref)
+    print(f"gate pre-gate y {dtype}: err {e:.2e}", flush=True)
+    assert e <= TOL[dtype]
+    with pytest.raises(ValueError):
+        ssd.ssd_bwd(*args, d["dy"], d["initial_states"], d["seq_idx"], chunk_size=chunk, nseqs=nseqs,
+                    y_pre_gate=f["y_pre_gate"], dt_bias=d["dt_bias"], dt_softplus=True)
 
 
 def with_channel_D(inputs, seed):
