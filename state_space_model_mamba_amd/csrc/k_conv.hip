@@ -45,12 +45,14 @@ constexpr int BEFORE_START = INT32_MIN, PAST_END = INT32_MIN + 1;
 // from a sweep at L = 16384 and 10240 bf16 channels.  The backward carries
 // more state per lane (the g ring and the gradient sums): with 8 bytes per
 // lane it keeps 3 waves per SIMD, and its longer runs amortise the halo rows
-// and the per-block slot.
+// and the per-block slot.  NTL / NTS: the walk's row loads / stores carry the
+// nontemporal hint (every byte is touched once; measured per walk).
 template <bool BWD> struct Walk {
   static constexpr int TT = BWD ? 128 : 32;
   static constexpr int NB = BWD ? 8 : 16;
   static constexpr int DEPTH = BWD ? 4 : 8;
   static constexpr int RB = NWAVE * TT;   // rows per block
+  static constexpr bool NTL = BWD, NTS = true;
 };
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -60,11 +62,17 @@ template <> struct RawT<2> { using type = u32x2_t; };
 template <> struct RawT<4> { using type = u32x4_t; };
 
 // A lane's NB bytes of one row: load, store, and conversion to and from fp32
-template <typename T, int NB> struct Io {
+template <typename T, int NB, bool NTL = false, bool NTS = false> struct Io {
   static constexpr int VEC = NB / static_cast<int>(sizeof(T)), NWD = NB / 4;
   using raw = typename RawT<NWD>::type;
-  static __device__ __forceinline__ raw load(const T* p) { return *reinterpret_cast<const raw*>(p); }
-  static __device__ __forceinline__ void store(T* p, raw r) { *reinterpret_cast<raw*>(p) = r; }
+  static __device__ __forceinline__ raw load(const T* p) {
+    if constexpr (NTL) return __builtin_nontemporal_load(reinterpret_cast<const raw*>(p));
+    else return *reinterpret_cast<const raw*>(p);
+  }
+  static __device__ __forceinline__ void store(T* p, raw r) {
+    if constexpr (NTS) __builtin_nontemporal_store(r, reinterpret_cast<raw*>(p));
+    else *reinterpret_cast<raw*>(p) = r;
+  }
   static __device__ __forceinline__ void unpack(raw u, float (&f)[VEC]) {
 #pragma unroll
     for (int i = 0; i < NWD; ++i) {
@@ -102,7 +110,7 @@ __device__ __forceinline__ float sigmoid(float p) { return __builtin_amdgcn_rcpf
 
 template <typename T, int W, bool SILU, bool BWD>
 __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
-  using IO = Io<T, Walk<BWD>::NB>;
+  using IO = Io<T, Walk<BWD>::NB, Walk<BWD>::NTL, Walk<BWD>::NTS>;
   constexpr int TT = Walk<BWD>::TT, RB = Walk<BWD>::RB, DEPTH = Walk<BWD>::DEPTH;
   constexpr int VEC = IO::VEC, CB = WAVE * VEC;
   constexpr int NSTEP = BWD ? (TT + W - 1 + DEPTH - 1) / DEPTH * DEPTH : TT;

@@ -24,6 +24,16 @@
 
 namespace ssd {
 
+// sigmoid(z) of the gate.  With bf16 I/O from the hardware exponential and
+// reciprocal (v_rcp_f32, 1 ulp): their error is far below the bf16 rounding
+// of the gate's outputs, and an IEEE division costs about ten instructions
+// per element.  With fp32 I/O the library expf and a correctly rounded division.
+template <typename T>
+__device__ __forceinline__ float gate_sigmoid(float z) {
+  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_rcpf(1.f + __expf(-z));
+  else return 1.f / (1.f + expf(-z));
+}
+
 // The backward's gate pass for one 16-byte piece of dout (du), z (zu) and y
 // (yu, rounded to the I/O dtype): the gated dy = dout silu(z) and
 // dz = dout y sigmoid(z) (1 + z (1 - sigmoid(z))), rounded to the I/O dtype.
@@ -33,7 +43,7 @@ __device__ __forceinline__ void gate_grads(uint4 du, uint4 zu, uint4 yu, T* dy_o
   T dyo[VEC], dzo[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz)), dv = vget<T>(du, e);
+    const float zz = vget<T>(zu, e), sg = gate_sigmoid<T>(zz), dv = vget<T>(du, e);
     dyo[e] = Elem<T>::from_f(dv * zz * sg);
     dzo[e] = Elem<T>::from_f(dv * vget<T>(yu, e) * sg * (1.f + zz * (1.f - sg)));
   }
@@ -544,7 +554,7 @@ __global__ __launch_bounds__((YCfg<T, Q, P, NS>::NTHR)) void k_y(Problem pb) {
           T o[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const float zz = vget<T>(zu, e), sg = 1.f / (1.f + expf(-zz));
+            const float zz = vget<T>(zu, e), sg = gate_sigmoid<T>(zz);
             o[e] = Elem<T>::from_f(vget<T>(yu, e) * zz * sg);
           }
           *reinterpret_cast<uint4*>(static_cast<T*>(pb.y) + off) = *reinterpret_cast<const uint4*>(o);
