@@ -23,10 +23,27 @@
 // staged row-major with 16-byte (or 8-byte) stores and read as MFMA
 // fragments with the LDS transpose reads; the next head's rows are loaded
 // into registers while the current head is multiplied.
+#include <type_traits>
+
 #include "ssd_problem.h"
 #include "ssd_tiles.h"
 
 namespace ssd {
+
+// The owned row tiles that a K slab of the dCB product touches vary with the
+// wave and the slab (causally dead slabs): the slab's body is instantiated per
+// combination of live tiles and chosen by one wave-uniform branch, so its
+// fragment reads and products stay one straight-line sequence (a branch per
+// product made every product wait for all LDS reads in flight).
+template <typename F>
+__device__ __forceinline__ void with_live(bool live0, bool live1, F&& f) {
+  if (live0 && live1)
+    f(std::true_type{}, std::true_type{});
+  else if (live0)
+    f(std::true_type{}, std::false_type{});
+  else if (live1)
+    f(std::false_type{}, std::true_type{});
+}
 
 template <typename T, int Q, int P, int NTG>
 struct DbdcCfg {
@@ -38,7 +55,9 @@ struct DbdcCfg {
   static_assert(NTHR >= Q, "one thread per chunk position");
   static constexpr int NCT = NTG / 16;
   static constexpr int VEC = Vec16<T>::N;
-  static constexpr int KSL = 32;                 // K slab of the dCB products
+  // K slab of the dCB products: 64 positions where that takes no more LDS
+  // than the head phase (P >= 64), else 32
+  static constexpr int KSL = P >= 64 ? 64 : 32;
   static constexpr int LDA = KSL + VEC;          // dCB slab rows [i][k]
   static constexpr int LDK = kn_pitch<T>(NTG);   // B / C rows [k][n]
   static constexpr int LDP = P + VEC;            // dy / x rows [i][p]
@@ -131,28 +150,32 @@ __device__ __forceinline__ void dcb_slab_product(const Problem& pb, const DbdcBl
     }
     constexpr int KS = KSL / Mma<T>::KSTEP;
     const int l = lane_id();
+    bool live[2];   // the row tile has causally live columns in this slab
+#pragma unroll
+    for (int a = 0; a < 2; ++a) live[a] = lower ? (k0 <= 16 * own[a] + 15) : (k0 + KSL > 16 * own[a]);
     // both owned row tiles take each column fragment from one LDS read
-    bool live[2];
-    typename Mma<T>::frag af[2][KS];
+    with_live(live[0], live[1], [&](auto L0, auto L1) {
+      constexpr bool LV[2] = {decltype(L0)::value, decltype(L1)::value};
+      typename Mma<T>::frag af[2][KS];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int R = own[a];
-      live[a] = lower ? (k0 <= 16 * R + 15) : (k0 + KSL > 16 * R);
+      for (int a = 0; a < 2; ++a)
+        if (LV[a])
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        af[a][ks] = Mma<T>::load_k(s_a + (16 * R + (l & 15)) * Cf::LDA + (l >> 4) * Mma<T>::KW + ks * Mma<T>::KSTEP);
-    }
+          for (int ks = 0; ks < KS; ++ks)
+            af[a][ks] = Mma<T>::load_k(s_a + (16 * own[a] + (l & 15)) * Cf::LDA + (l >> 4) * Mma<T>::KW +
+                                       ks * Mma<T>::KSTEP);
 #pragma unroll
-    for (int nt = 0; nt < NTG / 16; ++nt) {
+      for (int nt = 0; nt < NTG / 16; ++nt) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const typename Mma<T>::frag bf = load_kn<T>(s_k + 16 * nt, Cf::LDK, ks * Mma<T>::KSTEP);
+        for (int ks = 0; ks < KS; ++ks) {
+          const typename Mma<T>::frag bf = load_kn<T>(s_k + 16 * nt, Cf::LDK, ks * Mma<T>::KSTEP);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          if (live[a]) acc[a][nt] = Mma<T>::mma(af[a][ks], bf, acc[a][nt]);
+          for (int a = 0; a < 2; ++a)
+            if (LV[a]) acc[a][nt] = Mma<T>::mma(af[a][ks], bf, acc[a][nt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   }
 }
 
@@ -203,7 +226,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   int* s_segstart = s_seg + Q;
   float* s_red = reinterpret_cast<float*>(s_segstart + Q + 1);
 
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   DbdcBlock k = dbdc_block<Q, NTHR>(pb, s_seg, s_segstart);
   k.n0 = k.ntile * NTG;
   const T* dyg = static_cast<const T*>(pb.dy);
@@ -242,7 +265,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   };
   auto e_src = [&](int h, int m) -> ERows {
     const int64_t bhc = (static_cast<int64_t>(k.b) * pb.H + h) * pb.nc + k.c;
-    const int rank = seg_rank(s_seg[s_segstart[m]]);
+    const int rank = __builtin_amdgcn_readfirstlane(seg_rank(s_seg[s_segstart[m]]));
     if (rank == 0) return {static_cast<const T*>(pb.hin) + bhc * P * pb.N, false};
     if (!pb.h0) return {nullptr, true};
     const int s = clamp_seq(k.seqbase + rank - 1, pb.nseqs);
@@ -252,11 +275,16 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     return [=, &pb](int p) { return base + static_cast<int64_t>(p) * pb.N + k.n0; };
   };
   auto zero_row = [](int) -> const T* { return nullptr; };
+  // per-lane offsets of the head rows (dy) and of the state rows (E, dS) of this
+  // tile: fixed for the block, only the base moves from head to head
+  const auto off_dy = RowStage<T, Q, P, NTHR>::offsets(static_cast<uint32_t>(pb.H * P * sizeof(T)), pb.L - k.c * Q);
+  const auto off_st = RowStage<T, P, NTG, NTHR>::offsets(static_cast<uint32_t>(pb.N * sizeof(T)), P);
+  const T* dy_c = dyg + (static_cast<int64_t>(k.b) * pb.L + static_cast<int64_t>(k.c) * Q) * pb.H * P;
   auto load_e = [&](RowStage<T, P, NTG, NTHR>& st, ERows e) {
     if (!e.p)
       st.load(zero_row);
     else if (!e.h0)
-      st.load(state_row(static_cast<const T*>(e.p)));
+      st.load_at(static_cast<const T*>(e.p) + k.n0, off_st);
     else
       st.load_from_f32(state_row(static_cast<const float*>(e.p)));
   };
@@ -271,12 +299,9 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   auto load_head = [&](int hh) {
     const int h = k.g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(k.b) * pb.H + h) * pb.nc + k.c;
-    st_dy.load([&](int i) -> const T* {
-      const int t = k.c * Q + i;
-      return t < pb.L ? dyg + ((static_cast<int64_t>(k.b) * pb.L + t) * pb.H + h) * P : nullptr;
-    });
+    st_dy.load_at(dy_c + h * P, off_dy);
     load_e(st_e, e_src(h, 0));
-    if (single) st_s.load(state_row(static_cast<const T*>(pb.dstate) + bhc * P * pb.N));
+    if (single) st_s.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
     if (tid < Q) acs_n = pb.acs[bhc * Q + tid];
   };
   // prefetch the next head only where its registers fit, and only for a
@@ -316,7 +341,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
         __syncthreads();
         load_e(st_e, esrc);
         if (hi == Q && esrc.p) {
-          st_s.load(state_row(static_cast<const T*>(pb.dstate) + bhc * P * pb.N));
+          st_s.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
 #pragma unroll
           for (int kk = 0; kk < st_e.IT; ++kk)
 #pragma unroll
@@ -404,7 +429,7 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
   int* s_seg = reinterpret_cast<int*>(s_v + Q);
   int* s_segstart = s_seg + Q;
 
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r16 = l & 15, kg = l >> 4;
+  const int tid = threadIdx.x, w = wave_id_s(), l = lane_id(), r16 = l & 15, kg = l >> 4;
   DbdcBlock k = dbdc_block<Q, NTHR>(pb, s_seg, s_segstart);
   k.n0 = k.ntile * NTG;
   const T* xg = static_cast<const T*>(pb.x);
@@ -426,15 +451,16 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_db(Problem pb
   RowStage<T, Q, P, NTHR> st_x;
   RowStage<T, P, NTG, NTHR> st_s;
   float acs_n = 0.f, dt_n = 0.f, acs_end_n = 0.f;
+  // per-lane offsets of the x rows and the dS rows of this tile: fixed for
+  // the block, only the base moves from head to head
+  const auto off_x = RowStage<T, Q, P, NTHR>::offsets(static_cast<uint32_t>(pb.H * P * sizeof(T)), pb.L - k.c * Q);
+  const auto off_s = RowStage<T, P, NTG, NTHR>::offsets(static_cast<uint32_t>(pb.N * sizeof(T)), P);
+  const T* x_c = xg + (static_cast<int64_t>(k.b) * pb.L + static_cast<int64_t>(k.c) * Q) * pb.H * P;
   auto load_head = [&](int hh) {
     const int h = k.g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(k.b) * pb.H + h) * pb.nc + k.c;
-    st_x.load([&](int i) -> const T* {
-      const int t = k.c * Q + i;
-      return t < pb.L ? xg + ((static_cast<int64_t>(k.b) * pb.L + t) * pb.H + h) * P : nullptr;
-    });
-    const T* ds = static_cast<const T*>(pb.dstate) + bhc * P * pb.N;
-    st_s.load([=, &pb](int p) -> const T* { return ds + static_cast<int64_t>(p) * pb.N + k.n0; });
+    st_x.load_at(x_c + h * P, off_x);
+    st_s.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_s);
     if (tid < Q) {
       acs_n = pb.acs[bhc * Q + tid];
       dt_n = pb.dtc[bhc * Q + tid];

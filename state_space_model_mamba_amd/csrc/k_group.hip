@@ -226,7 +226,7 @@ __device__ __forceinline__ void dcb_write(const Problem& pb, int64_t bgc, const 
 template <typename T, int Q, int P>
 __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
   using Cf = DcbCfg<T, Q, P>;
-  constexpr int T16 = Cf::T16, NTHR = Cf::NTHR, VEC = Cf::VEC, LDP = Cf::LDP;
+  constexpr int NTHR = Cf::NTHR, LDP = Cf::LDP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* s_xk = reinterpret_cast<T*>(smem);
   T* s_dyk = s_xk + Q * LDP;
@@ -317,22 +317,20 @@ __global__ __launch_bounds__((DcbCfg<T, Q, P>::NTHR)) void k_dcb(Problem pb) {
 #pragma unroll
   for (int k = 0; k < Cf::NOWN; ++k) dcb[k] = zero4();
 
-  auto head_row = [&](const T* base, int h) {
-    return [=](int i) -> const T* {
-      const int t = c * Q + i;
-      return t < pb.L ? base + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
-    };
-  };
   // each head's x / dy rows and Acs / dt are loaded into registers while the
   // previous head's tiles are multiplied
   static_assert(NTHR >= Q, "one thread per chunk position");
   RowStage<T, Q, P, NTHR> st_x, st_dy;
   float acs_n = 0.f, dt_n = 0.f;
+  // per-lane offsets of the head rows: fixed for the block, only the base
+  // moves from head to head
+  const auto off_h = RowStage<T, Q, P, NTHR>::offsets(static_cast<uint32_t>(pb.H * P * sizeof(T)), pb.L - c * Q);
+  const int64_t row0 = (static_cast<int64_t>(b) * pb.L + static_cast<int64_t>(c) * Q) * pb.H * P;
   auto load_head = [&](int hh) {
     const int h = g * pb.hpg + hh;
     const int64_t bhc = (static_cast<int64_t>(b) * pb.H + h) * pb.nc + c;
-    st_x.load(head_row(xg, h));
-    st_dy.load(head_row(dyg, h));
+    st_x.load_at(xg + row0 + h * P, off_h);
+    st_dy.load_at(dyg + row0 + h * P, off_h);
     if (tid < Q) {
       acs_n = pb.acs[bhc * Q + tid];
       dt_n = pb.dtc[bhc * Q + tid];

@@ -93,6 +93,33 @@ struct RowStage {
       }
     }
   }
+  // Requests at fixed per-lane byte offsets from a wave-uniform base, for
+  // rows at a fixed byte pitch from it (one head's rows after another's:
+  // only the base moves, so a request takes no 64-bit address arithmetic per
+  // lane).  Rows at or past nrows are not read (their pieces are zero).
+  struct Offs {
+    uint32_t off[IT];
+    uint32_t ok;   // bit k: piece k is read
+  };
+  static __device__ __forceinline__ Offs offsets(uint32_t row_bytes, int nrows) {
+    Offs o;
+    o.ok = 0;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      const int r = v / CV;
+      o.off[k] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>((v % CV) * 16);
+      if ((NV % NTHR == 0 || v < NV) && r < nrows) o.ok |= 1u << k;
+    }
+    return o;
+  }
+  __device__ __forceinline__ void load_at(const TIN* base, const Offs& o) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      buf[k] = zero_u4();
+      if ((o.ok >> k) & 1u) buf[k] = ld_global16_at(base, o.off[k]);
+    }
+  }
   // The same rows read from fp32 memory and rounded to TIN (to nearest even):
   // each 16-byte piece takes 16 / sizeof(TIN) floats.  The conversion waits
   // for the loads, so this is for rarely taken paths.
