@@ -398,21 +398,20 @@ __device__ __forceinline__ ItemCoords item_coords(const Problem& pb, int64_t lb)
   return it;
 }
 
-// x and dy rows of item lb -> registers (rows past L read as zero).
+// x and dy rows of item lb -> registers (rows past L read as zero), at
+// 32-bit lane offsets (the rows of all heads at their pitch; the shape check
+// bounds a chunk's rows at 2^31 bytes) from a wave-uniform base.
 template <typename T, int Q, int P>
 __device__ __forceinline__ void load_item_rows(const Problem& pb, int64_t lb,
                                                RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_x,
                                                RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>& st_dy) {
+  using St = RowStage<T, Q, P, HeadCfg<T, Q, P>::NTHR>;
+  const typename St::Offs off = St::offsets(static_cast<uint32_t>(pb.H * P * sizeof(T)), Q);
   const ItemCoords it = item_coords(pb, lb);
-  const int c = it.c, b = it.b, h = it.h;
-  auto row = [&](const void* base) {
-    return [=, &pb](int i) -> const T* {
-      const int t = c * Q + i;
-      return t < pb.L ? static_cast<const T*>(base) + ((static_cast<int64_t>(b) * pb.L + t) * pb.H + h) * P : nullptr;
-    };
-  };
-  st_x.load(row(pb.x));
-  st_dy.load(row(pb.dy));
+  const int64_t row0 = ((static_cast<int64_t>(it.b) * pb.L + static_cast<int64_t>(it.c) * Q) * pb.H + it.h) * P;
+  const int nrows = pb.L - it.c * Q;
+  st_x.load_at(static_cast<const T*>(pb.x) + row0, off, nrows);
+  st_dy.load_at(static_cast<const T*>(pb.dy) + row0, off, nrows);
 }
 
 // One (batch, head, chunk) work item, logical index lb, whose x and dy rows

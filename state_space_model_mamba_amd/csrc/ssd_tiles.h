@@ -120,6 +120,16 @@ struct RowStage {
       if ((o.ok >> k) & 1u) buf[k] = ld_global16_at(base, o.off[k]);
     }
   }
+  // The same with the row count given per request (offsets taken for all
+  // ROWS rows): rows at or past nrows are not read.
+  __device__ __forceinline__ void load_at(const TIN* base, const Offs& o, int nrows) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+      buf[k] = zero_u4();
+      if ((o.ok >> k) & 1u && v / CV < nrows) buf[k] = ld_global16_at(base, o.off[k]);
+    }
+  }
   // The same rows read from fp32 memory and rounded to TIN (to nearest even):
   // each 16-byte piece takes 16 / sizeof(TIN) floats.  The conversion waits
   // for the loads, so this is for rarely taken paths.
