@@ -68,10 +68,11 @@ def step_compulsory_bytes(z):
 
 
 def group_fused(w):
-    """The library's choice of group kernels for this workload (split when their grid has >= 256 blocks)."""
+    """The library's choice of group kernels for this workload: fused when the split kernels'
+    grid has fewer than 256 blocks and a group has at most 16 heads, else split."""
     nc = -(-w.seqlen // w.chunk)
     ntg = w.dstate // next(t for t in (128, 64, 32, 16) if w.dstate % t == 0)
-    return w.batch * w.ngroups * nc * ntg < 256
+    return w.batch * w.ngroups * nc * ntg < 256 and w.nheads // w.ngroups <= 16
 
 
 def stage_alg_bytes(z, fused=False):
@@ -143,6 +144,7 @@ def measured_traffic(workload, stage):
 # stage of each library kernel (kernel name prefix -> stage)
 STAGE_OF_KERNEL = [("k_head_bwd", "head_bwd"), ("k_state_fwd", "state_fwd"), ("k_state_bwd", "state_bwd"),
                    ("k_dcb<", "dcb"), ("k_dc<", "dbdc"), ("k_db<", "dbdc"), ("k_cb<", "dcb"), ("k_grp<", "dbdc"),
+                   ("k_dcb_out<", "dcb"), ("k_bd_out<", "dbdc"),
                    ("k_prep", "prep"),
                    ("k_seqbase", "prep"), ("k_reduce", "reduce"),
                    ("k_cbf<", "fwd_cbf"), ("k_y<", "fwd_y"), ("k_final<", "fwd_final"), ("k_seqstart", "fwd_final")]

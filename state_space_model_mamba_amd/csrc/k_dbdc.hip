@@ -304,10 +304,12 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     if (single) st_s.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
     if (tid < Q) acs_n = pb.acs[bhc * Q + tid];
   };
-  // prefetch the next head only where its registers fit, and only for a
-  // single-segment chunk (the segment loop below reuses the same registers)
+  // prefetch the next head where its registers fit; a chunk's further segments
+  // (a sequence starts inside it) take their E and the chunk-end dS into
+  // registers of their own, so the prefetched head's stay untouched
   constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + 2 * RowStage<T, P, NTG, NTHR>::IT <= 16;
-  const bool pf = PF && single;
+  const bool pf = PF;
+  RowStage<T, P, NTG, NTHR> st_e2, st_s2;
   if (pf && k.hh_lo < k.hh_hi) load_head(k.hh_lo);
 
   for (int hh = k.hh_lo; hh < k.hh_hi; ++hh) {
@@ -339,15 +341,15 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
       if (m > 0) {
         // further segments (a sequence starts inside the chunk): stage their E here
         __syncthreads();
-        load_e(st_e, esrc);
+        load_e(st_e2, esrc);
         if (hi == Q && esrc.p) {
-          st_s.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
+          st_s2.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
 #pragma unroll
-          for (int kk = 0; kk < st_e.IT; ++kk)
+          for (int kk = 0; kk < st_e2.IT; ++kk)
 #pragma unroll
-            for (int e = 0; e < st_e.VEC; ++e) endp += vget<T>(st_s.buf[kk], e) * vget<T>(st_e.buf[kk], e);
+            for (int e = 0; e < st_e2.VEC; ++e) endp += vget<T>(st_s2.buf[kk], e) * vget<T>(st_e2.buf[kk], e);
         }
-        st_e.store(s_e, LDE);
+        st_e2.store(s_e, LDE);
         __syncthreads();
       }
       if (!esrc.p) continue;
