@@ -55,16 +55,6 @@ template <> __device__ __forceinline__ void store4f<bf16_t>(bf16_t* p, f32x4_t v
 template <> __device__ __forceinline__ void store4f<float>(float* p, f32x4_t v) {
   *reinterpret_cast<f32x4_t*>(p) = v;
 }
-// The same with the nontemporal hint, for output streams no later stage of
-// the kernel reads
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-template <typename T> __device__ __forceinline__ void store4f_nt(T* p, f32x4_t v);
-template <> __device__ __forceinline__ void store4f_nt<bf16_t>(bf16_t* p, f32x4_t v) {
-  __builtin_nontemporal_store(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, reinterpret_cast<u32x2_t*>(p));
-}
-template <> __device__ __forceinline__ void store4f_nt<float>(float* p, f32x4_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
-}
 
 // ---------------------------------------------------------------------------
 // Block-wide staging of a ROWS x COLS tile from global memory (rows given by
