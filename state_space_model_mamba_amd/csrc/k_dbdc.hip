@@ -210,7 +210,10 @@ __device__ __forceinline__ void write_rows(const Problem& pb, const DbdcBlock& k
 // ----------------------------------------------------------------------------
 // k_dc
 // ----------------------------------------------------------------------------
-template <typename T, int Q, int P, int NTG>
+// SEQ: the input has sequence boundaries (seq_idx), so chunks can hold
+// several segments; without them every chunk is one segment and the kernel
+// keeps no registers for a second segment's early requests.
+template <typename T, int Q, int P, int NTG, bool SEQ>
 __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb) {
   using Cf = DbdcCfg<T, Q, P, NTG>;
   constexpr int W = Cf::W, NTHR = Cf::NTHR, NCT = Cf::NCT, LDP = Cf::LDP, LDE = Cf::LDE, LDK = Cf::LDK;
@@ -310,6 +313,12 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
   constexpr bool PF = RowStage<T, Q, P, NTHR>::IT + 2 * RowStage<T, P, NTG, NTHR>::IT <= 16;
   const bool pf = PF;
   RowStage<T, P, NTG, NTHR> st_e2, st_s2;
+  // a second segment's entering state when it is a given initial state (fp32),
+  // requested before the first segment's products and rounded when staged
+  // (where its registers fit: at most four 16-byte pieces per thread)
+  using StE = RowStage<T, P, NTG, NTHR>;
+  constexpr bool E2PF = SEQ && StE::IT * StE::F4 <= 4;
+  uint4 e2raw[StE::IT][StE::F4];
   if (pf && k.hh_lo < k.hh_hi) load_head(k.hh_lo);
 
   for (int hh = k.hh_lo; hh < k.hh_hi; ++hh) {
@@ -329,6 +338,24 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
     if (tid < Q) s_v[tid] = Elem<T>::exp(acs_n);
     __syncthreads();
     if (pf && hh + 1 < k.hh_hi) load_head(hh + 1);
+    // A chunk in which a sequence starts: the second segment's E (the
+    // sequence's initial state) and, when that segment ends the chunk, the
+    // chunk-end dS are requested now, so that the first segment's products
+    // cover their latency; later segments load theirs when they come.
+    bool e2_early = false, s2_early = false;
+    if (SEQ && k.nseg > 1) {   // (uniform)
+      const ERows e1 = e_src(h, 1);
+      if constexpr (E2PF) {
+        if (e1.p && e1.h0) {
+          st_e2.load_f32_raw(state_row(static_cast<const float*>(e1.p)), e2raw);
+          e2_early = true;
+        }
+      }
+      if (s_segstart[2] == Q && e1.p) {
+        st_s2.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
+        s2_early = true;
+      }
+    }
 
     float offp[2][4];
 #pragma unroll
@@ -341,9 +368,16 @@ __global__ __launch_bounds__((DbdcCfg<T, Q, P, NTG>::NTHR)) void k_dc(Problem pb
       if (m > 0) {
         // further segments (a sequence starts inside the chunk): stage their E here
         __syncthreads();
-        load_e(st_e2, esrc);
+        bool staged = false;
+        if constexpr (E2PF) {
+          if (m == 1 && e2_early) {
+            st_e2.convert_f32(e2raw);
+            staged = true;
+          }
+        }
+        if (!staged) load_e(st_e2, esrc);
         if (hi == Q && esrc.p) {
-          st_s2.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
+          if (!(m == 1 && s2_early)) st_s2.load_at(static_cast<const T*>(pb.dstate) + bhc * P * pb.N + k.n0, off_st);
 #pragma unroll
           for (int kk = 0; kk < st_e2.IT; ++kk)
 #pragma unroll
@@ -554,11 +588,18 @@ __global__ __launch_bounds__(256) void k_bd_out(Problem pb, const float* part, v
 template <typename T, int Q, int P, int NTG>
 static hipError_t launch_dbdc_t(const Problem& pb, hipStream_t s) {
   using Cf = DbdcCfg<T, Q, P, NTG>;
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG>), Cf::LDS);
+  const bool seq = pb.seq_idx != nullptr;
+  hipError_t e = ensure_dynamic_lds(seq ? reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG, true>)
+                                        : reinterpret_cast<const void*>(&k_dc<T, Q, P, NTG, false>),
+                                    Cf::LDS);
   if (e == hipSuccess) e = ensure_dynamic_lds(reinterpret_cast<const void*>(&k_db<T, Q, P, NTG>), Cf::LDS_DB);
   if (e != hipSuccess) return e;
   const int64_t tiles = static_cast<int64_t>(pb.B) * pb.G * pb.nc * pb.ntg, blocks = tiles * pb.nslice_bd;
-  hipLaunchKernelGGL((k_dc<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
+  if (seq)
+    hipLaunchKernelGGL((k_dc<T, Q, P, NTG, true>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s, pb);
+  else
+    hipLaunchKernelGGL((k_dc<T, Q, P, NTG, false>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS, s,
+                       pb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_db<T, Q, P, NTG>), dim3(static_cast<unsigned>(blocks)), dim3(Cf::NTHR), Cf::LDS_DB, s, pb);

@@ -120,6 +120,34 @@ struct RowStage {
       if ((o.ok >> k) & 1u && v / CV < nrows) buf[k] = ld_global16_at(base, o.off[k]);
     }
   }
+  // fp32 rows requested now (16-byte loads, F4 per piece of TIN) and rounded
+  // to TIN later by convert_f32, so that the requests stay in flight meanwhile
+  static constexpr int F4 = VEC / 4;
+  template <typename RowPtr>
+  __device__ __forceinline__ void load_f32_raw(RowPtr rowptr, uint4 (&raw)[IT][F4]) const {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int v = static_cast<int>(threadIdx.x) + k * NTHR;
+#pragma unroll
+      for (int f = 0; f < F4; ++f) raw[k][f] = zero_u4();
+      if (NV % NTHR == 0 || v < NV) {
+        const float* p = rowptr(v / CV);
+        if (p) {
+#pragma unroll
+          for (int f = 0; f < F4; ++f) raw[k][f] = ld_global16(p + (v % CV) * VEC + 4 * f);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void convert_f32(const uint4 (&raw)[IT][F4]) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      TIN o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = Elem<TIN>::from_f(__uint_as_float((&raw[k][e / 4].x)[e % 4]));
+      buf[k] = *reinterpret_cast<const uint4*>(o);
+    }
+  }
   // The same rows read from fp32 memory and rounded to TIN (to nearest even):
   // each 16-byte piece takes 16 / sizeof(TIN) floats.  The conversion waits
   // for the loads, so this is for rarely taken paths.
