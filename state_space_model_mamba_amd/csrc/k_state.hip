@@ -508,34 +508,63 @@ __global__ __launch_bounds__((StateCfg<T, Q, P, NT>::NTHR)) void k_state_bwd(Pro
 #pragma unroll
             for (int r = 0; r < 4; ++r) dout[i][j][r] = R[i][j][r] + cur.decay * dout[i][j][r];
       } else {
+        // A chunk with a sequence start: per segment the same blocked product
+        // over the segment's positions (the rows outside it masked), each
+        // tile's products in ascending position order.  The segments go last
+        // first: the last one's d_init term takes the incoming dOut, and the
+        // segment that continues the previous chunk's sequence (segment 0, if
+        // any) becomes the outgoing dOut after all of them.
+        bool cont = false;
+        for (int m = cur.nseg - 1; m >= 0; --m) {
+          const int lo = __builtin_amdgcn_readfirstlane(s_segstart[m]);
+          const int hi = __builtin_amdgcn_readfirstlane(s_segstart[m + 1]);
+          f32x4_t R[BNB][BPB];
 #pragma unroll
-        for (int i = 0; i < BNB; ++i)
+          for (int i = 0; i < BNB; ++i)
 #pragma unroll
-          for (int j = 0; j < BPB; ++j) {
-            const int pt = BPB * bp + j, nt = BNB * bn + i;
-            const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
-            f32x4_t dhoff = zero4();
-            for (int m = 0; m < cur.nseg; ++m) {
-              const int lo = s_segstart[m], hi = s_segstart[m + 1];
-              f32x4_t R = zero4();
-              for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP)
-                R = Mma<T>::mma(Cf::BTile::frag(s_ct, nt * 16, k0),
-                                mask_k<T>(Cf::XTile::frag(s_dyt, pt * 16, k0), k0, lo, hi), R);
-              const int rank = seg_rank(s_seg[lo]);
-              if (rank == 0) {
-                dhoff = R;
-              } else if (pb.dinit) {
-                const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
+            for (int j = 0; j < BPB; ++j) R[i][j] = zero4();
+#pragma unroll 1
+          for (int k0 = (lo / Mma<T>::KSTEP) * Mma<T>::KSTEP; k0 < hi; k0 += Mma<T>::KSTEP) {
+            typename Mma<T>::frag af[BNB], bfr[BPB];
+#pragma unroll
+            for (int i = 0; i < BNB; ++i) af[i] = Cf::BTile::frag(s_ct, (BNB * bn + i) * 16, k0);
+#pragma unroll
+            for (int j = 0; j < BPB; ++j) bfr[j] = mask_k<T>(Cf::XTile::frag(s_dyt, (BPB * bp + j) * 16, k0), k0, lo, hi);
+#pragma unroll
+            for (int i = 0; i < BNB; ++i)
+#pragma unroll
+              for (int j = 0; j < BPB; ++j) R[i][j] = Mma<T>::mma(af[i], bfr[j], R[i][j]);
+          }
+          const int rank = __builtin_amdgcn_readfirstlane(seg_rank(s_seg[lo]));
+          if (rank == 0) {
+#pragma unroll
+            for (int i = 0; i < BNB; ++i)
+#pragma unroll
+              for (int j = 0; j < BPB; ++j) dout[i][j] = R[i][j];
+            cont = true;
+          } else if (pb.dinit) {
+            const int s = clamp_seq(cur.seqbase + rank - 1, pb.nseqs);
+#pragma unroll
+            for (int i = 0; i < BNB; ++i)
+#pragma unroll
+              for (int j = 0; j < BPB; ++j) {
+                const int pt = BPB * bp + j, nt = BNB * bn + i;
+                const int p = pt * 16 + r16, n = n0 + nt * 16 + 4 * kg;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                  float v = R[r];
+                  float v = R[i][j][r];
                   if (hi == Q) v += cur.decay * dout[i][j][r];
                   pb.dinit[((static_cast<int64_t>(s) * pb.H + h) * P + p) * pb.N + n + r] = v;
                 }
               }
-            }
-            dout[i][j] = dhoff;
           }
+        }
+        if (!cont) {
+#pragma unroll
+          for (int i = 0; i < BNB; ++i)
+#pragma unroll
+            for (int j = 0; j < BPB; ++j) dout[i][j] = zero4();
+        }
       }
     }
     __syncthreads();
