@@ -283,22 +283,26 @@ __device__ __forceinline__ void head_tiles(f32x4_t (&cb)[Q / 16 + 1], f32x4_t (&
         e4[r] = ok ? e : 0.f;
       }
     }
-    float gms = 0.f;
-    f32x4_t v;
+    f32x4_t gm;   // G o M
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float gv = cb[k][r] * e4[r];
       cb[k][r] = gv;
-      const float gm = gv * m[r];
-      gms += gm;
-      v[r] = gm * dtj;
+      gm[r] = gv * m[r];
     }
-    // column tile J's share of da at the rows of tile I (see the top of the file)
-    float sfx[4];   // in-lane suffix sums over the lane's 4 rows
-    sfx[3] = v[3];
-    sfx[2] = v[2] + sfx[3];
-    sfx[1] = v[1] + sfx[2];
-    sfx[0] = v[0] + sfx[1];
+    // column tile J's share of da at the rows of tile I (see the top of the
+    // file).  The lane's 4 values share the column j, so the in-lane suffix
+    // sums of V = G o M dt_j are dt_j times those of G o M, and the first of
+    // those is the tile's ddt_intra part of column j.
+    float sg[4];
+    sg[3] = gm[3];
+    sg[2] = gm[2] + sg[3];
+    sg[1] = gm[1] + sg[2];
+    sg[0] = gm[0] + sg[1];
+    const float gms = sg[0];
+    float sfx[4];   // in-lane suffix sums of V over the lane's 4 rows
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sfx[r] = sg[r] * dtj;
     if (diag) {
       // this lane's entries of M's diagonal, M[i][i] = dy_i . x_i (their sum over
       // the chunk is the head's dD term)
