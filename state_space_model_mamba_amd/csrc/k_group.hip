@@ -140,9 +140,9 @@ __device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, con
     for (int s = 0; s < In::MK; ++s) m = Mma<T>::mma(cur.ma[s], col.mb[s], m);
     const int j = 16 * J + r16;
     const float aj = col.aj, dtj = col.dtj;
-    f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+    f32x4_t e4;   // exp(Acs_i - Acs_j) dt_j where (i, j) is causal and in one segment, else 0
     if (UNI && k < Split::NOFF) {
-      const float ec = Elem<T>::exp(cur.acs_i0 - aj);
+      const float ec = Elem<T>::exp(cur.acs_i0 - aj) * dtj;
 #pragma unroll
       for (int r = 0; r < 4; ++r) e4[r] = cur.rowv[r] * ec;
     } else {
@@ -153,11 +153,11 @@ __device__ __forceinline__ void dcb_tiles(f32x4_t (&dcb)[NOWN], const T* xk, con
         const bool ok = (j <= i) & (loi == col.loj);
         // exp of a non-positive argument only; masked entries use a zero argument
         const float e = Elem<T>::exp(ok ? cur.rowv[r] - aj : 0.f);
-        e4[r] = ok ? e : 0.f;
+        e4[r] = ok ? e * dtj : 0.f;
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dcb[k][r] += (e4[r] * dtj) * m[r];
+    for (int r = 0; r < 4; ++r) dcb[k][r] += e4[r] * m[r];
     // the tile's sums are complete here: keeps them from being sunk past the
     // column branches below (which would hold every tile's products live)
     asm volatile("" : "+v"(dcb[k]));

@@ -336,9 +336,9 @@ __global__ __launch_bounds__((GrpCfg<T, Q, P, NTG>::NTHR)) void k_grp(Problem pb
         for (int s = 0; s < MK; ++s) m = Mma<T>::mma(ma[s], mb[s], m);
         const int j = 16 * J + r16;
         const float aj = lacs[j], dtj = ldt[j];
-        f32x4_t e4;   // exp(Acs_i - Acs_j) where (i, j) is causal and in one segment, else 0
+        f32x4_t e4;   // exp(Acs_i - Acs_j) dt_j where (i, j) is causal and in one segment, else 0
         if (uniform && I != J) {
-          const float ec = Elem<T>::exp(lacs[16 * I] - aj);
+          const float ec = Elem<T>::exp(lacs[16 * I] - aj) * dtj;
           const f32x4_t er4 = *reinterpret_cast<const f32x4_t*>(ler + 16 * I + 4 * kg);
 #pragma unroll
           for (int r = 0; r < 4; ++r) e4[r] = er4[r] * ec;
@@ -353,11 +353,11 @@ __global__ __launch_bounds__((GrpCfg<T, Q, P, NTG>::NTHR)) void k_grp(Problem pb
             const bool ok = (j <= i) & (seg_lo(sgi) == loj);
             // exp of a non-positive argument only; masked entries use a zero argument
             const float e = Elem<T>::exp(ok ? ai4[r] - aj : 0.f);
-            e4[r] = ok ? e : 0.f;
+            e4[r] = ok ? e * dtj : 0.f;
           }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dcb[k][r] += (e4[r] * dtj) * m[r];
+        for (int r = 0; r < 4; ++r) dcb[k][r] += e4[r] * m[r];
       }
       // one tile at a time: keeps the next tiles' operands out of this tile's registers
       __builtin_amdgcn_sched_barrier(0);
