@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NTHR) void k_conv(Args a) {
 
 // dweight[c][k] and dbias[c]: the slots added in slot order, in double.  Small
 // blocks spread the (W + 1) * C sums over every CU; the slot loads are issued
-// eight at a time ahead of their (ordered) adds.
+// 32 (then 8) at a time ahead of their (ordered) adds.
 constexpr int RED_THR = 64;
 __global__ __launch_bounds__(RED_THR) void k_conv_reduce(const float* part, int64_t nslot, int64_t C, int W,
                                                          float* dw, float* dbias) {
@@ -362,6 +362,13 @@ __global__ __launch_bounds__(RED_THR) void k_conv_reduce(const float* part, int6
   const float* p = part + k * C + c;
   double acc = 0.0;
   int64_t s = 0;
+  for (; s + 32 <= nslot; s += 32) {
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = p[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc += static_cast<double>(v[j]);
+  }
   for (; s + 8 <= nslot; s += 8) {
     float v[8];
 #pragma unroll
