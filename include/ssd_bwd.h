@@ -191,7 +191,7 @@ typedef struct {
  * buffer until dx overwrites it.
  *
  * The gate is not on the pages either: it is the output gate of the usual
- * Mamba-2 layer, the second half of the same "next" step as the front-end.
+ * Mamba-2 layer, which sits around the scan as the dt front-end does.
  *
  * d_last_states is what a split of the sequence axis needs (a stretch of a
  * sequence on one device, the rest on the next): the later stretch starts
