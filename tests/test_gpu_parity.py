@@ -295,6 +295,25 @@ def test_batch_rows_independent_bitwise():
         assert torch.equal(single["d_initial_states"][0], both["d_initial_states"][r])
 
 
+def test_seq_idx_of_whole_rows_equals_none_bitwise():
+    # seq_idx that is constant along each row means one sequence per row, as
+    # no seq_idx does; the library then takes kernels compiled for inputs with
+    # sequence boundaries (the dC kernel has a separate instance for them),
+    # and every chunk still has one segment, so the outputs are the same bits.
+    w = Workload("bf16_rows_h0", batch=2, seqlen=600, nheads=8, headdim=64, ngroups=2, dstate=128,
+                 chunk=256, dtype="bf16", seed=53)
+    inputs = make_inputs(w)
+    g = torch.Generator().manual_seed(530)
+    inputs["initial_states"] = 0.5 * torch.randn(w.batch, w.nheads, w.headdim, w.dstate, generator=g)
+    print("[case] seq_idx of whole rows vs none", flush=True)
+    none = run_library(inputs, 256)
+    rows = dict(inputs)
+    rows["seq_idx"] = torch.zeros(w.batch, w.seqlen, dtype=torch.int32)
+    with_idx = run_library(rows, 256)
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "d_initial_states"):
+        assert none[k] is not None and torch.equal(none[k], with_idx[k]), k
+
+
 def test_bitwise_independent_of_launch_geometry():
     # The persistent head kernel's block count decides which block takes which
     # (batch, head, chunk) item; the forward's heads per block decides which
